@@ -1,0 +1,255 @@
+"""Seeded synthetic inputs for the DiT denoise step.
+
+This module only draws random numbers and names tensor shapes. It holds none
+of the step's arithmetic, so both the CPU oracle's tests and the GPU harness
+can take their inputs from it without sharing any of the method.
+
+Scheme:
+  * every tensor has a name; its stream is NumPy PCG64 seeded with
+    (seed, crc32(name)), so a tensor never depends on which others were drawn;
+  * matrices are N(0, 1/fan_in) with fan_in = the contraction length K of an
+    [N, K] weight; activations are N(0, 1); QK-norm gains are 1 + 0.1 N(0, 1);
+  * every value is drawn in fp32 and then rounded to the nearest bf16 value
+    (ties to even), so a bf16 kernel and an fp64 oracle consume identical
+    numbers.
+
+The model follows the FLUX.2 [klein] layout the pages describe (model card
+"flux2-klein-p100a", sections "Caveats" and "Things that are easy to get
+wrong"; PYTHON.md "Modules": 5 dual-stream + 20 single-stream blocks).
+"""
+from __future__ import annotations
+
+import dataclasses
+import zlib
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+PRENORM_RMS = 0
+PRENORM_LAYER = 1
+
+
+@dataclasses.dataclass(frozen=True)
+class DitConfig:
+    hidden: int = 3072          # D
+    heads: int = 24             # H
+    head_dim: int = 128         # d
+    mlp_hidden: int = 9216      # F = 3 D (SwiGLU inner width)
+    n_dual: int = 5
+    n_single: int = 20
+    in_channels: int = 128      # 2x2-patchified latent channels
+    txt_channels: int = 7680    # three text-encoder layers of 2560, concatenated
+    axes_dim: Tuple[int, int, int, int] = (32, 32, 32, 32)
+    theta: float = 2000.0
+    eps: float = 1e-6
+    prenorm: int = PRENORM_RMS
+    time_channels: int = 256    # sinusoidal timestep features
+
+    @property
+    def mod_rows(self) -> int:
+        """Rows of the per-step modulation buffer: 6 + 6 + 3 + 2 vectors of D."""
+        return 17
+
+
+FLUX2_KLEIN = DitConfig()
+# Small dual-block configuration: hidden 256 = 2 heads x 128.
+TINY_256 = DitConfig(hidden=256, heads=2, head_dim=128, mlp_hidden=768,
+                     n_dual=1, n_single=0, in_channels=128, txt_channels=256)
+
+
+def bf16_round(a: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest bfloat16 value, ties to even.
+
+    Returns float32 holding bf16-representable values. Inputs are finite.
+    """
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    u = a.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32)
+
+
+def bf16_bits(a: np.ndarray) -> np.ndarray:
+    """The upper 16 bits of bf16-representable float32 values, as uint16."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    return (a.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def _rng(seed: int, name: str) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64([int(seed), zlib.crc32(name.encode())]))
+
+
+def normal(seed: int, name: str, shape: Sequence[int], std: float = 1.0,
+           mean: float = 0.0) -> np.ndarray:
+    """bf16-rounded N(mean, std^2) draws, float32 storage."""
+    x = _rng(seed, name).standard_normal(tuple(shape), dtype=np.float32)
+    if std != 1.0:
+        x *= np.float32(std)
+    if mean != 0.0:
+        x += np.float32(mean)
+    return bf16_round(x)
+
+
+def matrix(seed: int, name: str, n: int, k: int) -> np.ndarray:
+    """[n, k] weight in nn.Linear layout, N(0, 1/k)."""
+    return normal(seed, name, (n, k), std=1.0 / np.sqrt(k))
+
+
+def gain(seed: int, name: str, d: int) -> np.ndarray:
+    """QK-norm gain: 1 + 0.1 N(0, 1), bf16-rounded."""
+    return normal(seed, name, (d,), std=0.1, mean=1.0)
+
+
+# ---------------------------------------------------------------- weights
+
+def dual_weights(cfg: DitConfig, seed: int, idx: int) -> Dict[str, np.ndarray]:
+    """One dual-stream block. Stream 0 = text, stream 1 = image.
+
+    qkv: [3D, D] (q rows, then k rows, then v rows; head j = rows 128j..)
+    out: [D, D]; mlp_in: [2F, D] (gate rows, then up rows); mlp_out: [D, F].
+    """
+    D, F, d = cfg.hidden, cfg.mlp_hidden, cfg.head_dim
+    w: Dict[str, np.ndarray] = {}
+    for s, tag in ((0, "txt"), (1, "img")):
+        p = f"dual.{idx}.{tag}."
+        w[f"qkv{s}"] = matrix(seed, p + "qkv", 3 * D, D)
+        w[f"out{s}"] = matrix(seed, p + "out", D, D)
+        w[f"mlp_in{s}"] = matrix(seed, p + "mlp_in", 2 * F, D)
+        w[f"mlp_out{s}"] = matrix(seed, p + "mlp_out", D, F)
+        w[f"q_gain{s}"] = gain(seed, p + "q_gain", d)
+        w[f"k_gain{s}"] = gain(seed, p + "k_gain", d)
+    return w
+
+
+def single_weights(cfg: DitConfig, seed: int, idx: int) -> Dict[str, np.ndarray]:
+    """One single-stream block.
+
+    w_in: [3D + 2F, D] = [Wq; Wk; Wv; W_gate; W_up]; w_out: [D, D + F]
+    (columns 0..D-1 take the attention output, D.. the SwiGLU activation).
+    """
+    D, F, d = cfg.hidden, cfg.mlp_hidden, cfg.head_dim
+    p = f"single.{idx}."
+    return {
+        "w_in": matrix(seed, p + "w_in", 3 * D + 2 * F, D),
+        "w_out": matrix(seed, p + "w_out", D, D + F),
+        "q_gain": gain(seed, p + "q_gain", d),
+        "k_gain": gain(seed, p + "k_gain", d),
+    }
+
+
+def global_weights(cfg: DitConfig, seed: int) -> Dict[str, np.ndarray]:
+    """Time MLP, the four modulation projections, embeds and the output head."""
+    D = cfg.hidden
+    return {
+        "t_in": matrix(seed, "time.in", D, cfg.time_channels),
+        "t_out": matrix(seed, "time.out", D, D),
+        "mod_dual_img": matrix(seed, "mod.dual_img", 6 * D, D),
+        "mod_dual_txt": matrix(seed, "mod.dual_txt", 6 * D, D),
+        "mod_single": matrix(seed, "mod.single", 3 * D, D),
+        "mod_final": matrix(seed, "mod.final", 2 * D, D),
+        "x_embed": matrix(seed, "embed.x", D, cfg.in_channels),
+        "ctx_embed": matrix(seed, "embed.ctx", D, cfg.txt_channels),
+        "proj_out": matrix(seed, "proj_out", cfg.in_channels, D),
+    }
+
+
+class ModelWeights:
+    """Lazily drawn full-model weights (a 4B-parameter model is ~15 GB as
+    float32, so blocks are drawn on demand and may be dropped after use)."""
+
+    def __init__(self, cfg: DitConfig, seed: int = 0, cache: bool = False):
+        self.cfg, self.seed, self.cache = cfg, seed, cache
+        self._glob: Optional[Dict[str, np.ndarray]] = None
+        self._blocks: Dict[Tuple[str, int], Dict[str, np.ndarray]] = {}
+
+    @property
+    def glob(self) -> Dict[str, np.ndarray]:
+        if self._glob is None:
+            self._glob = global_weights(self.cfg, self.seed)
+        return self._glob
+
+    def dual(self, i: int) -> Dict[str, np.ndarray]:
+        key = ("dual", i)
+        if key in self._blocks:
+            return self._blocks[key]
+        w = dual_weights(self.cfg, self.seed, i)
+        if self.cache:
+            self._blocks[key] = w
+        return w
+
+    def single(self, i: int) -> Dict[str, np.ndarray]:
+        key = ("single", i)
+        if key in self._blocks:
+            return self._blocks[key]
+        w = single_weights(self.cfg, self.seed, i)
+        if self.cache:
+            self._blocks[key] = w
+        return w
+
+
+# ---------------------------------------------------------------- inputs
+
+def text_embedding(cfg: DitConfig, seed: int, n_txt: int) -> np.ndarray:
+    """Prompt embedding [n_txt, C_txt] standing in for the text encoder output."""
+    return normal(seed, "input.txt", (n_txt, cfg.txt_channels))
+
+
+def latents(cfg: DitConfig, seed: int, n_tok: int, name: str = "input.latents") -> np.ndarray:
+    """2x2-patchified latent tokens [n_tok, C_in]."""
+    return normal(seed, name, (n_tok, cfg.in_channels))
+
+
+def residual(cfg: DitConfig, seed: int, rows: int, name: str = "input.x") -> np.ndarray:
+    """Residual-stream activations [rows, D] for block-level tests."""
+    return normal(seed, name, (rows, cfg.hidden))
+
+
+def patch_grid(width_px: int, height_px: int) -> Tuple[int, int]:
+    """(Hp, Wp) patch rows/cols: /8 VAE factor, then 2x2 patches."""
+    return height_px // 16, width_px // 16
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """Shape of one step: batch, text rows, image grid and reference grids."""
+    name: str
+    batch: int
+    n_txt: int
+    img_grid: Tuple[int, int]                       # (Hp, Wp)
+    ref_grids: Tuple[Tuple[int, int], ...] = ()
+    sigma: float = 0.75
+
+    @property
+    def n_img(self) -> int:
+        return self.img_grid[0] * self.img_grid[1]
+
+    @property
+    def n_ref(self) -> int:
+        return sum(h * w for h, w in self.ref_grids)
+
+    @property
+    def seq(self) -> int:
+        return self.n_txt + self.n_img + self.n_ref
+
+
+# Configurations of the measured workloads.
+W_DUAL_TINY = Workload("dual_block_d256_s96", 1, 32, (8, 8), (), 0.5)
+W_SINGLE_1024 = Workload("single_block_1024px_s4608", 1, 512, (64, 64), (), 0.75)
+W_STEP_1024 = Workload("step_1024px_s4608", 1, 512, (64, 64), (), 0.75)
+W_STEP_1024_REF = Workload("step_1024px_1ref_s8704", 1, 512, (64, 64), ((64, 64),), 0.75)
+W_STEP_1920x1088_B4 = Workload("step_1920x1088_b4_s8672", 4, 512, (68, 120), (), 0.75)
+
+
+def step_inputs(cfg: DitConfig, wl: Workload, batch_row: int = 0,
+                input_seed: Optional[int] = None) -> Dict[str, np.ndarray]:
+    """Per-sample inputs: text embedding and image (+reference) latents.
+
+    Batch row b uses input seed b unless `input_seed` is given.
+    """
+    s = batch_row if input_seed is None else input_seed
+    lat = [latents(cfg, s, wl.n_img, "input.latents")]
+    for i, (h, w) in enumerate(wl.ref_grids):
+        lat.append(latents(cfg, s, h * w, f"input.ref{i}"))
+    return {
+        "txt": text_embedding(cfg, s, wl.n_txt),
+        "latents": np.concatenate(lat, axis=0),
+    }
