@@ -1,0 +1,190 @@
+#!/usr/bin/env python3
+"""Benchmark: ms per DiT denoise step at 1024x1024 (4608 tokens) on one MI355X.
+
+One step = global modulation + embeddings + 5 dual-stream + 20 single-stream
+blocks + final layer, through dit_step_forward, on synthetic bf16 weights of
+the FLUX.2 [klein] 4B shape and synthetic inputs (512 text rows of width 7680,
+64 x 64 latent tokens of width 128), all resident in HBM before timing.
+
+Prints one JSON line (rank 0). Timing: W untimed warm-up steps, then K steps
+bracketed by device synchronisation, per-step HIP events on the launch
+stream. A second, separate pass records HIP events around every kernel
+launch (dit_profile_begin/end) to give per-kernel durations for the
+roofline; the headline number comes from the clean pass. The CPU baseline
+times the oracle (float64 NumPy) on one single-stream block of the same
+workload and scales it by FLOP count to a full step.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "ms per DiT denoise step at 1024² (4608 tok) + attn/GEMM TFLOP/s vs peak"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+P100A_STEP_MS = 331.0       # per DiT step, 1024^2, Tenstorrent p100a ("flux2-klein-p100a")
+
+
+def log(msg):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def cpu_baseline(cfg, wl, seconds_hint=True):
+    """Time the oracle on one single-stream block of the workload (float64)."""
+    from oracle import dit_oracle as O
+    from diffusion_transformer_fwd_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    pos = O.position_ids(wl.n_txt, wl.img_grid, wl.ref_grids)
+    S = pos.shape[0]
+    x = synth.residual(cfg, 0, S)[None]
+    gw = synth.global_weights(cfg, 0)
+    mod = O.modulation(gw, np.array([wl.sigma]), cfg.time_channels)
+    cos, sin = O.rope_tables(pos, cfg.axes_dim, cfg.theta)
+    w = synth.single_weights(cfg, 0, 0)
+    t0 = time.perf_counter()
+    O.single_block(x, w, mod["single"], cos, sin, cfg.heads, cfg.eps, cfg.prenorm)
+    dt = time.perf_counter() - t0
+    D, F = cfg.hidden, cfg.mlp_hidden
+    blk_flops = 2.0 * S * D * (3 * D + 2 * F) + 2.0 * S * (D + F) * D + 4.0 * S * S * D
+    return dt, blk_flops, threads
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--profile-steps", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus must be 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from diffusion_transformer_fwd_amd import dit, synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dit.lib()
+    torch.cuda.set_device(0)
+    cfg = synth.FLUX2_KLEIN
+    wl = synth.W_STEP_1024
+
+    log("drawing weights and inputs")
+    t0 = time.time()
+    dw = dit.ModelWeights(synth.ModelWeights(cfg, 0))
+    ins = synth.step_inputs(cfg, wl)
+    txt = dit.to_bf16_device(ins["txt"][None])
+    lat = dit.to_bf16_device(ins["latents"][None])
+    pos = dit.position_ids(wl.n_txt, wl.img_grid, wl.ref_grids)
+    cos, sin = dit.rope_tables(cfg, pos)
+    ws = dit.Workspace()
+    out = torch.empty((1, wl.n_img, cfg.in_channels), dtype=torch.float32, device="cuda")
+    sigma = [wl.sigma]
+    torch.cuda.synchronize()
+    log(f"setup {time.time() - t0:.1f}s")
+
+    def one():
+        dit.step(cfg, dw, txt, lat, sigma, wl.n_img, cos, sin, ws=ws, out=out)
+
+    for _ in range(args.warmup):
+        one()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(K)]
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    for i in range(K):
+        evs[i][0].record()
+        one()
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    per = np.array([a.elapsed_time(b) for a, b in evs])
+    ms = float(wall * 1000.0 / K)
+    log(f"{K} steps: {ms:.3f} ms/step (wall), events median {np.median(per):.3f} "
+        f"p95 {np.percentile(per, 95):.3f}")
+    assert np.all(np.isfinite(out.cpu().numpy())), "non-finite output"
+
+    # per-kernel pass (event pair around every launch)
+    P = max(1, args.profile_steps)
+    dit.profile_begin()
+    for _ in range(P):
+        one()
+    kstats = dit.profile_end()
+    kern = {}
+    for name, s in kstats.items():
+        if s["launches"] == 0:
+            continue
+        e = {"launches_per_step": s["launches"] / P, "ms_per_step": s["total_ms"] / P,
+             "avg_launch_us": 1000.0 * s["total_ms"] / s["launches"]}
+        if s["flops"] > 0 and name in ("gemm", "attention"):
+            e["tflops"] = s["flops"] / (s["total_ms"] * 1e-3) / 1e12
+            e["frac_of_bf16_peak"] = e["tflops"] / PEAK_BF16_TFLOPS
+        if s["bytes"] > 0 and name not in ("gemm", "attention"):
+            e["gbs"] = s["bytes"] / (s["total_ms"] * 1e-3) / 1e9
+            e["frac_of_hbm_peak"] = e["gbs"] / PEAK_HBM_GBS
+        kern[name] = e
+    g, a = kstats["gemm"], kstats["attention"]
+    step_flops = sum(s["flops"] for s in kstats.values()) / P
+    ga_tflops = (g["flops"] + a["flops"]) / ((g["total_ms"] + a["total_ms"]) * 1e-3) / 1e12
+    gemm_per_launch = g["flops"] / g["launches"]
+    gemm_avg_s = g["total_ms"] / g["launches"] * 1e-3
+    achieved = gemm_per_launch / gemm_avg_s / 1e12
+    log("kernels: " + json.dumps(kern))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("CPU baseline: oracle single-stream block (float64)")
+        dt, blk_flops, threads = cpu_baseline(cfg, wl)
+        cpu_ms = dt * 1000.0 * step_flops / blk_flops
+        cpu = {"value": round(cpu_ms, 1), "unit": "ms", "cores": threads, "kind": "oracle",
+               "sample": f"one single-stream block of the 1024px step (S=4608) in float64 "
+                         f"NumPy, {dt:.1f} s, scaled to the 25-block step by FLOP count "
+                         f"({blk_flops / 1e12:.3f} of {step_flops / 1e12:.2f} TFLOP)"}
+        log(f"CPU baseline {cpu_ms:.0f} ms/step ({dt:.1f} s per block, {threads} threads)")
+
+    rec = {
+        "metric": METRIC, "value": round(ms, 4), "unit": "ms", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": round(ms / P100A_STEP_MS, 5),
+        "baseline": {"value": P100A_STEP_MS, "unit": "ms",
+                     "source": "per DiT step at 1024^2 on a Tenstorrent p100a (context only)"},
+        "dtype": "bf16", "data": "synthetic (seeded N(0,1/fan_in) weights, N(0,1) inputs)",
+        "config": {"workload": wl.name, "batch": 1, "seq_len": wl.seq, "n_txt": wl.n_txt,
+                   "n_img": wl.n_img, "blocks": "5 dual + 20 single", "hidden": cfg.hidden,
+                   "heads": cfg.heads, "parallelism": "none (1 GPU)"},
+        "ms_median": round(float(np.median(per)), 4),
+        "ms_p95": round(float(np.percentile(per, 95)), 4),
+        "step_tflop": round(step_flops / 1e12, 4),
+        "step_tflops": round(step_flops / (ms * 1e-3) / 1e12, 1),
+        "gemm_attn_tflops": round(ga_tflops, 1),
+        "gemm_attn_frac_of_peak": round(ga_tflops / PEAK_BF16_TFLOPS, 4),
+        "roofline": {"bound": "mfma", "kernel": "gemm_bf16_kernel",
+                     "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None,
+                     "per_launch_flop": gemm_per_launch, "avg_launch_us": gemm_avg_s * 1e6},
+        "kernels": kern,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,894 @@
+// C ABI of libdit.so: argument validation, workspace planning and the launch
+// sequence of the DiT step (the entry points and their maths are documented
+// in include/dit.h). Every check runs before the first launch, so an error
+// return leaves device memory untouched.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/dit.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+#define DIT_TRY(expr)                                                             \
+  do {                                                                            \
+    const hipError_t e_ = (expr);                                                 \
+    if (e_ != hipSuccess)                                                         \
+      return fail(DIT_E_HIP, "%s: %s", #expr, hipGetErrorString(e_));             \
+  } while (0)
+
+#define DIT_CHECK(status)                                                         \
+  do {                                                                            \
+    const int s_ = (status);                                                      \
+    if (s_ != DIT_OK) return s_;                                                  \
+  } while (0)
+
+constexpr size_t kAlign = 256;
+constexpr uint64_t kMaxBufferBytes = 0xFFFFFFFFull;  // 32-bit buffer offsets
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// ---------------------------------------------------------------- profiling
+// Optional event pairs around every launch (dit_profile_begin/end).
+struct ProfRecord {
+  int kind;
+  double flops, bytes;
+  hipEvent_t start, stop;
+};
+struct Profiler {
+  std::mutex mu;
+  bool on = false;
+  std::vector<ProfRecord> recs;
+  std::vector<hipEvent_t> pool;
+};
+Profiler g_prof;
+
+hipEvent_t prof_event() {
+  if (!g_prof.pool.empty()) {
+    hipEvent_t e = g_prof.pool.back();
+    g_prof.pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Runs `launch` (returning hipError_t); when profiling, brackets it with events.
+template <class F>
+hipError_t timed(int kind, double flops, double bytes, hipStream_t st, F&& launch) {
+  if (!g_prof.on) return launch();
+  std::lock_guard<std::mutex> lock(g_prof.mu);
+  ProfRecord r{kind, flops, bytes, prof_event(), prof_event()};
+  if (!r.start || !r.stop) return hipErrorOutOfMemory;
+  hipError_t e = hipEventRecord(r.start, st);
+  if (e != hipSuccess) return e;
+  e = launch();
+  if (e != hipSuccess) return e;
+  e = hipEventRecord(r.stop, st);
+  if (e != hipSuccess) return e;
+  g_prof.recs.push_back(r);
+  return hipSuccess;
+}
+
+// ---------------------------------------------------------------- layouts
+
+struct BlockLayout {
+  int64_t R = 0, S_pad = 0;
+  int64_t u_cols = 0;
+  size_t h = 0, u = 0, d6 = 0, o = 0, q = 0, k = 0, vt = 0, total = 0;
+};
+
+// kind: 0 = dual, 1 = single
+BlockLayout block_layout(const dit_config& c, int kind, int64_t B, int64_t S) {
+  BlockLayout L;
+  const int64_t D = c.hidden, F = c.mlp_hidden;
+  L.R = B * S;
+  L.S_pad = round_up(S, 128);
+  L.u_cols = kind == 0 ? std::max<int64_t>(3 * D, F) : 3 * D;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  L.h = take((size_t)L.R * D * 2);
+  L.u = take((size_t)L.R * L.u_cols * 2);
+  if (kind == 1) L.d6 = take((size_t)L.R * (D + F) * 2);
+  else L.o = take((size_t)L.R * D * 2);
+  const size_t qk = (size_t)B * c.heads * L.S_pad * c.head_dim * 2;
+  L.q = take(qk);
+  L.k = take(qk);
+  L.vt = take(qk);
+  L.total = off;
+  return L;
+}
+
+struct ModLayout {
+  size_t e = 0, t1 = 0, m = 0, total = 0;
+};
+
+ModLayout mod_layout(const dit_config& c, int64_t B) {
+  ModLayout L;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  L.e = take((size_t)B * c.time_channels * 4);
+  L.t1 = take((size_t)B * c.hidden * 4);
+  L.m = take((size_t)B * c.hidden * 4);
+  L.total = off;
+  return L;
+}
+
+struct StepLayout {
+  size_t x = 0, mod = 0, modws = 0, block = 0, total = 0;
+};
+
+StepLayout step_layout(const dit_config& c, int64_t B, int64_t S) {
+  StepLayout L;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  L.x = take((size_t)B * S * c.hidden * 4);
+  L.mod = take((size_t)B * DIT_MOD_ROWS * c.hidden * 4);
+  L.modws = take(mod_layout(c, B).total);
+  const size_t blk = std::max(block_layout(c, 0, B, S).total, block_layout(c, 1, B, S).total);
+  L.block = take(blk);
+  L.total = off;
+  return L;
+}
+
+// ---------------------------------------------------------------- validation
+
+int check_config(const dit_config* c) {
+  if (!c) return fail(DIT_E_NULL, "config is NULL");
+  if (c->head_dim != 128)
+    return fail(DIT_E_UNSUPPORTED, "head_dim %d: only 128 is supported", c->head_dim);
+  if (c->heads < 1 || c->heads > 256)
+    return fail(DIT_E_SHAPE, "heads %d out of range [1, 256]", c->heads);
+  if (c->hidden != c->heads * c->head_dim)
+    return fail(DIT_E_SHAPE, "hidden %d != heads %d x head_dim %d", c->hidden, c->heads,
+                c->head_dim);
+  if (c->hidden % 64 || c->hidden > 4096)
+    return fail(DIT_E_UNSUPPORTED, "hidden %d must be a multiple of 64 and <= 4096", c->hidden);
+  if (c->mlp_hidden < 64 || c->mlp_hidden % 64)
+    return fail(DIT_E_UNSUPPORTED, "mlp_hidden %d must be a positive multiple of 64",
+                c->mlp_hidden);
+  if (c->n_dual < 0 || c->n_single < 0 || c->n_dual > 1024 || c->n_single > 1024)
+    return fail(DIT_E_SHAPE, "block counts %d/%d out of range", c->n_dual, c->n_single);
+  if (c->in_channels < 64 || c->in_channels % 64)
+    return fail(DIT_E_UNSUPPORTED, "in_channels %d must be a positive multiple of 64",
+                c->in_channels);
+  if (c->txt_channels < 64 || c->txt_channels % 64)
+    return fail(DIT_E_UNSUPPORTED, "txt_channels %d must be a positive multiple of 64",
+                c->txt_channels);
+  if (c->time_channels < 2 || c->time_channels % 8 || c->time_channels > 4096)
+    return fail(DIT_E_UNSUPPORTED, "time_channels %d must be even, a multiple of 8, <= 4096",
+                c->time_channels);
+  int sum = 0;
+  for (int a = 0; a < 4; ++a) {
+    if (c->axes_dim[a] < 0 || c->axes_dim[a] % 2)
+      return fail(DIT_E_SHAPE, "axes_dim[%d] = %d must be even and >= 0", a, c->axes_dim[a]);
+    sum += c->axes_dim[a];
+  }
+  if (sum != c->head_dim)
+    return fail(DIT_E_SHAPE, "sum of axes_dim %d != head_dim %d", sum, c->head_dim);
+  if (c->prenorm != DIT_PRENORM_RMS && c->prenorm != DIT_PRENORM_LAYER)
+    return fail(DIT_E_VALUE, "prenorm %d is neither RMS (0) nor LAYER (1)", c->prenorm);
+  if (!std::isfinite(c->theta) || c->theta <= 1.0f)
+    return fail(DIT_E_VALUE, "theta %g must be finite and > 1", (double)c->theta);
+  if (!std::isfinite(c->eps) || c->eps < 0.0f)
+    return fail(DIT_E_VALUE, "eps %g must be finite and >= 0", (double)c->eps);
+  return DIT_OK;
+}
+
+int check_batch_seq(int32_t B, int64_t S) {
+  if (B < 1 || B > DIT_MAX_BATCH) return fail(DIT_E_SHAPE, "B %d out of range [1, %d]", B, DIT_MAX_BATCH);
+  if (S < 1 || S > (1 << 20)) return fail(DIT_E_SHAPE, "S %lld out of range [1, 2^20]", (long long)S);
+  return DIT_OK;
+}
+
+int check_ws(const void* ws, size_t have, size_t need) {
+  if (need > 0 && !ws) return fail(DIT_E_NULL, "workspace is NULL (%zu bytes needed)", need);
+  if (have < need) return fail(DIT_E_WORKSPACE, "workspace %zu bytes < %zu needed", have, need);
+  if (!aligned(ws, kAlign)) return fail(DIT_E_WORKSPACE, "workspace not 256-byte aligned");
+  return DIT_OK;
+}
+
+int check_ptr(const void* p, const char* what, size_t align = 16) {
+  if (!p) return fail(DIT_E_NULL, "%s is NULL", what);
+  if (!aligned(p, align)) return fail(DIT_E_SHAPE, "%s is not %zu-byte aligned", what, align);
+  return DIT_OK;
+}
+
+// Every GEMM operand must stay addressable with 32-bit byte offsets.
+int check_operand_sizes(const dit_config& c, int64_t rows) {
+  const uint64_t D = c.hidden, F = c.mlp_hidden;
+  const uint64_t widest = std::max<uint64_t>({3 * D, D + F, F, (uint64_t)c.txt_channels});
+  if ((uint64_t)rows * widest * 2 > kMaxBufferBytes)
+    return fail(DIT_E_UNSUPPORTED, "%lld rows x %llu columns exceeds 4 GiB per operand",
+                (long long)rows, (unsigned long long)widest);
+  if ((3 * D + 2 * F) * D * 2 > kMaxBufferBytes || D * (D + F) * 2 > kMaxBufferBytes)
+    return fail(DIT_E_UNSUPPORTED, "weights exceed 4 GiB per matrix");
+  return DIT_OK;
+}
+
+int check_dual_weights(const dit_dual_weights* w) {
+  if (!w) return fail(DIT_E_NULL, "dual weights are NULL");
+  for (int s = 0; s < 2; ++s) {
+    DIT_CHECK(check_ptr(w->qkv[s], "dual qkv"));
+    DIT_CHECK(check_ptr(w->out[s], "dual out"));
+    DIT_CHECK(check_ptr(w->mlp_in[s], "dual mlp_in"));
+    DIT_CHECK(check_ptr(w->mlp_out[s], "dual mlp_out"));
+    DIT_CHECK(check_ptr(w->q_gain[s], "dual q_gain"));
+    DIT_CHECK(check_ptr(w->k_gain[s], "dual k_gain"));
+  }
+  return DIT_OK;
+}
+
+int check_single_weights(const dit_single_weights* w) {
+  if (!w) return fail(DIT_E_NULL, "single weights are NULL");
+  DIT_CHECK(check_ptr(w->w_in, "single w_in"));
+  DIT_CHECK(check_ptr(w->w_out, "single w_out"));
+  DIT_CHECK(check_ptr(w->q_gain, "single q_gain"));
+  DIT_CHECK(check_ptr(w->k_gain, "single k_gain"));
+  return DIT_OK;
+}
+
+int check_model_weights(const dit_config& c, const dit_model_weights* w, bool blocks) {
+  if (!w) return fail(DIT_E_NULL, "model weights are NULL");
+  DIT_CHECK(check_ptr(w->t_in, "t_in"));
+  DIT_CHECK(check_ptr(w->t_out, "t_out"));
+  DIT_CHECK(check_ptr(w->mod_dual_img, "mod_dual_img"));
+  DIT_CHECK(check_ptr(w->mod_dual_txt, "mod_dual_txt"));
+  DIT_CHECK(check_ptr(w->mod_single, "mod_single"));
+  DIT_CHECK(check_ptr(w->mod_final, "mod_final"));
+  if (!blocks) return DIT_OK;
+  DIT_CHECK(check_ptr(w->x_embed, "x_embed"));
+  DIT_CHECK(check_ptr(w->ctx_embed, "ctx_embed"));
+  DIT_CHECK(check_ptr(w->proj_out, "proj_out"));
+  if (c.n_dual > 0 && !w->dual) return fail(DIT_E_NULL, "dual block array is NULL");
+  if (c.n_single > 0 && !w->single) return fail(DIT_E_NULL, "single block array is NULL");
+  for (int i = 0; i < c.n_dual; ++i) DIT_CHECK(check_dual_weights(&w->dual[i]));
+  for (int i = 0; i < c.n_single; ++i) DIT_CHECK(check_single_weights(&w->single[i]));
+  return DIT_OK;
+}
+
+int check_sigmas(const float* sigma, int32_t B) {
+  if (!sigma) return fail(DIT_E_NULL, "sigma_host is NULL");
+  for (int b = 0; b < B; ++b)
+    if (!std::isfinite(sigma[b]))
+      return fail(DIT_E_VALUE, "sigma[%d] is not finite", b);
+  return DIT_OK;
+}
+
+// ---------------------------------------------------------------- launches
+
+using dit::bf16_t;
+
+const bf16_t* bf(const void* p) { return static_cast<const bf16_t*>(p); }
+bf16_t* bf(void* p) { return static_cast<bf16_t*>(p); }
+char* at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
+
+dit::GemmProblem problem(const void* A, int64_t lda, const void* W, int64_t ldw, int M, int N,
+                         int K, int epi, void* C, int64_t ldc) {
+  dit::GemmProblem p{};
+  p.A = bf(A);
+  p.W = bf(W);
+  p.C = C;
+  p.lda = lda;
+  p.ldw = ldw;
+  p.ldc = ldc;
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  p.epi = epi;
+  p.seg_len = std::max(M, 1);
+  p.seg_stride = 0;
+  p.seg_off = 0;
+  return p;
+}
+
+void set_rows(dit::GemmProblem& p, int seg_len, int64_t seg_stride, int seg_off) {
+  p.seg_len = std::max(seg_len, 1);
+  p.seg_stride = seg_stride;
+  p.seg_off = seg_off;
+}
+
+int run_gemm(dit::GemmBatch& g, hipStream_t st) {
+  double flops = 0, bytes = 0;
+  for (int i = 0; i < g.count; ++i) {
+    const dit::GemmProblem& p = g.p[i];
+    const double n_w = p.epi == dit::EPI_SWIGLU ? 2.0 * p.N : (double)p.N;
+    flops += 2.0 * p.M * n_w * p.K;
+    const double out = p.epi == dit::EPI_RESID ? 8.0 : (p.epi == dit::EPI_F32 ? 4.0 : 2.0);
+    bytes += 2.0 * p.M * p.K + 2.0 * n_w * p.K + out * p.M * p.N;
+  }
+  DIT_TRY(timed(DIT_K_GEMM, flops, bytes, st, [&] { return dit::gemm_launch(g, st); }));
+  return DIT_OK;
+}
+
+int run_norm(const dit::NormArgs& na, hipStream_t st) {
+  double rows = 0;
+  for (int i = 0; i < na.nseg; ++i) rows += (double)na.B * na.seg[i].seg_len;
+  DIT_TRY(timed(DIT_K_MODNORM, 0.0, rows * na.D * 6.0, st,
+                [&] { return dit::modnorm_launch(na, st); }));
+  return DIT_OK;
+}
+
+int run_qk_rope(const dit::QkRopeArgs& qa, hipStream_t st) {
+  const double tok = (double)qa.B * qa.S;
+  DIT_TRY(timed(DIT_K_QK_ROPE, 0.0, tok * 3.0 * qa.D * 2.0 * 2.0, st,
+                [&] { return dit::qk_rope_launch(qa, st); }));
+  return DIT_OK;
+}
+
+int run_attention(const dit::AttnArgs& aa, hipStream_t st) {
+  const double bh = (double)aa.B * aa.H, S = (double)aa.S;
+  DIT_TRY(timed(DIT_K_ATTENTION, 4.0 * bh * S * S * 128.0, bh * S * 128.0 * 2.0 * 4.0, st,
+                [&] { return dit::attention_launch(aa, st); }));
+  return DIT_OK;
+}
+
+int run_gemv(const dit::GemvArgs& g, hipStream_t st) {
+  double bytes = 0;
+  for (int i = 0; i < g.nseg; ++i) bytes += 2.0 * g.seg[i].rows * g.K;
+  bytes += 4.0 * g.B * (g.K + g.total_rows);
+  DIT_TRY(timed(DIT_K_GEMV, 2.0 * g.B * g.total_rows * g.K, bytes, st,
+                [&] { return dit::gemv_launch(g, st); }));
+  return DIT_OK;
+}
+
+int launch_modulation(const dit_config& c, const dit_model_weights& w, const float* sigma,
+                      int32_t B, float* mod, void* ws, hipStream_t st) {
+  const ModLayout L = mod_layout(c, B);
+  const int64_t D = c.hidden;
+  float* e = reinterpret_cast<float*>(at(ws, L.e));
+  float* t1 = reinterpret_cast<float*>(at(ws, L.t1));
+  float* m = reinterpret_cast<float*>(at(ws, L.m));
+  for (int b0 = 0; b0 < B; b0 += 4) {
+    const int nb = std::min(4, B - b0);
+    dit::TimeArgs ta{};
+    ta.e = e;
+    ta.B = nb;
+    ta.C = c.time_channels;
+    for (int i = 0; i < nb; ++i) ta.sigma[i] = sigma[b0 + i];
+    DIT_TRY(timed(DIT_K_TIME, 0.0, 4.0 * nb * c.time_channels, st,
+                  [&] { return dit::time_features_launch(ta, st); }));
+    // t1 = SiLU(W_in e)
+    dit::GemvArgs g{};
+    g.x = e;
+    g.y = t1;
+    g.ldy = D;
+    g.B = nb;
+    g.K = c.time_channels;
+    g.act_in = dit::ACT_NONE;
+    g.act_out = dit::ACT_SILU;
+    g.nseg = 1;
+    g.total_rows = (int)D;
+    g.seg[0] = dit::GemvSegment{bf(w.t_in), 0, (int)D, 0};
+    DIT_CHECK(run_gemv(g, st));
+    // m = SiLU(W_out t1)
+    g.x = t1;
+    g.y = m;
+    g.K = (int)D;
+    g.seg[0] = dit::GemvSegment{bf(w.t_out), 0, (int)D, 0};
+    DIT_CHECK(run_gemv(g, st));
+    // mod[b] = [W_dual_img m; W_dual_txt m; W_single m; W_final m]
+    g.x = m;
+    g.y = mod + (int64_t)b0 * DIT_MOD_ROWS * D;
+    g.ldy = DIT_MOD_ROWS * D;
+    g.act_out = dit::ACT_NONE;
+    g.nseg = 4;
+    g.seg[0] = dit::GemvSegment{bf(w.mod_dual_img), DIT_MOD_DUAL_IMG * D, (int)(6 * D), 0};
+    g.seg[1] = dit::GemvSegment{bf(w.mod_dual_txt), DIT_MOD_DUAL_TXT * D, (int)(6 * D), (int)(6 * D)};
+    g.seg[2] = dit::GemvSegment{bf(w.mod_single), DIT_MOD_SINGLE * D, (int)(3 * D), (int)(12 * D)};
+    g.seg[3] = dit::GemvSegment{bf(w.mod_final), DIT_MOD_FINAL * D, (int)(2 * D), (int)(15 * D)};
+    g.total_rows = (int)(17 * D);
+    DIT_CHECK(run_gemv(g, st));
+  }
+  return DIT_OK;
+}
+
+int launch_dual(const dit_config& c, const dit_dual_weights& w, float* x, int32_t B, int64_t S,
+                int64_t n_txt, const float* mod_txt, const float* mod_img, int64_t mbs,
+                const float* cos_t, const float* sin_t, void* ws, hipStream_t st) {
+  const BlockLayout L = block_layout(c, 0, B, S);
+  const int64_t D = c.hidden, F = c.mlp_hidden, n_img = S - n_txt;
+  const int64_t Rt = (int64_t)B * n_txt, Ri = (int64_t)B * n_img;
+  bf16_t* h = bf(at(ws, L.h));
+  bf16_t* u = bf(at(ws, L.u));
+  bf16_t* o = bf(at(ws, L.o));
+  const float* mods[2] = {mod_txt, mod_img};
+  const int64_t rows[2] = {Rt, Ri};
+  const int64_t first[2] = {0, Rt};
+  const int64_t segoff[2] = {0, n_txt};
+  const int64_t seglen[2] = {n_txt, n_img};
+
+  auto norm = [&](int shift_row, int scale_row) -> int {
+    dit::NormArgs na{};
+    na.x = x;
+    na.h = h;
+    na.S = S;
+    na.mod_bstride = mbs;
+    na.D = (int)D;
+    na.B = B;
+    na.kind = c.prenorm;
+    na.eps = c.eps;
+    na.nseg = 2;
+    for (int s = 0; s < 2; ++s) {
+      na.seg[s].shift = mods[s] + shift_row * D;
+      na.seg[s].scale = mods[s] + scale_row * D;
+      na.seg[s].out_base = first[s];
+      na.seg[s].seg_off = (int)segoff[s];
+      na.seg[s].seg_len = (int)seglen[s];
+    }
+    DIT_CHECK(run_norm(na, st));
+    return DIT_OK;
+  };
+  // stream-major GEMM problems over h / o / act rows -> x rows (residual)
+  auto resid = [&](const bf16_t* A, int64_t lda, const void* const* W, int K, int gate_row)
+      -> int {
+    dit::GemmBatch g{};
+    g.count = 0;
+    for (int s = 0; s < 2; ++s) {
+      if (rows[s] == 0) continue;
+      dit::GemmProblem p = problem(A + first[s] * lda, lda, W[s], K, (int)rows[s], (int)D, K,
+                                   dit::EPI_RESID, x, D);
+      set_rows(p, (int)seglen[s], S, (int)segoff[s]);
+      p.gate = mods[s] + gate_row * D;
+      p.gate_bstride = mbs;
+      g.p[g.count++] = p;
+    }
+    return run_gemm(g, st);
+  };
+
+  // attention branch
+  DIT_CHECK(norm(0, 1));
+  {
+    dit::GemmBatch g{};
+    for (int s = 0; s < 2; ++s) {
+      if (rows[s] == 0) continue;
+      g.p[g.count++] = problem(h + first[s] * D, D, w.qkv[s], D, (int)rows[s], (int)(3 * D),
+                               (int)D, dit::EPI_BF16, u + first[s] * L.u_cols, L.u_cols);
+    }
+    DIT_CHECK(run_gemm(g, st));
+  }
+  dit::QkRopeArgs qa{};
+  qa.u = u;
+  qa.q = bf(at(ws, L.q));
+  qa.k = bf(at(ws, L.k));
+  qa.vt = bf(at(ws, L.vt));
+  qa.cos_t = cos_t;
+  qa.sin_t = sin_t;
+  for (int s = 0; s < 2; ++s) {
+    qa.q_gain[s] = w.q_gain[s];
+    qa.k_gain[s] = w.k_gain[s];
+  }
+  qa.ldu = L.u_cols;
+  qa.S = S;
+  qa.S_pad = L.S_pad;
+  qa.n_txt = n_txt;
+  qa.B = B;
+  qa.H = c.heads;
+  qa.D = (int)D;
+  qa.stream_major = 1;
+  qa.eps = c.eps;
+  DIT_CHECK(run_qk_rope(qa, st));
+  dit::AttnArgs aa{};
+  aa.q = qa.q;
+  aa.k = qa.k;
+  aa.vt = qa.vt;
+  aa.o = o;
+  aa.S = S;
+  aa.S_pad = L.S_pad;
+  aa.ldo = D;
+  aa.n_txt = n_txt;
+  aa.B = B;
+  aa.H = c.heads;
+  aa.stream_major = 1;
+  aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)c.head_dim));
+  DIT_CHECK(run_attention(aa, st));
+  DIT_CHECK(resid(o, D, w.out, (int)D, 2));
+
+  // MLP branch
+  DIT_CHECK(norm(3, 4));
+  {
+    dit::GemmBatch g{};
+    for (int s = 0; s < 2; ++s) {
+      if (rows[s] == 0) continue;
+      g.p[g.count++] = problem(h + first[s] * D, D, w.mlp_in[s], D, (int)rows[s], (int)F,
+                               (int)D, dit::EPI_SWIGLU, u + first[s] * F, F);
+    }
+    DIT_CHECK(run_gemm(g, st));
+  }
+  DIT_CHECK(resid(u, F, w.mlp_out, (int)F, 5));
+  return DIT_OK;
+}
+
+int launch_single(const dit_config& c, const dit_single_weights& w, float* x, int32_t B,
+                  int64_t S, const float* mod, int64_t mbs, const float* cos_t,
+                  const float* sin_t, void* ws, hipStream_t st) {
+  const BlockLayout L = block_layout(c, 1, B, S);
+  const int64_t D = c.hidden, F = c.mlp_hidden, R = L.R;
+  bf16_t* h = bf(at(ws, L.h));
+  bf16_t* u = bf(at(ws, L.u));
+  bf16_t* d6 = bf(at(ws, L.d6));
+  const int64_t ld6 = D + F;
+
+  dit::NormArgs na{};
+  na.x = x;
+  na.h = h;
+  na.S = S;
+  na.mod_bstride = mbs;
+  na.D = (int)D;
+  na.B = B;
+  na.kind = c.prenorm;
+  na.eps = c.eps;
+  na.nseg = 1;
+  na.seg[0].shift = mod;
+  na.seg[0].scale = mod + D;
+  na.seg[0].out_base = 0;
+  na.seg[0].seg_off = 0;
+  na.seg[0].seg_len = (int)S;
+  DIT_CHECK(run_norm(na, st));
+
+  {
+    dit::GemmBatch g{};
+    g.count = 2;
+    g.p[0] = problem(h, D, w.w_in, D, (int)R, (int)(3 * D), (int)D, dit::EPI_BF16, u, 3 * D);
+    g.p[1] = problem(h, D, bf(w.w_in) + 3 * D * D, D, (int)R, (int)F, (int)D, dit::EPI_SWIGLU,
+                     d6 + D, ld6);
+    DIT_CHECK(run_gemm(g, st));
+  }
+  dit::QkRopeArgs qa{};
+  qa.u = u;
+  qa.q = bf(at(ws, L.q));
+  qa.k = bf(at(ws, L.k));
+  qa.vt = bf(at(ws, L.vt));
+  qa.cos_t = cos_t;
+  qa.sin_t = sin_t;
+  qa.q_gain[0] = qa.q_gain[1] = w.q_gain;
+  qa.k_gain[0] = qa.k_gain[1] = w.k_gain;
+  qa.ldu = 3 * D;
+  qa.S = S;
+  qa.S_pad = L.S_pad;
+  qa.n_txt = 0;
+  qa.B = B;
+  qa.H = c.heads;
+  qa.D = (int)D;
+  qa.stream_major = 0;
+  qa.eps = c.eps;
+  DIT_CHECK(run_qk_rope(qa, st));
+  dit::AttnArgs aa{};
+  aa.q = qa.q;
+  aa.k = qa.k;
+  aa.vt = qa.vt;
+  aa.o = d6;
+  aa.S = S;
+  aa.S_pad = L.S_pad;
+  aa.ldo = ld6;
+  aa.n_txt = 0;
+  aa.B = B;
+  aa.H = c.heads;
+  aa.stream_major = 0;
+  aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)c.head_dim));
+  DIT_CHECK(run_attention(aa, st));
+  {
+    dit::GemmBatch g{};
+    g.count = 1;
+    g.p[0] = problem(d6, ld6, w.w_out, ld6, (int)R, (int)D, (int)ld6, dit::EPI_RESID, x, D);
+    set_rows(g.p[0], (int)S, S, 0);
+    g.p[0].gate = mod + 2 * D;
+    g.p[0].gate_bstride = mbs;
+    DIT_CHECK(run_gemm(g, st));
+  }
+  return DIT_OK;
+}
+
+int check_block_common(const dit_config* cfg, float* x, int32_t B, int64_t S,
+                       int64_t mod_batch_stride, const float* cos_t, const float* sin_t) {
+  DIT_CHECK(check_config(cfg));
+  DIT_CHECK(check_batch_seq(B, S));
+  DIT_CHECK(check_ptr(x, "x"));
+  DIT_CHECK(check_ptr(cos_t, "cos"));
+  DIT_CHECK(check_ptr(sin_t, "sin"));
+  if (mod_batch_stride < 0 || mod_batch_stride % 4)
+    return fail(DIT_E_SHAPE, "mod_batch_stride %lld must be >= 0 and a multiple of 4",
+                (long long)mod_batch_stride);
+  DIT_CHECK(check_operand_sizes(*cfg, (int64_t)B * S));
+  return DIT_OK;
+}
+
+}  // namespace
+
+// ======================================================================= ABI
+
+extern "C" {
+
+const char* dit_status_string(int status) {
+  switch (status) {
+    case DIT_OK: return "ok";
+    case DIT_E_NULL: return "null pointer";
+    case DIT_E_SHAPE: return "inconsistent or out-of-range sizes";
+    case DIT_E_UNSUPPORTED: return "unsupported configuration";
+    case DIT_E_WORKSPACE: return "workspace too small or misaligned";
+    case DIT_E_HIP: return "HIP runtime error";
+    case DIT_E_VALUE: return "invalid scalar value";
+    default: return "unknown status";
+  }
+}
+
+const char* dit_last_error(void) { return g_last_error.c_str(); }
+
+int dit_config_check(const dit_config* cfg) { return check_config(cfg); }
+
+int64_t dit_position_ids(int64_t n_txt, int32_t hp, int32_t wp, int32_t n_ref,
+                         const int32_t* ref_hp, const int32_t* ref_wp, int32_t* out,
+                         int64_t cap_rows) {
+  if (n_txt < 0 || hp < 0 || wp < 0)
+    return fail(DIT_E_SHAPE, "negative size (n_txt %lld, grid %d x %d)", (long long)n_txt, hp, wp);
+  if (n_ref < 0 || n_ref > 3) return fail(DIT_E_SHAPE, "n_ref %d out of range [0, 3]", n_ref);
+  if (n_ref > 0 && (!ref_hp || !ref_wp)) return fail(DIT_E_NULL, "reference grids are NULL");
+  int64_t S = n_txt + (int64_t)hp * wp;
+  for (int i = 0; i < n_ref; ++i) {
+    if (ref_hp[i] < 0 || ref_wp[i] < 0)
+      return fail(DIT_E_SHAPE, "reference %d grid %d x %d is negative", i, ref_hp[i], ref_wp[i]);
+    S += (int64_t)ref_hp[i] * ref_wp[i];
+  }
+  if (S > cap_rows) return fail(DIT_E_SHAPE, "%lld rows exceed capacity %lld", (long long)S,
+                                (long long)cap_rows);
+  if (S > 0 && !out) return fail(DIT_E_NULL, "out is NULL");
+  int64_t r = 0;
+  auto put = [&](int t, int h, int w, int l) {
+    out[4 * r + 0] = t;
+    out[4 * r + 1] = h;
+    out[4 * r + 2] = w;
+    out[4 * r + 3] = l;
+    ++r;
+  };
+  for (int64_t l = 0; l < n_txt; ++l) put(0, 0, 0, (int)l);
+  for (int i = 0; i < hp; ++i)
+    for (int j = 0; j < wp; ++j) put(0, i, j, 0);
+  for (int k = 0; k < n_ref; ++k)
+    for (int i = 0; i < ref_hp[k]; ++i)
+      for (int j = 0; j < ref_wp[k]; ++j) put(10 + 10 * k, i, j, 0);
+  return S;
+}
+
+size_t dit_workspace_bytes(const dit_config* cfg, int32_t kind, int32_t B, int64_t S) {
+  if (check_config(cfg) != DIT_OK) return 0;
+  if (kind == DIT_WS_MOD) {
+    if (B < 1 || B > DIT_MAX_BATCH) {
+      fail(DIT_E_SHAPE, "B %d out of range", B);
+      return 0;
+    }
+    return mod_layout(*cfg, B).total;
+  }
+  if (check_batch_seq(B, S) != DIT_OK) return 0;
+  switch (kind) {
+    case DIT_WS_DUAL: return block_layout(*cfg, 0, B, S).total;
+    case DIT_WS_SINGLE: return block_layout(*cfg, 1, B, S).total;
+    case DIT_WS_STEP: return step_layout(*cfg, B, S).total;
+    default: fail(DIT_E_VALUE, "unknown workspace kind %d", kind); return 0;
+  }
+}
+
+int dit_rope_tables_build(const dit_config* cfg, const int32_t* pos_dev, int64_t S,
+                          float* cos_dev, float* sin_dev, dit_stream_t stream) {
+  DIT_CHECK(check_config(cfg));
+  if (S < 0 || S > (1 << 20)) return fail(DIT_E_SHAPE, "S %lld out of range", (long long)S);
+  if (S == 0) return DIT_OK;
+  DIT_CHECK(check_ptr(pos_dev, "pos", 4));
+  DIT_CHECK(check_ptr(cos_dev, "cos"));
+  DIT_CHECK(check_ptr(sin_dev, "sin"));
+  dit::RopeArgs ra{};
+  ra.pos = pos_dev;
+  ra.cos_t = cos_dev;
+  ra.sin_t = sin_dev;
+  ra.S = S;
+  ra.pairs = cfg->head_dim / 2;
+  int j = 0;
+  for (int a = 0; a < 4; ++a) {
+    const int dim = cfg->axes_dim[a];
+    for (int p = 0; p < dim / 2; ++p, ++j) {
+      ra.axis_of[j] = a;
+      ra.omega[j] = std::pow((double)cfg->theta, -2.0 * p / (double)dim);
+    }
+  }
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  DIT_TRY(timed(DIT_K_ROPE_TABLES, 0.0, (double)S * (16.0 + ra.pairs * 8.0), st,
+                [&] { return dit::rope_tables_launch(ra, st); }));
+  return DIT_OK;
+}
+
+int dit_modulation_forward(const dit_config* cfg, const dit_model_weights* w,
+                           const float* sigma_host, int32_t B, float* mod_dev, void* ws,
+                           size_t ws_bytes, dit_stream_t stream) {
+  DIT_CHECK(check_config(cfg));
+  if (B < 1 || B > DIT_MAX_BATCH) return fail(DIT_E_SHAPE, "B %d out of range", B);
+  DIT_CHECK(check_model_weights(*cfg, w, false));
+  DIT_CHECK(check_sigmas(sigma_host, B));
+  DIT_CHECK(check_ptr(mod_dev, "mod"));
+  DIT_CHECK(check_ws(ws, ws_bytes, mod_layout(*cfg, B).total));
+  return launch_modulation(*cfg, *w, sigma_host, B, mod_dev, ws,
+                           reinterpret_cast<hipStream_t>(stream));
+}
+
+int dit_dual_block_forward(const dit_config* cfg, const dit_dual_weights* w, float* x,
+                           int32_t B, int64_t S, int64_t n_txt, const float* mod_txt,
+                           const float* mod_img, int64_t mod_batch_stride,
+                           const float* cos_dev, const float* sin_dev, void* ws,
+                           size_t ws_bytes, dit_stream_t stream) {
+  DIT_CHECK(check_block_common(cfg, x, B, S, mod_batch_stride, cos_dev, sin_dev));
+  if (n_txt < 0 || n_txt > S)
+    return fail(DIT_E_SHAPE, "n_txt %lld out of range [0, S=%lld]", (long long)n_txt,
+                (long long)S);
+  DIT_CHECK(check_dual_weights(w));
+  DIT_CHECK(check_ptr(mod_txt, "mod_txt"));
+  DIT_CHECK(check_ptr(mod_img, "mod_img"));
+  DIT_CHECK(check_ws(ws, ws_bytes, block_layout(*cfg, 0, B, S).total));
+  return launch_dual(*cfg, *w, x, B, S, n_txt, mod_txt, mod_img, mod_batch_stride, cos_dev,
+                     sin_dev, ws, reinterpret_cast<hipStream_t>(stream));
+}
+
+int dit_single_block_forward(const dit_config* cfg, const dit_single_weights* w, float* x,
+                             int32_t B, int64_t S, const float* mod, int64_t mod_batch_stride,
+                             const float* cos_dev, const float* sin_dev, void* ws,
+                             size_t ws_bytes, dit_stream_t stream) {
+  DIT_CHECK(check_block_common(cfg, x, B, S, mod_batch_stride, cos_dev, sin_dev));
+  DIT_CHECK(check_single_weights(w));
+  DIT_CHECK(check_ptr(mod, "mod"));
+  DIT_CHECK(check_ws(ws, ws_bytes, block_layout(*cfg, 1, B, S).total));
+  return launch_single(*cfg, *w, x, B, S, mod, mod_batch_stride, cos_dev, sin_dev, ws,
+                       reinterpret_cast<hipStream_t>(stream));
+}
+
+int dit_step_forward(const dit_config* cfg, const dit_model_weights* w, const void* txt,
+                     const void* latents, const float* sigma_host, int32_t B, int64_t n_txt,
+                     int64_t n_img, int64_t n_ref, const float* cos_dev, const float* sin_dev,
+                     float* v_out, void* ws, size_t ws_bytes, dit_stream_t stream) {
+  DIT_CHECK(check_config(cfg));
+  if (n_txt < 0 || n_img < 1 || n_ref < 0)
+    return fail(DIT_E_SHAPE, "token counts n_txt %lld, n_img %lld, n_ref %lld invalid",
+                (long long)n_txt, (long long)n_img, (long long)n_ref);
+  const int64_t S = n_txt + n_img + n_ref;
+  DIT_CHECK(check_batch_seq(B, S));
+  DIT_CHECK(check_operand_sizes(*cfg, (int64_t)B * S));
+  DIT_CHECK(check_model_weights(*cfg, w, true));
+  if (n_txt > 0) DIT_CHECK(check_ptr(txt, "txt"));
+  DIT_CHECK(check_ptr(latents, "latents"));
+  DIT_CHECK(check_sigmas(sigma_host, B));
+  DIT_CHECK(check_ptr(cos_dev, "cos"));
+  DIT_CHECK(check_ptr(sin_dev, "sin"));
+  DIT_CHECK(check_ptr(v_out, "v_out"));
+  const StepLayout L = step_layout(*cfg, B, S);
+  DIT_CHECK(check_ws(ws, ws_bytes, L.total));
+
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const dit_config& c = *cfg;
+  const int64_t D = c.hidden;
+  float* x = reinterpret_cast<float*>(at(ws, L.x));
+  float* mod = reinterpret_cast<float*>(at(ws, L.mod));
+  void* bws = at(ws, L.block);
+  const int64_t mbs = DIT_MOD_ROWS * D;
+
+  // 1. global modulation, once for the whole step
+  DIT_CHECK(launch_modulation(c, *w, sigma_host, B, mod, at(ws, L.modws), st));
+
+  // 2. embeddings straight into the residual rows
+  {
+    dit::GemmBatch g{};
+    if (n_txt > 0) {
+      dit::GemmProblem p = problem(txt, c.txt_channels, w->ctx_embed, c.txt_channels,
+                                   (int)(B * n_txt), (int)D, c.txt_channels, dit::EPI_F32, x, D);
+      set_rows(p, (int)n_txt, S, 0);
+      g.p[g.count++] = p;
+    }
+    dit::GemmProblem p = problem(latents, c.in_channels, w->x_embed, c.in_channels,
+                                 (int)(B * (n_img + n_ref)), (int)D, c.in_channels, dit::EPI_F32,
+                                 x, D);
+    set_rows(p, (int)(n_img + n_ref), S, (int)n_txt);
+    g.p[g.count++] = p;
+    DIT_CHECK(run_gemm(g, st));
+  }
+
+  // 3. blocks, all reading the one modulation buffer
+  for (int i = 0; i < c.n_dual; ++i)
+    DIT_CHECK(launch_dual(c, w->dual[i], x, B, S, n_txt, mod + DIT_MOD_DUAL_TXT * D,
+                          mod + DIT_MOD_DUAL_IMG * D, mbs, cos_dev, sin_dev, bws, st));
+  for (int i = 0; i < c.n_single; ++i)
+    DIT_CHECK(launch_single(c, w->single[i], x, B, S, mod + DIT_MOD_SINGLE * D, mbs, cos_dev,
+                            sin_dev, bws, st));
+
+  // 4. final AdaLN of the image rows + projection to the latent width
+  {
+    const BlockLayout BL = block_layout(c, 1, B, S);
+    bf16_t* h = bf(at(bws, BL.h));
+    dit::NormArgs na{};
+    na.x = x;
+    na.h = h;
+    na.S = S;
+    na.mod_bstride = mbs;
+    na.D = (int)D;
+    na.B = B;
+    na.kind = c.prenorm;
+    na.eps = c.eps;
+    na.nseg = 1;
+    na.seg[0].shift = mod + DIT_MOD_FINAL * D;
+    na.seg[0].scale = mod + (DIT_MOD_FINAL + 1) * D;
+    na.seg[0].out_base = 0;
+    na.seg[0].seg_off = (int)n_txt;
+    na.seg[0].seg_len = (int)n_img;
+    DIT_CHECK(run_norm(na, st));
+    dit::GemmBatch g{};
+    g.count = 1;
+    g.p[0] = problem(h, D, w->proj_out, D, (int)(B * n_img), c.in_channels, (int)D,
+                     dit::EPI_F32, v_out, c.in_channels);
+    DIT_CHECK(run_gemm(g, st));
+  }
+  return DIT_OK;
+}
+
+int dit_profile_begin(void) {
+  std::lock_guard<std::mutex> lock(g_prof.mu);
+  g_prof.recs.clear();
+  g_prof.on = true;
+  return DIT_OK;
+}
+
+int dit_profile_end(dit_kernel_stats* out) {
+  if (!out) return fail(DIT_E_NULL, "out is NULL");
+  std::lock_guard<std::mutex> lock(g_prof.mu);
+  if (!g_prof.on) return fail(DIT_E_VALUE, "dit_profile_end without dit_profile_begin");
+  g_prof.on = false;
+  for (int k = 0; k < DIT_K_COUNT; ++k) out[k] = dit_kernel_stats{k, 0, 0.0, 0.0, 0.0};
+  int status = DIT_OK;
+  for (ProfRecord& r : g_prof.recs) {
+    float ms = 0.f;
+    hipError_t e = hipEventSynchronize(r.stop);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.start, r.stop);
+    if (e != hipSuccess && status == DIT_OK)
+      status = fail(DIT_E_HIP, "profile events: %s", hipGetErrorString(e));
+    dit_kernel_stats& k = out[r.kind];
+    k.launches += 1;
+    k.total_ms += ms;
+    k.flops += r.flops;
+    k.bytes += r.bytes;
+    g_prof.pool.push_back(r.start);
+    g_prof.pool.push_back(r.stop);
+  }
+  g_prof.recs.clear();
+  return status;
+}
+
+}  // extern "C"

@@ -1,0 +1,147 @@
+// Host-side launch interface of the gfx950 kernels (internal to libdit.so).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dit {
+
+typedef uint16_t bf16_t;
+
+// ------------------------------------------------------------------ GEMM
+// C = A W^T with A [M, K] bf16 (row stride lda) and W [N', K] bf16 (row
+// stride ldw), fp32 accumulation on MFMA, and one of four epilogues.
+// Output row r of a problem is written to row
+//   (r / seg_len) * seg_stride + seg_off + (r % seg_len)
+// of C, which lets one launch scatter stream-major rows back to the token
+// order of x[B, S, D] without copies.
+enum Epilogue : int32_t {
+  EPI_BF16 = 0,    // C bf16 [., ldc]:  C[row, n] = acc
+  EPI_SWIGLU = 1,  // C bf16: C[row, n] = SiLU(acc_gate) * acc_up; W rows
+                   //   [0, N) are gate rows and [N, 2N) are up rows
+  EPI_RESID = 2,   // C fp32: C[row, n] += gate[b * gate_bstride + n] * acc,
+                   //   b = r / seg_len
+  EPI_F32 = 3      // C fp32: C[row, n] = acc
+};
+
+struct GemmProblem {
+  const bf16_t* A;
+  const bf16_t* W;
+  void* C;
+  const float* gate;
+  int64_t lda, ldw, ldc, gate_bstride, seg_stride;
+  int32_t M, N, K, epi;
+  int32_t seg_len, seg_off;
+  int32_t tiles_m, tiles_n, tile_begin, pad_;
+};
+
+constexpr int kMaxGemmProblems = 4;
+
+struct GemmBatch {
+  GemmProblem p[kMaxGemmProblems];
+  int32_t count;
+  int32_t total_tiles;
+};
+
+// Requirements checked by the caller: K % 64 == 0, N % 32 == 0,
+// lda/ldw % 8 == 0, 16-byte aligned A and W; ldc % 4 == 0.
+constexpr int kGemmBM = 256, kGemmBN = 256, kGemmBK = 64;
+
+// Fills tiles_m/tiles_n/tile_begin/total_tiles and launches.
+hipError_t gemm_launch(GemmBatch& batch, hipStream_t stream);
+
+// ------------------------------------------------------------------ norms
+// h[out_base + r] = N(x[row(r)]) * (1 + scale[b]) + shift[b] (bf16), for up
+// to two row segments; row(r) = b * S + seg_off + r % seg_len, b = r / seg_len.
+struct NormSegment {
+  const float* shift;  // + b * mod_bstride
+  const float* scale;
+  int64_t out_base;    // first output row
+  int32_t seg_off, seg_len;
+};
+struct NormArgs {
+  const float* x;
+  bf16_t* h;
+  int64_t S, mod_bstride;
+  int32_t D, B, kind, nseg;
+  float eps;
+  NormSegment seg[2];
+};
+hipError_t modnorm_launch(const NormArgs& a, hipStream_t stream);
+
+// ------------------------------------------------------------------ QK-norm + RoPE
+// From the fused projection rows (q | k | v, each D wide, row stride ldu),
+// writes q, k: [B, H, S_pad, 128] and v^T: [B, H, 128, S_pad] (bf16); rows
+// s >= S of the padded outputs are zero. A token (b, s) is read from row
+//   stream_major ? (s < n_txt ? b*n_txt + s : B*n_txt + b*(S-n_txt) + s-n_txt)
+//                : b*S + s.
+// Text rows use gains [0], the rest gains [1].
+struct QkRopeArgs {
+  const bf16_t* u;
+  bf16_t* q;
+  bf16_t* k;
+  bf16_t* vt;
+  const float* cos_t;  // [S, 64]
+  const float* sin_t;
+  const float* q_gain[2];
+  const float* k_gain[2];
+  int64_t ldu, S, S_pad, n_txt;
+  int32_t B, H, D, stream_major;
+  float eps;
+};
+hipError_t qk_rope_launch(const QkRopeArgs& a, hipStream_t stream);
+
+// ------------------------------------------------------------------ attention
+// O = softmax(q k^T / sqrt(128)) v for every (b, h), no mask, over S keys.
+// q, k [B, H, S_pad, 128], vt [B, H, 128, S_pad] (zero beyond S). Output row
+// of token (b, s) as in QkRopeArgs' mapping; written at o + row * ldo + h*128.
+struct AttnArgs {
+  const bf16_t* q;
+  const bf16_t* k;
+  const bf16_t* vt;
+  bf16_t* o;
+  int64_t S, S_pad, ldo, n_txt;
+  int32_t B, H, stream_major;
+  float scale_log2;  // log2(e) / sqrt(head_dim)
+};
+hipError_t attention_launch(const AttnArgs& a, hipStream_t stream);
+
+// ------------------------------------------------------------------ small ops
+// RoPE tables from int32 positions [S, 4]: omega[a][j] given in double.
+struct RopeArgs {
+  const int32_t* pos;
+  float* cos_t;
+  float* sin_t;
+  int64_t S;
+  int32_t pairs;          // head_dim / 2
+  int32_t axis_of[64];    // pair -> axis
+  double omega[64];       // pair -> frequency
+};
+hipError_t rope_tables_launch(const RopeArgs& a, hipStream_t stream);
+
+// Sinusoidal timestep features e[B, C] (fp32) from per-row sigma.
+struct TimeArgs {
+  float* e;
+  int32_t B, C;
+  float sigma[64];
+};
+hipError_t time_features_launch(const TimeArgs& a, hipStream_t stream);
+
+// y[b, out_off_s + n] = act_out(sum_k W_s[n, k] act_in(x[b, k])), fp32 out,
+// for up to four weight segments sharing one input x [B, K] (fp32).
+enum Act : int32_t { ACT_NONE = 0, ACT_SILU = 1 };
+struct GemvSegment {
+  const bf16_t* W;   // [rows, K]
+  int64_t out_off;   // first output column in y
+  int32_t rows, row_begin;  // row_begin: first global row of this segment
+};
+struct GemvArgs {
+  const float* x;    // [B, K]
+  float* y;          // [B, ldy]
+  int64_t ldy;
+  int32_t B, K, act_in, act_out, nseg, total_rows;
+  GemvSegment seg[4];
+};
+hipError_t gemv_launch(const GemvArgs& a, hipStream_t stream);
+
+}  // namespace dit

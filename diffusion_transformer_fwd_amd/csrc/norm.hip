@@ -1,0 +1,308 @@
+// Bandwidth-bound kernels of the step on gfx950:
+//   * modnorm: AdaLN pre-norm of the fp32 residual into a bf16 GEMM operand
+//   * qk_rope: per-head QK-RMSNorm + RoPE + relayout for attention
+//   * rope_tables: cos/sin of every pair angle from integer positions
+//   * time_features + gemv: the global modulation vectors from sigma
+//
+// The maths each one follows is stated at its kernel; the pages it comes
+// from are "flux2-klein-p100a" (Caveats: modulation global per step) and
+// "tt_flux2_klein - Python reference" (Things that are easy to get wrong:
+// RoPE of 32 dims per axis, theta 2000, adjacent pairs).
+#include <math.h>
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace dit {
+namespace {
+
+// ------------------------------------------------------------------ modnorm
+// One wavefront per output row, the row held in registers (VPL float4 per
+// lane, D <= 256 * VPL): one read of x, one write of h, coalesced 16-byte /
+// 8-byte accesses. h = N(x) * (1 + scale[b]) + shift[b] in bf16, with
+// N = RMS: x / sqrt(mean(x^2) + eps), or LAYER: (x - mean) / sqrt(var + eps).
+template <int VPL>
+__global__ __launch_bounds__(256) void modnorm_kernel(const NormArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  // segment lookup: seg[1] (if any) starts after seg[0]'s output rows
+  const int si = (a.nseg > 1 && row >= a.seg[1].out_base) ? 1 : 0;
+  const NormSegment& sg = si ? a.seg[1] : a.seg[0];
+  const int64_t r = row - sg.out_base;
+  if (r < 0 || r >= (int64_t)a.B * sg.seg_len) return;
+  const int b = (int)(r / sg.seg_len);
+  const int64_t xrow = (int64_t)b * a.S + sg.seg_off + (r - (int64_t)b * sg.seg_len);
+  const int D = a.D, D4 = D >> 2;
+  const f32x4* xr = reinterpret_cast<const f32x4*>(a.x + xrow * D);
+  f32x4 v[VPL];
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    const int c = i * 64 + lane;
+    v[i] = c < D4 ? xr[c] : f32x4{0.f, 0.f, 0.f, 0.f};
+    s += v[i][0] + v[i][1] + v[i][2] + v[i][3];
+  }
+  float mean = 0.f;
+  if (a.kind == 1) mean = wave_sum(s) / D;
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    const int c = i * 64 + lane;
+    if (c < D4) {
+      const f32x4 d = v[i] - mean;
+      ss += d[0] * d[0] + d[1] * d[1] + d[2] * d[2] + d[3] * d[3];
+    }
+  }
+  const float rstd = rsqrtf(wave_sum(ss) / D + a.eps);
+  const f32x4* sh = reinterpret_cast<const f32x4*>(sg.shift + (int64_t)b * a.mod_bstride);
+  const f32x4* sc = reinterpret_cast<const f32x4*>(sg.scale + (int64_t)b * a.mod_bstride);
+  u32x2* out = reinterpret_cast<u32x2*>(a.h + row * D);
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    const int c = i * 64 + lane;
+    if (c < D4) {
+      const f32x4 y = (v[i] - mean) * rstd * (1.f + sc[c]) + sh[c];
+      out[c] = pack_bf16x4(y);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ qk_rope
+// Workgroup = (64 tokens, one head, one batch row), 256 threads.
+//  q, k: each token's 128-wide head vector is handled by 16 lanes (8
+//   elements = 4 adjacent pairs each): fp32 RMS over the group of 16 lanes,
+//   times the gain, then each pair (x0, x1) -> (x0 c - x1 s, x0 s + x1 c)
+//   with the token's (c, s) for that pair; written token-major per head.
+//  v: the 64 x 128 block is transposed through LDS and written
+//   feature-major (v^T), the layout the attention kernel's PV product reads.
+//  Tokens s >= S of the padded outputs are written as zeros.
+__global__ __launch_bounds__(256) void qk_rope_kernel(const QkRopeArgs a) {
+  __shared__ uint16_t vtile[64][128 + 8];
+  const int tid = threadIdx.x;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int64_t s0 = (int64_t)blockIdx.x * 64;
+  const int D = a.D;
+  const int64_t bh = (int64_t)b * a.H + h;
+
+  auto src_row = [&](int64_t s) -> int64_t {
+    if (!a.stream_major) return (int64_t)b * a.S + s;
+    if (s < a.n_txt) return (int64_t)b * a.n_txt + s;
+    return (int64_t)a.B * a.n_txt + (int64_t)b * (a.S - a.n_txt) + (s - a.n_txt);
+  };
+
+  // q and k: 64 tokens x 2 tensors = 128 vectors, 16 lanes each -> 8 passes
+  const int g = tid >> 4, gl = tid & 15;  // group (16 per pass), lane in group
+#pragma unroll 2
+  for (int pass = 0; pass < 8; ++pass) {
+    const int vec = pass * 16 + g;         // 0..127
+    const int which = vec >> 6;            // 0 = q, 1 = k
+    const int64_t s = s0 + (vec & 63);
+    bf16_t* dst = (which ? a.k : a.q) + (bh * a.S_pad + s) * 128 + gl * 8;
+    if (s >= a.S) {
+      *reinterpret_cast<u32x4*>(dst) = u32x4{0u, 0u, 0u, 0u};
+      continue;
+    }
+    const bf16_t* src = a.u + src_row(s) * a.ldu + which * D + h * 128 + gl * 8;
+    const u32x4 raw = *reinterpret_cast<const u32x4*>(src);
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[2 * e] = bf16_to_f32(raw[e] & 0xFFFFu);
+      x[2 * e + 1] = bf16_to_f32(raw[e] >> 16);
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
+    ss = group_sum<16>(ss);
+    const float rstd = rsqrtf(ss * (1.f / 128.f) + a.eps);
+    const int st = s < a.n_txt ? 0 : 1;
+    const float* gain = which ? a.k_gain[st] : a.q_gain[st];
+    const f32x4 g0 = *reinterpret_cast<const f32x4*>(gain + gl * 8);
+    const f32x4 g1 = *reinterpret_cast<const f32x4*>(gain + gl * 8 + 4);
+    const float gv[8] = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
+    const f32x4 c = *reinterpret_cast<const f32x4*>(a.cos_t + s * 64 + gl * 4);
+    const f32x4 sn = *reinterpret_cast<const f32x4*>(a.sin_t + s * 64 + gl * 4);
+    f32x8 y;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const float x0 = x[2 * p] * rstd * gv[2 * p];
+      const float x1 = x[2 * p + 1] * rstd * gv[2 * p + 1];
+      y[2 * p] = x0 * c[p] - x1 * sn[p];
+      y[2 * p + 1] = x0 * sn[p] + x1 * c[p];
+    }
+    *reinterpret_cast<bf16x8*>(dst) = pack_bf16x8(y);
+  }
+
+  // v: stage 64 tokens x 128 features, then write 128 features x 64 tokens
+  {
+    const int t = tid >> 2, part = tid & 3;  // token, 32-feature quarter
+    const int64_t s = s0 + t;
+    u32x4 vals[4];
+    if (s < a.S) {
+      const bf16_t* src = a.u + src_row(s) * a.ldu + 2 * D + h * 128 + part * 32;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vals[i] = reinterpret_cast<const u32x4*>(src)[i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vals[i] = u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        vtile[t][part * 32 + i * 8 + 2 * e] = (uint16_t)(vals[i][e] & 0xFFFFu);
+        vtile[t][part * 32 + i * 8 + 2 * e + 1] = (uint16_t)(vals[i][e] >> 16);
+      }
+  }
+  __syncthreads();
+  {
+    // thread -> feature f = tid / 2, 32 tokens (half = tid & 1)
+    const int f = tid >> 1, half = tid & 1;
+    bf16_t* dst = a.vt + (bh * 128 + f) * a.S_pad + s0 + half * 32;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      u32x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = half * 32 + i * 8 + 2 * e;
+        w[e] = (uint32_t)vtile[t][f] | ((uint32_t)vtile[t + 1][f] << 16);
+      }
+      reinterpret_cast<u32x4*>(dst)[i] = w;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ rope tables
+// cos/sin[s, j] of pos[s, axis(j)] * omega[j], angle and cos/sin in double.
+__global__ __launch_bounds__(256) void rope_tables_kernel(const RopeArgs a) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= a.S * a.pairs) return;
+  const int64_t s = i / a.pairs;
+  const int j = (int)(i - s * a.pairs);
+  const double phi = (double)a.pos[s * 4 + a.axis_of[j]] * a.omega[j];
+  double sv, cv;
+  sincos(phi, &sv, &cv);
+  a.cos_t[i] = (float)cv;
+  a.sin_t[i] = (float)sv;
+}
+
+// ------------------------------------------------------------------ time features
+// e[b] = [cos(tau f_k) | sin(tau f_k)], tau = 1000 sigma_b,
+// f_k = exp(-ln(1e4) k / half); evaluated in double.
+__global__ __launch_bounds__(256) void time_features_kernel(const TimeArgs a) {
+  const int b = blockIdx.x;
+  const int half = a.C / 2;
+  const double tau = 1000.0 * (double)a.sigma[b];
+  for (int k = threadIdx.x; k < half; k += 256) {
+    const double f = exp(-log(10000.0) * (double)k / (double)half);
+    double sv, cv;
+    sincos(tau * f, &sv, &cv);
+    a.e[(int64_t)b * a.C + k] = (float)cv;
+    a.e[(int64_t)b * a.C + half + k] = (float)sv;
+  }
+}
+
+// ------------------------------------------------------------------ gemv
+// y[b, out_off + n] = act_out(sum_k W[n, k] act_in(x[b, k])) for B <= 4
+// batch rows per launch. Workgroup = 4 waves, one weight row per wave per
+// iteration; the B input rows are staged in LDS (fp32, after act_in) and the
+// weight row is streamed once with 16-byte loads: the kernel reads each
+// weight byte exactly once.
+constexpr int kGemvMaxB = 4;
+constexpr int kGemvMaxK = 4096;
+__global__ __launch_bounds__(256) void gemv_kernel(const GemvArgs a) {
+  __shared__ float xs[kGemvMaxB][kGemvMaxK];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < a.B * a.K; i += 256) {
+    const int b = i / a.K, k = i - b * a.K;
+    float v = a.x[(int64_t)b * a.K + k];
+    xs[b][k] = a.act_in == ACT_SILU ? silu_f(v) : v;
+  }
+  __syncthreads();
+  const int K8 = a.K >> 3;
+  for (int row = blockIdx.x * 4 + wave; row < a.total_rows; row += gridDim.x * 4) {
+    int si = 0;
+#pragma unroll
+    for (int i = 1; i < 4; ++i)
+      if (i < a.nseg && row >= a.seg[i].row_begin) si = i;
+    const GemvSegment& sg = a.seg[si];
+    const int n = row - sg.row_begin;
+    const u32x4* w = reinterpret_cast<const u32x4*>(sg.W + (int64_t)n * a.K);
+    float acc[kGemvMaxB] = {0.f, 0.f, 0.f, 0.f};
+    for (int c = lane; c < K8; c += 64) {
+      const u32x4 raw = w[c];
+      float wv[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        wv[2 * e] = bf16_to_f32(raw[e] & 0xFFFFu);
+        wv[2 * e + 1] = bf16_to_f32(raw[e] >> 16);
+      }
+#pragma unroll
+      for (int b = 0; b < kGemvMaxB; ++b) {
+        if (b < a.B) {
+          const float* xb = &xs[b][c * 8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[b] += wv[e] * xb[e];
+        }
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < kGemvMaxB; ++b) {
+      if (b < a.B) {
+        float v = wave_sum(acc[b]);
+        if (lane == 0) {
+          if (a.act_out == ACT_SILU) v = silu_f(v);
+          a.y[(int64_t)b * a.ldy + sg.out_off + n] = v;
+        }
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t modnorm_launch(const NormArgs& a, hipStream_t stream) {
+  int64_t rows = 0;
+  for (int i = 0; i < a.nseg; ++i)
+    rows = max(rows, a.seg[i].out_base + (int64_t)a.B * a.seg[i].seg_len);
+  if (rows == 0) return hipSuccess;
+  const dim3 grid((unsigned)((rows + 3) / 4));
+  const int vpl = (a.D / 4 + 63) / 64;
+  if (vpl <= 1) hipLaunchKernelGGL(modnorm_kernel<1>, grid, dim3(256), 0, stream, a);
+  else if (vpl <= 2) hipLaunchKernelGGL(modnorm_kernel<2>, grid, dim3(256), 0, stream, a);
+  else if (vpl <= 4) hipLaunchKernelGGL(modnorm_kernel<4>, grid, dim3(256), 0, stream, a);
+  else if (vpl <= 8) hipLaunchKernelGGL(modnorm_kernel<8>, grid, dim3(256), 0, stream, a);
+  else if (vpl <= 12) hipLaunchKernelGGL(modnorm_kernel<12>, grid, dim3(256), 0, stream, a);
+  else if (vpl <= 16) hipLaunchKernelGGL(modnorm_kernel<16>, grid, dim3(256), 0, stream, a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t qk_rope_launch(const QkRopeArgs& a, hipStream_t stream) {
+  if (a.S_pad == 0 || a.B == 0) return hipSuccess;
+  const dim3 grid((unsigned)(a.S_pad / 64), (unsigned)a.H, (unsigned)a.B);
+  hipLaunchKernelGGL(qk_rope_kernel, grid, dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t rope_tables_launch(const RopeArgs& a, hipStream_t stream) {
+  const int64_t n = a.S * a.pairs;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(rope_tables_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+
+hipError_t time_features_launch(const TimeArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(time_features_kernel, dim3((unsigned)a.B), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t gemv_launch(const GemvArgs& a, hipStream_t stream) {
+  if (a.B > kGemvMaxB || a.K > kGemvMaxK || (a.K & 7)) return hipErrorInvalidValue;
+  const int blocks = min(2048, (a.total_rows + 3) / 4);
+  hipLaunchKernelGGL(gemv_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace dit

@@ -62,10 +62,14 @@ def bf16_round(a: np.ndarray) -> np.ndarray:
 
     Returns float32 holding bf16-representable values. Inputs are finite.
     """
-    a = np.ascontiguousarray(a, dtype=np.float32)
-    u = a.view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
-    return u.astype(np.uint32).view(np.float32)
+    a = np.array(a, dtype=np.float32, copy=True, order="C")
+    u = a.view(np.uint32)
+    # finite inputs: u + 0x8000 never wraps (max finite magnitude is 0x7F7FFFFF)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    u += np.uint32(0x7FFF)
+    u += lsb
+    u &= np.uint32(0xFFFF0000)
+    return a
 
 
 def bf16_bits(a: np.ndarray) -> np.ndarray:
