@@ -8,12 +8,12 @@
 //
 // Design (one workgroup = 4 waves = 256 threads, one 256 x 256 output tile):
 //  * A [M, K] and W [N, K] are both K-contiguous, so one 64-wide K slice of
-//    each tile is a set of 128-byte row segments: every thread fetches 16
-//    bytes per row segment (coalesced), and the slice is stored to LDS with
-//    its 16-byte chunks XOR-swizzled by row so that MFMA fragment reads are
-//    free of bank conflicts. Two LDS stages (128 KiB of the CU's 160 KiB):
-//    the next slice is fetched into registers while the current one feeds
-//    the MFMAs, then written to the other stage; one barrier per slice.
+//    each tile is a set of 128-byte row segments. Slices go from HBM/L2
+//    straight into LDS with buffer loads that write LDS (no register
+//    staging, no LDS store instructions), their 16-byte chunks XOR-swizzled
+//    by row so that MFMA fragment reads are free of bank conflicts. Two LDS
+//    stages (128 KiB of the CU's 160 KiB), one barrier per slice; fragments
+//    for the next 16-wide k-step are read while the current one's MFMAs run.
 //  * Each wave owns a 128 x 128 sub-tile as 4 x 4 blocks of
 //    v_mfma_f32_32x32x16_bf16 (fp32 accumulators, 256 per lane). The weight
 //    fragment is the MFMA's first operand and the activation fragment the
@@ -49,7 +49,7 @@ constexpr int CH_A = BM * ROW_U / NT;         // chunks per thread per slice
 constexpr int CH_W = BN * ROW_U / NT;
 constexpr int STAGE_U = (BM + BN) * ROW_U;    // 16-byte units per stage
 
-static_assert(CH_A == 8 && CH_W == 8, "loader assumes 8 chunks per thread");
+static_assert(CH_A == 8 && CH_W == 8 && NT == 256, "loader assumes 4 waves x 8 rows x 8 chunks");
 
 // Chunk swizzle by row: distinct for 8 consecutive rows and for the 8 rows of
 // either parity among 16 consecutive rows.
@@ -84,6 +84,8 @@ __device__ __forceinline__ void store4(const GemmProblem& P, int epi, int64_t ou
   }
 }
 
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
 __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const GemmBatch args) {
   __shared__ u32x4 lds[2 * STAGE_U];
 
@@ -105,38 +107,58 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const GemmBatch args) 
   tile_coords(L - P.tile_begin, P.tiles_m, P.tiles_n, tm, tn);
   const int m0 = tm * BM;
 
-  // ---- global -> LDS loader: thread owns chunk ckc of rows crow + 32 i.
-  // Buffer loads: rows past the end of A or W read as zero (tail tiles).
-  const int crow = tid >> 3, ckc = tid & 7;
+  // ---- global -> LDS: buffer loads that write LDS directly (no VGPR
+  // staging). Wave w, instruction i fills tile rows 64 w + 8 i + lane / 8;
+  // lane writes physical chunk lane % 8 of its row, so it fetches logical
+  // chunk (lane % 8) ^ swz(row). Rows past the end of A or W read as zero.
   const int w_rows = epi == EPI_SWIGLU ? 2 * N : N;
-  const uint32_t a_bytes = clamp_u32((int64_t)M * P.lda * 2);
-  const uint32_t w_bytes = clamp_u32((int64_t)w_rows * P.ldw * 2);
-  const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(P.A, a_bytes);
-  const __amdgpu_buffer_rsrc_t w_rsrc = make_rsrc(P.W, w_bytes);
-  const uint32_t a_voff = (uint32_t)(((int64_t)(m0 + crow) * P.lda + ckc * 8) * 2);
-  const uint32_t a_step = (uint32_t)(32 * P.lda * 2);
-  uint32_t w_voff, w_step[CH_W];
-  if (epi == EPI_SWIGLU) {
-    // tile column j = crow + 32 i: wave column half wn = i / 4; i % 4 < 2 are
-    // gate rows, the rest the matching up rows (N further down)
-    w_voff = (uint32_t)(((int64_t)(tn * (BN / 2) + crow) * P.ldw + ckc * 8) * 2);
+  const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(P.A, clamp_u32((int64_t)M * P.lda * 2));
+  const __amdgpu_buffer_rsrc_t w_rsrc = make_rsrc(P.W, clamp_u32((int64_t)w_rows * P.ldw * 2));
+  const int lr = lane >> 3, lp = lane & 7;
+  uint32_t a_off[2], w_off[2];
 #pragma unroll
-    for (int i = 0; i < CH_W; ++i)
-      w_step[i] = (uint32_t)(((i / 4) * (WTN / 2) + 32 * (i % 2) + ((i % 4) >= 2 ? N : 0)) *
-                             P.ldw * 2);
-  } else {
-    w_voff = (uint32_t)(((int64_t)(tn * BN + crow) * P.ldw + ckc * 8) * 2);
-#pragma unroll
-    for (int i = 0; i < CH_W; ++i) w_step[i] = (uint32_t)(i * 32 * P.ldw * 2);
+  for (int par = 0; par < 2; ++par) {
+    const int c = lp ^ (lr ^ par);
+    a_off[par] = (uint32_t)(((int64_t)(m0 + 64 * wave + lr) * P.lda + c * 8) * 2);
+    // SwiGLU: tile rows [64w, 64w + 64) are gate rows for even w and the
+    // matching up rows (N further down) for odd w, so each wave's 128 output
+    // columns hold gate and up values of the same 64 activation columns
+    int64_t wrow;
+    if (epi == EPI_SWIGLU) wrow = tn * (BN / 2) + (wave >> 1) * 64 + lr + ((wave & 1) ? N : 0);
+    else wrow = (int64_t)tn * BN + 64 * wave + lr;
+    w_off[par] = (uint32_t)((wrow * P.ldw + c * 8) * 2);
   }
-  const int st_off = crow * ROW_U + (ckc ^ swz(crow));
+  const uint32_t a_istep = (uint32_t)(8 * P.lda * 2), w_istep = (uint32_t)(8 * P.ldw * 2);
+  auto dma = [&](int kt, int stage) {
+    const uint32_t ko = (uint32_t)kt * (BK * 2);
+    u32x4* base = lds + stage * STAGE_U + wave * 64 * ROW_U;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_ptr_t)(base + i * 64), 16,
+                                               a_off[i & 1] + i * a_istep + ko, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rsrc, (lds_ptr_t)(base + BM * ROW_U + i * 64),
+                                               16, w_off[i & 1] + i * w_istep + ko, 0, 0, 0);
+  };
 
-  // ---- MFMA fragment readers
+  // ---- MFMA fragment readers (double-buffered across the 4 k-steps)
   const int fr = lane & 31, fg = lane >> 5;
   const int wm = wave & 1, wn = wave >> 1;
   const int a_rd = (wm * WTM + fr) * ROW_U;
   const int w_rd = BM * ROW_U + (wn * WTN + fr) * ROW_U;
   const int sfr = swz(fr);
+  bf16x8 af[2][FM], wf[2][FN];
+  auto fload = [&](int stage, int s, int buf) {
+    const u32x4* st = lds + stage * STAGE_U;
+    const int ch = (2 * s + fg) ^ sfr;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+      af[buf][i] = __builtin_bit_cast(bf16x8, st[a_rd + i * 32 * ROW_U + ch]);
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      wf[buf][j] = __builtin_bit_cast(bf16x8, st[w_rd + j * 32 * ROW_U + ch]);
+  };
 
   f32x16 acc[FM][FN];
 #pragma unroll
@@ -144,58 +166,39 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const GemmBatch args) 
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
 
-  u32x4 ra[CH_A], rw[CH_W];
+  // Two LDS stages; the slice kt + 2 is fetched while slice kt + 1 is being
+  // waited for and slice kt consumed. One barrier per slice.
   const int nk = K / BK;
-
-#pragma unroll
-  for (int i = 0; i < CH_A; ++i)
-    ra[i] = __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, a_voff + i * a_step, 0, 0);
-#pragma unroll
-  for (int i = 0; i < CH_W; ++i)
-    rw[i] = __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, w_voff + w_step[i], 0, 0);
-#pragma unroll
-  for (int i = 0; i < CH_A; ++i) lds[st_off + i * 32 * ROW_U] = ra[i];
-#pragma unroll
-  for (int i = 0; i < CH_W; ++i) lds[BM * ROW_U + st_off + i * 32 * ROW_U] = rw[i];
+  dma(0, 0);
+  if (nk > 1) {
+    dma(1, 1);
+    asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  } else {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
   __syncthreads();
 
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      const uint32_t ko = (uint32_t)(kt + 1) * (BK * 2);
-#pragma unroll
-      for (int i = 0; i < CH_A; ++i)
-        ra[i] = __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, a_voff + i * a_step + ko, 0, 0);
-#pragma unroll
-      for (int i = 0; i < CH_W; ++i)
-        rw[i] = __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, w_voff + w_step[i] + ko, 0, 0);
-    }
-    const u32x4* st = lds + cur * STAGE_U;
+    fload(cur, 0, 0);
 #pragma unroll
     for (int s = 0; s < BK / 16; ++s) {
-      const int ch = (2 * s + fg) ^ sfr;
-      bf16x8 af[FM], wf[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-        af[i] = __builtin_bit_cast(bf16x8, st[a_rd + i * 32 * ROW_U + ch]);
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-        wf[j] = __builtin_bit_cast(bf16x8, st[w_rd + j * 32 * ROW_U + ch]);
+      if (s + 1 < BK / 16) fload(cur, s + 1, (s + 1) & 1);
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[j], af[i], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[s & 1][j], af[s & 1][i],
+                                                              acc[i][j], 0, 0, 0);
+      if (s + 1 < BK / 16) {
+        // issue the next k-step's 8 fragment reads ahead of these 16 MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+      }
     }
-    if (more) {
-      u32x4* dst = lds + (cur ^ 1) * STAGE_U;
-#pragma unroll
-      for (int i = 0; i < CH_A; ++i) dst[st_off + i * 32 * ROW_U] = ra[i];
-#pragma unroll
-      for (int i = 0; i < CH_W; ++i) dst[BM * ROW_U + st_off + i * 32 * ROW_U] = rw[i];
-    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    if (kt + 2 < nk) dma(kt + 2, cur);
   }
 
   // ---- epilogue: lane holds row m0 + wm*128 + i*32 + fr, columns
