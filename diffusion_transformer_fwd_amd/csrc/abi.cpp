@@ -107,7 +107,7 @@ BlockLayout block_layout(const dit_config& c, int kind, int64_t B, int64_t S) {
   BlockLayout L;
   const int64_t D = c.hidden, F = c.mlp_hidden;
   L.R = B * S;
-  L.S_pad = round_up(S, 128);
+  L.S_pad = round_up(S, 256);  // attention reads whole 256-query blocks
   L.u_cols = kind == 0 ? std::max<int64_t>(3 * D, F) : 3 * D;
   size_t off = 0;
   auto take = [&](size_t bytes) {
