@@ -6,7 +6,7 @@
 // the final projection ("tt_flux2_klein - Python reference", Modules: the
 // DiT's 5 dual + 20 single blocks; the block maths is stated in dit.h).
 //
-// Design (one workgroup = 4 waves = 256 threads, one 256 x 256 output tile):
+// Design (one workgroup = 8 waves = 512 threads, one 256 x 256 output tile):
 //  * A [M, K] and W [N, K] are both K-contiguous, so one 64-wide K slice of
 //    each tile is a set of 128-byte row segments. Slices go from HBM/L2
 //    straight into LDS with buffer loads that write LDS (no register
@@ -14,8 +14,12 @@
 //    by row so that MFMA fragment reads are free of bank conflicts. Two LDS
 //    stages (128 KiB of the CU's 160 KiB), one barrier per slice; fragments
 //    for the next 16-wide k-step are read while the current one's MFMAs run.
-//  * Each wave owns a 128 x 128 sub-tile as 4 x 4 blocks of
-//    v_mfma_f32_32x32x16_bf16 (fp32 accumulators, 256 per lane). The weight
+//    Feeding a 256 x 256 tile is bound by how fast a CU can pull slices
+//    from L2, so the tile runs 8 waves (two per SIMD): more requests in
+//    flight per CU than 4 waves give, and one wave's waits overlap the
+//    other's MFMAs.
+//  * Each wave owns a 64 x 128 sub-tile (4 x 2 waves) as 2 x 4 blocks of
+//    v_mfma_f32_32x32x16_bf16 (fp32 accumulators, 128 per lane). The weight
 //    fragment is the MFMA's first operand and the activation fragment the
 //    second, so each lane ends up holding one output row and runs of four
 //    consecutive output columns: epilogue stores are 8-byte (bf16) or
@@ -41,15 +45,13 @@ namespace dit {
 namespace {
 
 constexpr int BM = kGemmBM, BN = kGemmBN, BK = kGemmBK;
-constexpr int NT = 256;
-constexpr int WTM = 128, WTN = 128;
+constexpr int NT = 512;                       // 8 waves, two per SIMD
+constexpr int WTM = 64, WTN = 128;            // wave tile: 4 x 2 waves
 constexpr int FM = WTM / 32, FN = WTN / 32;
 constexpr int ROW_U = BK / 8;                 // 16-byte units per LDS row
-constexpr int CH_A = BM * ROW_U / NT;         // chunks per thread per slice
-constexpr int CH_W = BN * ROW_U / NT;
 constexpr int STAGE_U = (BM + BN) * ROW_U;    // 16-byte units per stage
 
-static_assert(CH_A == 8 && CH_W == 8 && NT == 256, "loader assumes 4 waves x 8 rows x 8 chunks");
+static_assert(NT == 512 && BM == 256 && BN == 256, "loader assumes 8 waves x 32 rows");
 
 // Chunk swizzle by row: distinct for 8 consecutive rows and for the 8 rows of
 // either parity among 16 consecutive rows.
@@ -107,10 +109,11 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const GemmBatch args) 
   tile_coords(L - P.tile_begin, P.tiles_m, P.tiles_n, tm, tn);
   const int m0 = tm * BM;
 
-  // ---- global -> LDS: buffer loads that write LDS directly (no VGPR
-  // staging). Wave w, instruction i fills tile rows 64 w + 8 i + lane / 8;
-  // lane writes physical chunk lane % 8 of its row, so it fetches logical
-  // chunk (lane % 8) ^ swz(row). Rows past the end of A or W read as zero.
+  // ---- global -> LDS: buffer loads that write LDS directly (no register
+  // staging). Wave w fills tile rows 32 w .. 32 w + 31 of A and of W, four
+  // instructions of 8 rows each; a lane writes physical chunk lane % 8 of
+  // its row, so it fetches logical chunk (lane % 8) ^ swz(row). Rows past
+  // the end of A or W read as zero.
   const int w_rows = epi == EPI_SWIGLU ? 2 * N : N;
   const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(P.A, clamp_u32((int64_t)M * P.lda * 2));
   const __amdgpu_buffer_rsrc_t w_rsrc = make_rsrc(P.W, clamp_u32((int64_t)w_rows * P.ldw * 2));
@@ -119,32 +122,35 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const GemmBatch args) 
 #pragma unroll
   for (int par = 0; par < 2; ++par) {
     const int c = lp ^ (lr ^ par);
-    a_off[par] = (uint32_t)(((int64_t)(m0 + 64 * wave + lr) * P.lda + c * 8) * 2);
-    // SwiGLU: tile rows [64w, 64w + 64) are gate rows for even w and the
-    // matching up rows (N further down) for odd w, so each wave's 128 output
-    // columns hold gate and up values of the same 64 activation columns
+    a_off[par] = (uint32_t)(((int64_t)(m0 + 32 * wave + lr) * P.lda + c * 8) * 2);
+    // SwiGLU: tile row j = 32 w + r belongs to wave column group j / 128 =
+    // w / 4; rows with (w % 4) < 2 are gate rows, the others the matching up
+    // rows (N further down), so each wave's 128 output columns hold gate and
+    // up values of the same 64 activations
     int64_t wrow;
-    if (epi == EPI_SWIGLU) wrow = tn * (BN / 2) + (wave >> 1) * 64 + lr + ((wave & 1) ? N : 0);
-    else wrow = (int64_t)tn * BN + 64 * wave + lr;
+    if (epi == EPI_SWIGLU)
+      wrow = tn * (BN / 2) + (wave >> 2) * 64 + 32 * (wave & 1) + lr + (((wave & 3) >= 2) ? N : 0);
+    else
+      wrow = (int64_t)tn * BN + 32 * wave + lr;
     w_off[par] = (uint32_t)((wrow * P.ldw + c * 8) * 2);
   }
   const uint32_t a_istep = (uint32_t)(8 * P.lda * 2), w_istep = (uint32_t)(8 * P.ldw * 2);
   auto dma = [&](int kt, int stage) {
     const uint32_t ko = (uint32_t)kt * (BK * 2);
-    u32x4* base = lds + stage * STAGE_U + wave * 64 * ROW_U;
+    u32x4* base = lds + stage * STAGE_U + wave * 32 * ROW_U;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 4; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_ptr_t)(base + i * 64), 16,
                                                a_off[i & 1] + i * a_istep + ko, 0, 0, 0);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 4; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rsrc, (lds_ptr_t)(base + BM * ROW_U + i * 64),
                                                16, w_off[i & 1] + i * w_istep + ko, 0, 0, 0);
   };
 
-  // ---- MFMA fragment readers (double-buffered across the 4 k-steps)
+  // ---- MFMA fragments, double-buffered across k-steps
   const int fr = lane & 31, fg = lane >> 5;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave & 3, wn = wave >> 2;
   const int a_rd = (wm * WTM + fr) * ROW_U;
   const int w_rd = BM * ROW_U + (wn * WTN + fr) * ROW_U;
   const int sfr = swz(fr);
@@ -159,49 +165,55 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const GemmBatch args) 
     for (int j = 0; j < FN; ++j)
       wf[buf][j] = __builtin_bit_cast(bf16x8, st[w_rd + j * 32 * ROW_U + ch]);
   };
-
   f32x16 acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
+  auto mfmas = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[buf][j], af[buf][i], acc[i][j],
+                                                            0, 0, 0);
+  };
 
-  // Two LDS stages; the slice kt + 2 is fetched while slice kt + 1 is being
-  // waited for and slice kt consumed. One barrier per slice.
+  // Two LDS stages. Slice kt + 2 is fetched while kt + 1 is in flight and kt
+  // is consumed; one barrier per slice, placed before the slice's last
+  // k-step so that k-step's MFMAs (operands already in registers) cover the
+  // first fragment reads of the next slice. Scheduling barriers keep each
+  // k-step's fragment reads ahead of the previous k-step's MFMAs.
   const int nk = K / BK;
   dma(0, 0);
   if (nk > 1) {
     dma(1, 1);
-    asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
   } else {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
   __syncthreads();
-
+  fload(0, 0, 0);
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
-    fload(cur, 0, 0);
 #pragma unroll
-    for (int s = 0; s < BK / 16; ++s) {
-      if (s + 1 < BK / 16) fload(cur, s + 1, (s + 1) & 1);
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[s & 1][j], af[s & 1][i],
-                                                              acc[i][j], 0, 0, 0);
-      if (s + 1 < BK / 16) {
-        // issue the next k-step's 8 fragment reads ahead of these 16 MFMAs
-        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
-      }
+    for (int s = 0; s < BK / 16 - 1; ++s) {
+      fload(cur, s + 1, (s + 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas(s & 1);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // everyone is done with this stage and slice kt + 1 has landed
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
     __syncthreads();
     if (kt + 2 < nk) dma(kt + 2, cur);
+    if (kt + 1 < nk) fload(cur ^ 1, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas((BK / 16 - 1) & 1);
+    __builtin_amdgcn_sched_barrier(0);
   }
 
-  // ---- epilogue: lane holds row m0 + wm*128 + i*32 + fr, columns
+  // ---- epilogue: lane holds row m0 + wm*64 + i*32 + fr, columns
   //      (block j) j*32 + 8*q + 4*fg + 0..3 for q = 0..3
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
