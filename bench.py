@@ -15,6 +15,10 @@ times the oracle (float64 NumPy) on one single-stream block of the same
 workload and scales it by FLOP count to a full step.
 """
 import argparse
+import collections
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -29,6 +33,74 @@ METRIC = "ms per DiT denoise step at 1024² (4608 tok) + attn/GEMM TFLOP/s vs pe
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 P100A_STEP_MS = 331.0       # per DiT step, 1024^2, Tenstorrent p100a ("flux2-klein-p100a")
+COPY_CAL_BYTES = 512 << 20  # device-to-device copy used to calibrate the HBM byte counters
+GEMM_SRC = os.path.join(ROOT, "diffusion_transformer_fwd_amd", "csrc", "gemm.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_bf16_kernel_step_1024px_hbm_traffic.md")
+
+
+def gemm_source_hash():
+    with open(GEMM_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def stored_gemm_traffic():
+    """HBM bytes per GEMM launch from the committed counter summary, or None
+    when it is missing or was taken on a different GEMM kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            kv = dict(line.split(":", 1) for line in f if line.startswith(("bytes_per_launch:",
+                                                                         "gemm_source_sha256:")))
+    except OSError:
+        return None
+    if kv.get("gemm_source_sha256", "").strip() != gemm_source_hash():
+        return None
+    try:
+        return float(kv["bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def summarize(d):
+    """Markdown summary of the rocprofv3 CSV output in directory d: the
+    kernel-statistics table, and/or per-kernel counter means with FETCH_SIZE /
+    WRITE_SIZE converted to bytes by the calibration kernels (torch
+    elementwise kernels that each move COPY_CAL_BYTES, see --copy-calibration)."""
+    out = []
+    for f in sorted(glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)):
+        rows = list(csv.DictReader(open(f)))
+        out.append("| kernel | calls | avg us | total ms | % |\n|---|---|---|---|---|")
+        for r in rows:
+            name = r["Name"].replace("dit::(anonymous namespace)::", "").split("(")[0]
+            out.append(f"| {name} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                       f"{float(r['TotalDurationNs']) / 1e6:.2f} | {float(r['Percentage']):.2f} |")
+    for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+        per = collections.defaultdict(lambda: collections.defaultdict(float))
+        names = {}
+        for r in csv.DictReader(open(f)):
+            per[r["Dispatch_Id"]][r["Counter_Name"]] += float(r["Counter_Value"])
+            names[r["Dispatch_Id"]] = r["Kernel_Name"]
+        by_kernel = collections.defaultdict(list)
+        for disp, ctr in per.items():
+            by_kernel[names[disp].replace("dit::(anonymous namespace)::", "").split("(")[0]].append(ctr)
+        cal = {}
+        copies = [x for k, lst in by_kernel.items() if "elementwise_kernel" in k for x in lst]
+        for c in ("FETCH_SIZE", "WRITE_SIZE"):
+            vals = [x[c] for x in copies if c in x]
+            if vals:
+                cal[c] = COPY_CAL_BYTES / (max(vals) * 1024.0)  # bytes per counted KiB
+        out.append(f"counters from {os.path.basename(f)}; calibration kernels moving {COPY_CAL_BYTES} B: "
+                   + ", ".join(f"{c} x {1024 * v:.4f}" for c, v in cal.items()))
+        out.append("| kernel | dispatches | counter | mean per dispatch |\n|---|---|---|---|")
+        for k, lst in sorted(by_kernel.items()):
+            for c in sorted({c for x in lst for c in x}):
+                vals = [x[c] for x in lst if c in x]
+                out.append(f"| {k} | {len(vals)} | {c} | {sum(vals) / len(vals):.6g} |")
+        gemm = by_kernel.get("gemm_bf16_kernel", [])
+        for c in ("FETCH_SIZE", "WRITE_SIZE"):
+            vals = [x[c] for x in gemm if c in x]
+            if vals and c in cal:
+                out.append(f"gemm_{c.lower()}_bytes_per_launch: {sum(vals) / len(vals) * 1024 * cal[c]:.0f}")
+    print("\n".join(out))
 
 
 def log(msg):
@@ -66,7 +138,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--profile-steps", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="end with three device copies of COPY_CAL_BYTES (counter calibration)")
+    ap.add_argument("--summarize", metavar="DIR",
+                    help="print a markdown summary of rocprofv3 CSV output in DIR and exit")
     args = ap.parse_args()
+    if args.summarize:
+        summarize(args.summarize)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(--gpus must be 1).", file=sys.stderr)
@@ -159,6 +238,18 @@ def main():
                          f"({blk_flops / 1e12:.3f} of {step_flops / 1e12:.2f} TFLOP)"}
         log(f"CPU baseline {cpu_ms:.0f} ms/step ({dt:.1f} s per block, {threads} threads)")
 
+    if args.copy_calibration:
+        # a fill (writes COPY_CAL_BYTES) and elementwise negations (read and
+        # write COPY_CAL_BYTES each), so both counters see a known byte count
+        src = torch.empty(COPY_CAL_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+
+    traffic = stored_gemm_traffic()
     rec = {
         "metric": METRIC, "value": round(ms, 4), "unit": "ms", "n_gpus": 1, "steps": K,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": False,
@@ -178,7 +269,8 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "gemm_bf16_kernel",
                      "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None,
+                     "traffic": None if traffic is None else round(traffic),
+                     "alg_bytes_per_launch": round(g["bytes"] / g["launches"]),
                      "per_launch_flop": gemm_per_launch, "avg_launch_us": gemm_avg_s * 1e6},
         "kernels": kern,
         "cpu_baseline": cpu,

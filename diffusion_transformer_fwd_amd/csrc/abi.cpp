@@ -503,6 +503,7 @@ int launch_dual(const dit_config& c, const dit_dual_weights& w, float* x, int32_
   qa.D = (int)D;
   qa.stream_major = 1;
   qa.eps = c.eps;
+  qa.q_scale = (float)(1.4426950408889634 / std::sqrt((double)c.head_dim));
   DIT_CHECK(run_qk_rope(qa, st));
   dit::AttnArgs aa{};
   aa.q = qa.q;
@@ -516,7 +517,6 @@ int launch_dual(const dit_config& c, const dit_dual_weights& w, float* x, int32_
   aa.B = B;
   aa.H = c.heads;
   aa.stream_major = 1;
-  aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)c.head_dim));
   DIT_CHECK(run_attention(aa, st));
   DIT_CHECK(resid(o, D, w.out, (int)D, 2));
 
@@ -588,6 +588,7 @@ int launch_single(const dit_config& c, const dit_single_weights& w, float* x, in
   qa.D = (int)D;
   qa.stream_major = 0;
   qa.eps = c.eps;
+  qa.q_scale = (float)(1.4426950408889634 / std::sqrt((double)c.head_dim));
   DIT_CHECK(run_qk_rope(qa, st));
   dit::AttnArgs aa{};
   aa.q = qa.q;
@@ -601,7 +602,6 @@ int launch_single(const dit_config& c, const dit_single_weights& w, float* x, in
   aa.B = B;
   aa.H = c.heads;
   aa.stream_major = 0;
-  aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)c.head_dim));
   DIT_CHECK(run_attention(aa, st));
   {
     dit::GemmBatch g{};

@@ -5,27 +5,42 @@
 // wrong: all 512 text rows take part with no mask.
 //
 // Flash-style, one pass over K/V with an online softmax:
-//  * Workgroup = 8 waves = 256 queries (32 per wave, two waves per SIMD so
-//    one wave's softmax overlaps the other's MFMAs); the wave's Q block
-//    lives in registers for the whole pass.
+//  * Q arrives pre-scaled by log2(e) / sqrt(head_dim) (the QK-norm/RoPE
+//    kernel applies it before rounding to bf16), so a score in log2 units is
+//    a plain dot product and the probability is exp2(score - m).
+//  * Workgroup = 8 waves = 256 queries (32 per wave); a wave's Q block lives
+//    in registers for the whole pass.
 //  * K/V advance in tiles of 64 keys that buffer loads write straight into
 //    LDS (K as [key][128], V as V^T [128][key], both 16-byte-chunk swizzled),
-//    three stages deep so two tiles are in flight while one is consumed.
+//    four stages deep.
+//  * Ping-pong: waves 0-3 and waves 4-7 (one of each on every SIMD) run the
+//    same loop half an iteration apart. An iteration is a matrix phase
+//    (scores of tile t and the P V product of tile t - 1: 34 MFMAs) and a
+//    softmax phase (exp2 and bf16 packing of tile t: vector ALU only), each
+//    closed by a workgroup barrier, so one wave's MFMAs run under its
+//    partner's softmax.
+//  * Waves 0-3 alone issue the K/V tile loads (tile t + 2, spread through
+//    their matrix phase for tile t) and wait for tile t + 1 at the end of
+//    their softmax phase; the stage a load overwrites was last read by the
+//    lagging waves before the barrier that precedes the load.
 //  * Workgroups walk (batch, head, query block) XCD-contiguously, so a
 //    head's K and V^T are shared through one XCD's L2.
 //  * Scores are computed transposed, S^T = K Q^T, with
 //    v_mfma_f32_32x32x16_bf16: each lane then holds 32 scores of ONE query,
-//    so the running max / sum are lane-local (one cross-lane exchange per
-//    tile for the max, one at the end for the sum).
+//    so the softmax bookkeeping is lane-local.
 //  * The K rows feeding the score MFMA are permuted so that the score
 //    registers of a lane are, 8 at a time, exactly the operand layout of the
 //    next product, O^T = V^T P^T: probabilities go from accumulator to MFMA
 //    operand by a bf16 conversion, with no shuffles or LDS round trip.
-//  * exp2 with log2(e)/sqrt(d) folded into one scale; the running max is
-//    only raised (and O, l rescaled) when a tile's max exceeds it by more
-//    than 8 (a factor 256), which keeps every probability <= 256 in fp32
-//    and bf16 and skips most rescales. The result is the same softmax; only
-//    the rounding differs.
+//  * The running max m (per query, kept exactly representable in bf16) is
+//    subtracted by the score MFMA itself: a ninth k-step multiplies a key
+//    column of ones by a query row of -m, so the accumulator ends as
+//    score - m and each probability costs one exp2. m is set from the first
+//    tile and raised only when the row sum passes 2^64 (a guard far below
+//    fp32 / bf16 overflow): softmax is invariant to the offset, so no
+//    per-tile max is needed. The row sum l adds the fp32 probabilities with
+//    plain adds: the bf16 dot2 instruction would share the matrix pipeline
+//    with the partner wave's MFMAs and stall behind them.
 //  * Keys past S in the last tile are masked to -inf (the padded V rows are
 //    zero); queries past S are computed but not stored.
 #include <type_traits>
@@ -39,12 +54,13 @@ namespace {
 constexpr int NT = 512;    // 8 waves
 constexpr int QB = 256;    // queries per workgroup (32 per wave)
 constexpr int KT = 64;     // keys per tile
-constexpr int NSTAGE = 3;  // LDS stages (tiles in flight)
+constexpr int NSTAGE = 4;  // LDS stages
 constexpr int KU = 16;     // 16-byte units per K row (128 bf16)
 constexpr int VU = 8;      // 16-byte units per V^T row (64 keys)
-constexpr int K_UNITS = KT * KU;   // 1024
-constexpr int V_UNITS = 128 * VU;  // 1024
-constexpr int STAGE_U = K_UNITS + V_UNITS;
+constexpr int K_BYTES = KT * KU * 16;    // 16 KiB per K stage
+constexpr int V_BYTES = 128 * VU * 16;   // 16 KiB per V^T stage
+constexpr int V_BASE = NSTAGE * K_BYTES; // V^T stages follow the K stages
+constexpr float kSumGuard = 18446744073709551616.f;  // 2^64
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -63,10 +79,37 @@ __device__ __forceinline__ int key_of_row(int r) {
   return 16 * (j >> 1) + 8 * gp + 4 * (j & 1) + t;
 }
 
+// max / sum of x over lanes l and l ^ 32
+__device__ __forceinline__ float half_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <int STG>
+using stage_t = std::integral_constant<int, STG>;
+
+// Workgroup barrier without __syncthreads()' release fence, which would also
+// wait for the tile loads still in flight. LDS reads before it have all been
+// consumed by MFMAs (so they completed), and a tile's loads are waited for by
+// the wave that issued them before the barrier that publishes the tile.
+__device__ __forceinline__ void wg_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 __global__ __launch_bounds__(NT, 1) void attention_kernel(const AttnArgs a) {
-  __shared__ u32x4 lds[NSTAGE * STAGE_U];
+  __shared__ u32x4 lds[(V_BASE + NSTAGE * V_BYTES) / 16];
+  char* const lb = reinterpret_cast<char*>(lds);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bool loader = wave < 4;  // waves 0-3 lead and load; 4-7 lag half an iteration
   // XCD-contiguous work order: consecutive query blocks of one (b, h) run on
   // the same XCD, so that head's K and V^T stay in that XCD's L2.
   const int n_qb = (int)((a.S + QB - 1) / QB);
@@ -87,132 +130,206 @@ __global__ __launch_bounds__(NT, 1) void attention_kernel(const AttnArgs a) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // K / V^T tiles go straight from memory into LDS (buffer loads that write
-  // LDS at M0 + 16 * lane). Wave w fills K rows 8 w .. 8 w + 7 (two
-  // instructions of 4 rows x 16 chunks) and V^T rows 16 w .. 16 w + 15 (two
-  // of 8 rows x 8 chunks); each lane fetches the logical chunk whose
+  // LDS at M0 + 16 * lane). Loader wave w fills K rows 16 w .. 16 w + 15
+  // (four instructions of 4 rows x 16 chunks) and V^T rows 32 w .. 32 w + 31
+  // (four of 8 rows x 8 chunks); each lane fetches the logical chunk whose
   // swizzled position is its own.
   const __amdgpu_buffer_rsrc_t k_rsrc =
       make_rsrc(a.k + bh * a.S_pad * 128, clamp_u32(a.S_pad * 128 * 2));
   const __amdgpu_buffer_rsrc_t v_rsrc =
       make_rsrc(a.vt + bh * 128 * a.S_pad, clamp_u32(a.S_pad * 128 * 2));
-  uint32_t k_off[2], v_off[2];
+  const int lw = wave & 3;
+  uint32_t k_off[4], v_off[4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int krow = 8 * wave + 4 * i + (lane >> 4);
+  for (int i = 0; i < 4; ++i) {
+    const int krow = 16 * lw + 4 * i + (lane >> 4);
     k_off[i] = (uint32_t)((krow * 128 + (((lane & 15) ^ kswz(krow)) * 8)) * 2);
-    const int vrow = 16 * wave + 8 * i + (lane >> 3);
+    const int vrow = 32 * lw + 8 * i + (lane >> 3);
     v_off[i] = (uint32_t)((vrow * a.S_pad + (((lane & 7) ^ vswz(vrow)) * 8)) * 2);
   }
-  auto dma = [&](int t, int stage) {
-    u32x4* st = lds + stage * STAGE_U;
-    const uint32_t kk = (uint32_t)t * KT * 128 * 2, vk = (uint32_t)t * KT * 2;
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(k_rsrc, (lds_ptr_t)(st + (8 * wave + 4 * i) * KU),
-                                               16, k_off[i] + kk, 0, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
+  // instruction j (0..7) of this wave's share of tile t: K rows for j < 4,
+  // V^T rows for j >= 4
+  auto dma_part = [&](int t, auto stage, int j) {
+    constexpr int STG = decltype(stage)::value;
+    if (j < 4)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          v_rsrc, (lds_ptr_t)(st + K_UNITS + (16 * wave + 8 * i) * VU), 16, v_off[i] + vk, 0, 0, 0);
+          k_rsrc, (lds_ptr_t)(lb + STG * K_BYTES + (16 * lw + 4 * j) * KU * 16), 16,
+          k_off[j] + (uint32_t)t * KT * 128 * 2, 0, 0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          v_rsrc, (lds_ptr_t)(lb + V_BASE + STG * V_BYTES + (32 * lw + 8 * (j - 4)) * VU * 16),
+          16, v_off[j - 4] + (uint32_t)t * KT * 2, 0, 0, 0);
   };
 
-  // fragment read offsets
-  int k_rd[2];
+  // fragment read addresses (bytes, stage 0): K row key_of_row(qi) (+32 rows
+  // for the second key block), chunk 2 ks + g; V^T row qi (+32 per dim block),
+  // chunk 2 s + g; both through their swizzles.
+  uint32_t k_rd[8], v_rd[4];
+  {
+    const int krow = key_of_row(qi), ksw = kswz(krow), vsw = vswz(qi);
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) k_rd[kb] = (kb * 32 + key_of_row(qi)) * KU;
-  const int kswz0 = kswz(key_of_row(qi));  // same for kb = 0, 1 (low 4 bits)
-  const int v_rd = K_UNITS + qi * VU;      // + db * 32 rows
-  const int vsw = vswz(qi);
+    for (int ks = 0; ks < 8; ++ks) k_rd[ks] = (uint32_t)((krow * KU + ((2 * ks + g) ^ ksw)) * 16);
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      v_rd[s] = (uint32_t)(V_BASE + (qi * VU + ((2 * s + g) ^ vsw)) * 16);
+  }
+
+  // ninth k-step of the score product: every key row carries a 1 and the
+  // query column carries -m at k = 0 (lanes g = 0), zeros elsewhere
+  bf16x8 kaug = {}, qaug = {};
+  kaug[0] = (__bf16)(g == 0 ? 1.0f : 0.0f);
+  float m = 0.f;  // running max (log2 units), exact in bf16; set by the first tile
 
   f32x16 o[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) o[i] = f32x16{};
-  float m = -INFINITY, l = 0.f;
-
+  f32x16 sacc[2];
+  bf16x8 pf[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) pf[i] = bf16x8{};
+  float l = 0.f;
+  // V^T stage NSTAGE - 1 is read (times P = 0) before any tile lands there
+  {
+    u32x4* vz = reinterpret_cast<u32x4*>(lb + V_BASE + (NSTAGE - 1) * V_BYTES);
+    for (int i = tid; i < V_BYTES / 16; i += NT) vz[i] = u32x4{};
+  }
   const int n_tiles = (int)((a.S + KT - 1) / KT);
-  dma(0, 0);
-  if (n_tiles > 1) dma(1, 1);
 
-  // One 64-key tile: scores, online softmax, PV. MASKED (only the last tile
-  // of a ragged sequence) sets scores of keys >= S to -inf.
-  auto tile = [&](int t, auto masked_tag) {
-    constexpr bool MASKED = decltype(masked_tag)::value;
-    // tile t landed (this wave's loads), then everyone's: the barrier also
-    // retires all reads of tile t - 1, whose stage receives tile t + 2
-    if (t + 1 < n_tiles) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (t + 2 < n_tiles) dma(t + 2, (t + 2) % NSTAGE);
-    const u32x4* st = lds + (t % NSTAGE) * STAGE_U;
-
-    // S^T block: 64 keys x 32 queries as two 32x32 accumulators
-    f32x16 sacc[2] = {f32x16{}, f32x16{}};
+  // Matrix phase of iteration t: S^T - m of tile t (2 + 16 MFMAs into sacc)
+  // and O^T += V^T P^T of tile t - 1 (16 MFMAs into o), alternating, with
+  // the fragments read from LDS PF operations ahead; a loader wave issues
+  // its eight loads of tile t + 2 along the way. Every iteration runs both
+  // products (one code path keeps the register allocation tight): at t = 0
+  // the PV product reads a zeroed V^T stage with P = 0, and the scores
+  // computed at t = n_tiles are never used.
+  auto matrix_phase = [&](int t, auto stage) {
+    constexpr int STG = decltype(stage)::value;
+    constexpr int PSTG = (STG + NSTAGE - 1) % NSTAGE;
+    constexpr int N = 32, PF = 4;
+    const bool load = loader && t + 2 < n_tiles;
+    // op i: even -> score block (ks, kb) = (i / 4, (i / 2) % 2);
+    //        odd  -> PV block (s, db) = (i / 8, (i / 2) % 4)
+    auto frag = [&](int i) -> u32x4 {
+      const int j = i >> 1;
+      const uint32_t addr = (i & 1) == 0
+          ? k_rd[j >> 1] + STG * K_BYTES + (j & 1) * 32 * KU * 16
+          : v_rd[j >> 2] + PSTG * V_BYTES + (j & 3) * 32 * VU * 16;
+      return *reinterpret_cast<const u32x4*>(lb + addr);
+    };
+    u32x4 buf[PF];
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const int ch = (2 * ks + g) ^ kswz0;
+    for (int i = 0; i < PF; ++i) buf[i] = frag(i);
+    sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kaug, qaug, f32x16{}, 0, 0, 0);
+    sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kaug, qaug, f32x16{}, 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 kf = __builtin_bit_cast(bf16x8, st[k_rd[kb] + ch]);
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc[kb], 0, 0, 0);
-      }
+    for (int i = 0; i < N; ++i) {
+      const bf16x8 x = __builtin_bit_cast(bf16x8, buf[i % PF]);
+      if (i + PF < N) buf[i % PF] = frag(i + PF);
+      const int j = i >> 1;
+      if ((i & 1) == 0)
+        sacc[j & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, qf[j >> 1], sacc[j & 1], 0, 0, 0);
+      else
+        o[j & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, pf[j >> 2], o[j & 3], 0, 0, 0);
+      if ((i & 3) == 1 && load) dma_part(t + 2, stage_t<(STG + 2) % NSTAGE>{}, i >> 2);
+      __builtin_amdgcn_sched_barrier(0);  // keep the read-ahead distance
     }
+  };
 
-    if (MASKED) {
-      const int valid = (int)(a.S - (int64_t)t * KT);  // keys [0, valid) exist
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kb * 32 + 16 * (i >> 3) + 8 * g + (i & 7);
-          if (key >= valid) sacc[kb][i] = -INFINITY;
-        }
-    }
-    // raw-score max of this lane's query over the tile (the scale is > 0)
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, sacc[kb][i]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * a.scale_log2;
-    if (__ballot(tmax > m + 8.f) != 0) {
-      const float mn = fmaxf(m, tmax);
-      const float alpha = __builtin_amdgcn_exp2f(m - mn);
-      l *= alpha;
-#pragma unroll
-      for (int db = 0; db < 4; ++db) o[db] *= alpha;
-      m = mn;
-    }
-
-    // probabilities exp2(s * scale - m) -> bf16 operands of O^T += V^T P^T
-    bf16x8 pf[4];
+  // probabilities exp2(sacc - shift) of this lane's 32 scores as bf16 MFMA
+  // operands, their sum added to l
+  auto probabilities = [&](float shift) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       f32x8 p;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float pv =
-            __builtin_amdgcn_exp2f(fmaf(sacc[s >> 1][8 * (s & 1) + e], a.scale_log2, -m));
-        p[e] = pv;
-        l += pv;
-      }
+      for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(sacc[s >> 1][8 * (s & 1) + e] - shift);
       pf[s] = pack_bf16x8(p);
-    }
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int ch = (2 * s + g) ^ vsw;
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const bf16x8 vf = __builtin_bit_cast(bf16x8, st[v_rd + db * 32 * VU + ch]);
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[s], o[db], 0, 0, 0);
-      }
+      for (int e = 0; e < 8; ++e) l += p[e];
     }
   };
-  for (int t = 0; t + 1 < n_tiles; ++t) tile(t, std::false_type{});
-  if (a.S % KT) tile(n_tiles - 1, std::true_type{});
-  else tile(n_tiles - 1, std::false_type{});
+
+  // softmax phase of iteration t (t < n_tiles)
+  auto softmax_phase = [&](int t) {
+    if (t + 1 == n_tiles && (a.S % KT)) {
+      // keys [0, valid) exist; entry i of block kb is key kb*32 + 16(i/8) + 8g + i%8
+      const int lim = (int)(a.S - (int64_t)t * KT) - 8 * g;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (kb * 32 + 16 * (i >> 3) + (i & 7) >= lim) sacc[kb][i] = -INFINITY;
+    }
+    const float l_prev = l;
+    probabilities(0.f);
+    if (t == 0 || __ballot(!(l <= kSumGuard)) != 0) {
+      // (re)set the offset: m_new = max(m, bf16(m + tile max)); the first
+      // tile sets it outright. O and l scale by 2^(m - m_new).
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, sacc[kb][i]);
+      tmax = half_max(tmax);
+      float m_new = (float)(__bf16)(m + tmax);
+      if (t > 0) m_new = fmaxf(m_new, m);
+      const float shift = m_new - m;
+      const float alpha = t == 0 ? 0.f : __builtin_amdgcn_exp2f(-shift);
+      l = l_prev * alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o[db] *= alpha;
+      probabilities(shift);
+      m = m_new;
+      qaug[0] = (__bf16)(g == 0 ? -m : 0.f);
+    }
+    // materialise the results here, ahead of the loader's wait that follows
+#pragma unroll
+    for (int s = 0; s < 4; ++s) asm volatile("" : "+v"(pf[s]));
+    asm volatile("" : "+v"(l));
+  };
+
+  // one iteration: matrix phase, barrier, softmax phase, barrier. Returns
+  // true after the drain iteration t == n_tiles.
+  auto iteration = [&](int t, auto stage) -> bool {
+    matrix_phase(t, stage);
+    wg_barrier();
+    if (t < n_tiles) {
+      softmax_phase(t);
+      // the leading waves' loads of tile t + 1 have landed
+      if (loader) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (t + 2 < n_tiles) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
+    }
+    wg_barrier();
+    return t == n_tiles;
+  };
+
+  if (loader) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) dma_part(0, stage_t<0>{}, j);
+    if (n_tiles > 1) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) dma_part(1, stage_t<1>{}, j);
+      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+  }
+  __syncthreads();  // tiles 0 (and 1) requested, tile 0 landed, zero stage written
+  if (!loader) wg_barrier();  // lag by one phase
+  for (int t = 0;; t += NSTAGE) {
+    if (iteration(t, stage_t<0>{})) break;
+    if (iteration(t + 1, stage_t<1>{})) break;
+    if (iteration(t + 2, stage_t<2>{})) break;
+    if (iteration(t + 3, stage_t<3>{})) break;
+  }
+  if (loader) wg_barrier();  // match the lagging waves' barrier count
 
   // normalise and store: lane holds query q0 + qi, dims db*32 + 8 j + 4 g + 0..3
-  l += __shfl_xor(l, 32, 64);
+  l = half_sum(l);
   const int64_t q = q0 + qi;
   if (q >= a.S) return;
   const float inv = 1.f / l;

@@ -88,6 +88,7 @@ struct QkRopeArgs {
   int64_t ldu, S, S_pad, n_txt;
   int32_t B, H, D, stream_major;
   float eps;
+  float q_scale;  // applied to q before rounding: log2(e) / sqrt(head_dim)
 };
 hipError_t qk_rope_launch(const QkRopeArgs& a, hipStream_t stream);
 
@@ -102,7 +103,6 @@ struct AttnArgs {
   bf16_t* o;
   int64_t S, S_pad, ldo, n_txt;
   int32_t B, H, stream_major;
-  float scale_log2;  // log2(e) / sqrt(head_dim)
 };
 hipError_t attention_launch(const AttnArgs& a, hipStream_t stream);
 

@@ -73,6 +73,8 @@ __global__ __launch_bounds__(256) void modnorm_kernel(const NormArgs a) {
 //   elements = 4 adjacent pairs each): fp32 RMS over the group of 16 lanes,
 //   times the gain, then each pair (x0, x1) -> (x0 c - x1 s, x0 s + x1 c)
 //   with the token's (c, s) for that pair; written token-major per head.
+//   q is also multiplied by q_scale = log2(e) / sqrt(head_dim), the softmax
+//   scale in base 2 that the attention kernel expects to find applied.
 //  v: the 64 x 128 block is transposed through LDS and written
 //   feature-major (v^T), the layout the attention kernel's PV product reads.
 //  Tokens s >= S of the padded outputs are written as zeros.
@@ -122,11 +124,14 @@ __global__ __launch_bounds__(256) void qk_rope_kernel(const QkRopeArgs a) {
     const float gv[8] = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
     const f32x4 c = *reinterpret_cast<const f32x4*>(a.cos_t + s * 64 + gl * 4);
     const f32x4 sn = *reinterpret_cast<const f32x4*>(a.sin_t + s * 64 + gl * 4);
+    // q also takes the attention scale log2(e) / sqrt(head_dim) here, so
+    // that its single rounding to bf16 happens on the scaled value
+    const float sc = which ? rstd : rstd * a.q_scale;
     f32x8 y;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-      const float x0 = x[2 * p] * rstd * gv[2 * p];
-      const float x1 = x[2 * p + 1] * rstd * gv[2 * p + 1];
+      const float x0 = x[2 * p] * sc * gv[2 * p];
+      const float x1 = x[2 * p + 1] * sc * gv[2 * p + 1];
       y[2 * p] = x0 * c[p] - x1 * sn[p];
       y[2 * p + 1] = x0 * sn[p] + x1 * c[p];
     }
