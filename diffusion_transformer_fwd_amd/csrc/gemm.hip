@@ -14,10 +14,11 @@
 //    by row so that MFMA fragment reads are free of bank conflicts. Two LDS
 //    stages (128 KiB of the CU's 160 KiB), one barrier per slice; fragments
 //    for the next 16-wide k-step are read while the current one's MFMAs run.
-//    Feeding a 256 x 256 tile is bound by how fast a CU can pull slices
-//    from L2, so the tile runs 8 waves (two per SIMD): more requests in
-//    flight per CU than 4 waves give, and one wave's waits overlap the
-//    other's MFMAs.
+//    A CU pulls about 36 bytes per clock from L2 into LDS this way, close to
+//    the 32 B/clk a 256 x 256 tile consumes at the full MFMA rate, so the
+//    loads must overlap the math: the tile runs 8 waves (two per SIMD) and
+//    only the upper four issue loads, while the lower four keep issuing
+//    MFMAs.
 //  * Each wave owns a 64 x 128 sub-tile (4 x 2 waves) as 2 x 4 blocks of
 //    v_mfma_f32_32x32x16_bf16 (fp32 accumulators, 128 per lane). The weight
 //    fragment is the MFMA's first operand and the activation fragment the
@@ -110,42 +111,54 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const GemmBatch args) 
   const int m0 = tm * BM;
 
   // ---- global -> LDS: buffer loads that write LDS directly (no register
-  // staging). Wave w fills tile rows 32 w .. 32 w + 31 of A and of W, four
-  // instructions of 8 rows each; a lane writes physical chunk lane % 8 of
-  // its row, so it fetches logical chunk (lane % 8) ^ swz(row). Rows past
-  // the end of A or W read as zero.
+  // staging). Waves 4-7 issue every load of a slice: wave w fills tile rows
+  // 32 w' .. 32 w' + 31 of A and of W for w' = w and w' = w - 4, four
+  // instructions of 8 rows each per block of 32 rows. Waves 0-3 issue none,
+  // so their MFMAs never queue behind a load issue that waits for room in the
+  // CU's vector-memory queue, and each SIMD (one wave of either half) keeps
+  // its matrix core busy. A lane writes physical chunk lane % 8 of its row,
+  // so it fetches logical chunk (lane % 8) ^ swz(row). Rows past the end of
+  // A or W read as zero.
   const int w_rows = epi == EPI_SWIGLU ? 2 * N : N;
   const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(P.A, clamp_u32((int64_t)M * P.lda * 2));
   const __amdgpu_buffer_rsrc_t w_rsrc = make_rsrc(P.W, clamp_u32((int64_t)w_rows * P.ldw * 2));
   const int lr = lane >> 3, lp = lane & 7;
-  uint32_t a_off[2], w_off[2];
+  const bool loader = wave >= 4;
+  uint32_t a_off[2][2], w_off[2][2];  // [row block h: w' = wave - 4 h][row parity]
 #pragma unroll
-  for (int par = 0; par < 2; ++par) {
-    const int c = lp ^ (lr ^ par);
-    a_off[par] = (uint32_t)(((int64_t)(m0 + 32 * wave + lr) * P.lda + c * 8) * 2);
-    // SwiGLU: tile row j = 32 w + r belongs to wave column group j / 128 =
-    // w / 4; rows with (w % 4) < 2 are gate rows, the others the matching up
-    // rows (N further down), so each wave's 128 output columns hold gate and
-    // up values of the same 64 activations
-    int64_t wrow;
-    if (epi == EPI_SWIGLU)
-      wrow = tn * (BN / 2) + (wave >> 2) * 64 + 32 * (wave & 1) + lr + (((wave & 3) >= 2) ? N : 0);
-    else
-      wrow = (int64_t)tn * BN + 32 * wave + lr;
-    w_off[par] = (uint32_t)((wrow * P.ldw + c * 8) * 2);
-  }
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+      const int wb = wave - 4 * h;  // row block 32 wb .. 32 wb + 31
+      const int c = lp ^ (lr ^ par);
+      a_off[h][par] = (uint32_t)(((int64_t)(m0 + 32 * wb + lr) * P.lda + c * 8) * 2);
+      // SwiGLU: tile row j = 32 wb + r belongs to wave column group j / 128 =
+      // wb / 4; rows with (wb % 4) < 2 are gate rows, the others the matching
+      // up rows (N further down), so each wave's 128 output columns hold gate
+      // and up values of the same 64 activations
+      int64_t wrow;
+      if (epi == EPI_SWIGLU)
+        wrow = tn * (BN / 2) + (wb >> 2) * 64 + 32 * (wb & 1) + lr + (((wb & 3) >= 2) ? N : 0);
+      else
+        wrow = (int64_t)tn * BN + 32 * wb + lr;
+      w_off[h][par] = (uint32_t)((wrow * P.ldw + c * 8) * 2);
+    }
   const uint32_t a_istep = (uint32_t)(8 * P.lda * 2), w_istep = (uint32_t)(8 * P.ldw * 2);
   auto dma = [&](int kt, int stage) {
+    if (!loader) return;
     const uint32_t ko = (uint32_t)kt * (BK * 2);
-    u32x4* base = lds + stage * STAGE_U + wave * 32 * ROW_U;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_ptr_t)(base + i * 64), 16,
-                                               a_off[i & 1] + i * a_istep + ko, 0, 0, 0);
+    for (int h = 0; h < 2; ++h) {
+      u32x4* base = lds + stage * STAGE_U + (wave - 4 * h) * 32 * ROW_U;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rsrc, (lds_ptr_t)(base + BM * ROW_U + i * 64),
-                                               16, w_off[i & 1] + i * w_istep + ko, 0, 0, 0);
+      for (int i = 0; i < 4; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_ptr_t)(base + i * 64), 16,
+                                                 a_off[h][i & 1] + i * a_istep + ko, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rsrc, (lds_ptr_t)(base + BM * ROW_U + i * 64),
+                                                 16, w_off[h][i & 1] + i * w_istep + ko, 0, 0, 0);
+    }
   };
 
   // ---- MFMA fragments, double-buffered across k-steps
@@ -188,7 +201,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const GemmBatch args) 
   dma(0, 0);
   if (nk > 1) {
     dma(1, 1);
-    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    asm volatile("s_waitcnt vmcnt(16)" ::: "memory");  // a loader's 16 loads of slice 1 may fly
   } else {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
