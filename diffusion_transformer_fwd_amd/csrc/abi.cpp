@@ -108,7 +108,7 @@ BlockLayout block_layout(const dit_config& c, int kind, int64_t B, int64_t S) {
   const int64_t D = c.hidden, F = c.mlp_hidden;
   L.R = B * S;
   L.S_pad = round_up(S, 256);  // attention reads whole 256-query blocks
-  L.u_cols = kind == 0 ? std::max<int64_t>(3 * D, F) : 3 * D;
+  L.u_cols = kind == 0 ? F : 0;  // dual: the SwiGLU activation (q, k, v go straight to L.q/k/vt)
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -116,7 +116,7 @@ BlockLayout block_layout(const dit_config& c, int kind, int64_t B, int64_t S) {
     return o;
   };
   L.h = take((size_t)L.R * D * 2);
-  L.u = take((size_t)L.R * L.u_cols * 2);
+  if (L.u_cols) L.u = take((size_t)L.R * L.u_cols * 2);
   if (kind == 1) L.d6 = take((size_t)L.R * (D + F) * 2);
   else L.o = take((size_t)L.R * D * 2);
   const size_t qk = (size_t)B * c.heads * L.S_pad * c.head_dim * 2;
@@ -345,11 +345,36 @@ int run_norm(const dit::NormArgs& na, hipStream_t st) {
   return DIT_OK;
 }
 
-int run_qk_rope(const dit::QkRopeArgs& qa, hipStream_t st) {
-  const double tok = (double)qa.B * qa.S;
-  DIT_TRY(timed(DIT_K_QK_ROPE, 0.0, tok * 3.0 * qa.D * 2.0 * 2.0, st,
-                [&] { return dit::qk_rope_launch(qa, st); }));
+int run_qkv_pad(const dit::QkvPadArgs& pa, hipStream_t st) {
+  if (pa.S_pad <= pa.S) return DIT_OK;
+  const double bytes = (double)pa.B * pa.H * (pa.S_pad - pa.S) * 128.0 * 2.0 * 3.0;
+  DIT_TRY(timed(DIT_K_QKV_PAD, 0.0, bytes, st, [&] { return dit::qkv_pad_launch(pa, st); }));
   return DIT_OK;
+}
+
+// QKV projection with QK-RMSNorm + RoPE in the epilogue, then the zeros of the
+// padded rows. problems[] already hold A, W, rows and the token map.
+int run_qkv(const dit_config& c, const BlockLayout& L, void* ws, dit::GemmBatch& g,
+            const float* const* q_gain, const float* const* k_gain, const float* cos_t,
+            const float* sin_t, int32_t B, int64_t S, hipStream_t st) {
+  dit::QkvEpilogue& E = g.qkv;
+  E.q = bf(at(ws, L.q));
+  E.k = bf(at(ws, L.k));
+  E.vt = bf(at(ws, L.vt));
+  E.cos_t = cos_t;
+  E.sin_t = sin_t;
+  for (int i = 0; i < g.count; ++i) {
+    E.q_gain[i] = q_gain[i];
+    E.k_gain[i] = k_gain[i];
+  }
+  E.S_pad = L.S_pad;
+  E.H = c.heads;
+  E.D = c.hidden;
+  E.eps = c.eps;
+  E.q_scale = (float)(1.4426950408889634 / std::sqrt((double)c.head_dim));
+  DIT_CHECK(run_gemm(g, st));
+  dit::QkvPadArgs pa{E.q, E.k, E.vt, S, L.S_pad, B, c.heads};
+  return run_qkv_pad(pa, st);
 }
 
 int run_attention(const dit::AttnArgs& aa, hipStream_t st) {
@@ -476,39 +501,23 @@ int launch_dual(const dit_config& c, const dit_dual_weights& w, float* x, int32_
   DIT_CHECK(norm(0, 1));
   {
     dit::GemmBatch g{};
+    const float* qg[2];
+    const float* kg[2];
     for (int s = 0; s < 2; ++s) {
       if (rows[s] == 0) continue;
-      g.p[g.count++] = problem(h + first[s] * D, D, w.qkv[s], D, (int)rows[s], (int)(3 * D),
-                               (int)D, dit::EPI_BF16, u + first[s] * L.u_cols, L.u_cols);
+      dit::GemmProblem p = problem(h + first[s] * D, D, w.qkv[s], D, (int)rows[s], (int)(3 * D),
+                                   (int)D, dit::EPI_QKV, nullptr, 0);
+      set_rows(p, (int)seglen[s], 0, (int)segoff[s]);
+      qg[g.count] = w.q_gain[s];
+      kg[g.count] = w.k_gain[s];
+      g.p[g.count++] = p;
     }
-    DIT_CHECK(run_gemm(g, st));
+    DIT_CHECK(run_qkv(c, L, ws, g, qg, kg, cos_t, sin_t, B, S, st));
   }
-  dit::QkRopeArgs qa{};
-  qa.u = u;
-  qa.q = bf(at(ws, L.q));
-  qa.k = bf(at(ws, L.k));
-  qa.vt = bf(at(ws, L.vt));
-  qa.cos_t = cos_t;
-  qa.sin_t = sin_t;
-  for (int s = 0; s < 2; ++s) {
-    qa.q_gain[s] = w.q_gain[s];
-    qa.k_gain[s] = w.k_gain[s];
-  }
-  qa.ldu = L.u_cols;
-  qa.S = S;
-  qa.S_pad = L.S_pad;
-  qa.n_txt = n_txt;
-  qa.B = B;
-  qa.H = c.heads;
-  qa.D = (int)D;
-  qa.stream_major = 1;
-  qa.eps = c.eps;
-  qa.q_scale = (float)(1.4426950408889634 / std::sqrt((double)c.head_dim));
-  DIT_CHECK(run_qk_rope(qa, st));
   dit::AttnArgs aa{};
-  aa.q = qa.q;
-  aa.k = qa.k;
-  aa.vt = qa.vt;
+  aa.q = bf(at(ws, L.q));
+  aa.k = bf(at(ws, L.k));
+  aa.vt = bf(at(ws, L.vt));
   aa.o = o;
   aa.S = S;
   aa.S_pad = L.S_pad;
@@ -541,7 +550,6 @@ int launch_single(const dit_config& c, const dit_single_weights& w, float* x, in
   const BlockLayout L = block_layout(c, 1, B, S);
   const int64_t D = c.hidden, F = c.mlp_hidden, R = L.R;
   bf16_t* h = bf(at(ws, L.h));
-  bf16_t* u = bf(at(ws, L.u));
   bf16_t* d6 = bf(at(ws, L.d6));
   const int64_t ld6 = D + F;
 
@@ -565,35 +573,18 @@ int launch_single(const dit_config& c, const dit_single_weights& w, float* x, in
   {
     dit::GemmBatch g{};
     g.count = 2;
-    g.p[0] = problem(h, D, w.w_in, D, (int)R, (int)(3 * D), (int)D, dit::EPI_BF16, u, 3 * D);
+    g.p[0] = problem(h, D, w.w_in, D, (int)R, (int)(3 * D), (int)D, dit::EPI_QKV, nullptr, 0);
+    set_rows(g.p[0], (int)S, 0, 0);
     g.p[1] = problem(h, D, bf(w.w_in) + 3 * D * D, D, (int)R, (int)F, (int)D, dit::EPI_SWIGLU,
                      d6 + D, ld6);
-    DIT_CHECK(run_gemm(g, st));
+    const float* qg[2] = {w.q_gain, nullptr};
+    const float* kg[2] = {w.k_gain, nullptr};
+    DIT_CHECK(run_qkv(c, L, ws, g, qg, kg, cos_t, sin_t, B, S, st));
   }
-  dit::QkRopeArgs qa{};
-  qa.u = u;
-  qa.q = bf(at(ws, L.q));
-  qa.k = bf(at(ws, L.k));
-  qa.vt = bf(at(ws, L.vt));
-  qa.cos_t = cos_t;
-  qa.sin_t = sin_t;
-  qa.q_gain[0] = qa.q_gain[1] = w.q_gain;
-  qa.k_gain[0] = qa.k_gain[1] = w.k_gain;
-  qa.ldu = 3 * D;
-  qa.S = S;
-  qa.S_pad = L.S_pad;
-  qa.n_txt = 0;
-  qa.B = B;
-  qa.H = c.heads;
-  qa.D = (int)D;
-  qa.stream_major = 0;
-  qa.eps = c.eps;
-  qa.q_scale = (float)(1.4426950408889634 / std::sqrt((double)c.head_dim));
-  DIT_CHECK(run_qk_rope(qa, st));
   dit::AttnArgs aa{};
-  aa.q = qa.q;
-  aa.k = qa.k;
-  aa.vt = qa.vt;
+  aa.q = bf(at(ws, L.q));
+  aa.k = bf(at(ws, L.k));
+  aa.vt = bf(at(ws, L.vt));
   aa.o = d6;
   aa.S = S;
   aa.S_pad = L.S_pad;

@@ -79,18 +79,6 @@ __device__ __forceinline__ int key_of_row(int r) {
   return 16 * (j >> 1) + 8 * gp + 4 * (j & 1) + t;
 }
 
-// max / sum of x over lanes l and l ^ 32
-__device__ __forceinline__ float half_max(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                                  false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float half_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                                  false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
 template <int STG>
 using stage_t = std::integral_constant<int, STG>;
 

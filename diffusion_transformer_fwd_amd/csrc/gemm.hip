@@ -27,7 +27,9 @@
 //    16-byte (fp32) vectors.
 //  * Epilogues: bf16 store; SwiGLU (each wave's column half is gate rows and
 //    the other half the matching up rows, so SiLU(g) * u is lane-local);
-//    gated residual x += gate[b] * acc on the fp32 residual; fp32 store.
+//    gated residual x += gate[b] * acc on the fp32 residual; fp32 store; and
+//    QK-RMSNorm + RoPE straight into the attention operands (a wave's 128
+//    columns are one head), so the fused projection never round-trips HBM.
 //    Output rows go through a (segment length, stride, offset) map, so
 //    stream-major operands scatter back into x[B, S, D] in place.
 //  * Up to four independent problems share one launch (text + image
@@ -70,27 +72,16 @@ __device__ __forceinline__ void tile_coords(int local, int tiles_m, int tiles_n,
   tn = in / gsize;
 }
 
-__device__ __forceinline__ void store4(const GemmProblem& P, int epi, int64_t out_row,
-                                       int col, int b, f32x4 v) {
-  if (epi == EPI_BF16 || epi == EPI_SWIGLU) {
-    bf16_t* c = static_cast<bf16_t*>(P.C) + out_row * P.ldc + col;
-    *reinterpret_cast<u32x2*>(c) = pack_bf16x4(v);
-  } else if (epi == EPI_F32) {
-    float* c = static_cast<float*>(P.C) + out_row * P.ldc + col;
-    *reinterpret_cast<f32x4*>(c) = v;
-  } else {
-    float* c = static_cast<float*>(P.C) + out_row * P.ldc + col;
-    const f32x4 g = *reinterpret_cast<const f32x4*>(P.gate + (int64_t)b * P.gate_bstride + col);
-    f32x4 x = *reinterpret_cast<f32x4*>(c);
-    x += g * v;
-    *reinterpret_cast<f32x4*>(c) = x;
-  }
-}
-
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
+// EPI_QKV for one wave tile (64 rows x 128 columns = one head of q, k or v):
+// a row's 128 accumulators sit in lanes l and l ^ 32 (64 each), so the RMS
+// is lane-local plus one cross-half exchange; each lane's runs of 4 columns
+// hold two whole rotation pairs.
 __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const GemmBatch args) {
-  __shared__ u32x4 lds[2 * STAGE_U];
+  // two K-slice stages, then (EPI_QKV) 1 / rms of each tile row per wave column
+  __shared__ u32x4 lds[2 * STAGE_U + 2 * BM * 4 / 16];
+  float (*const row_scale)[BM] = reinterpret_cast<float (*)[BM]>(lds + 2 * STAGE_U);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int L = xcd_remap(blockIdx.x, gridDim.x);
@@ -226,39 +217,213 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const GemmBatch args) 
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  // ---- epilogue: lane holds row m0 + wm*64 + i*32 + fr, columns
-  //      (block j) j*32 + 8*q + 4*fg + 0..3 for q = 0..3
+  // ---- epilogue. Lane holds row wm*64 + i*32 + fr of the tile, columns
+  // (block j) wn*128 + j*32 + 8*q + 4*fg + 0..3 for q = 0..3. Results are
+  // staged in LDS (free now: every fragment read of the loop happened before
+  // its last barrier) and leave in whole rows, 16 bytes per lane: stores
+  // straight from the MFMA layout would be 16-byte pieces of 32 rows per
+  // instruction. Every wave reaches every barrier below.
+  char* const T = reinterpret_cast<char*>(lds);
+  // bf16 stage [256][256]: 16-byte chunk c of row r at c ^ (r & 31)
+  auto stage_bf16 = [&](int r, int col, f32x4 v) {
+    *reinterpret_cast<u32x2*>(T + r * 512 + (((col >> 3) ^ (r & 31)) << 4) + ((col & 4) << 1)) =
+        pack_bf16x4(v);
+  };
+  auto out_row_of = [&](int gr, int& b) -> int64_t {
+    b = gr / P.seg_len;
+    return (int64_t)b * P.seg_stride + P.seg_off + (gr - b * P.seg_len);
+  };
+
+  if (epi == EPI_F32 || epi == EPI_RESID) {
+    // fp32 stage [128][256] per pass (rows 128 p ..), 16-byte chunk c of row r at c ^ (r & 31)
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    const int r = m0 + wm * WTM + i * 32 + fr;
-    if (r >= M) continue;
-    const int b = r / P.seg_len;
-    const int64_t out_row = (int64_t)b * P.seg_stride + P.seg_off + (r - b * P.seg_len);
-    if (epi == EPI_SWIGLU) {
+    for (int pass = 0; pass < 2; ++pass) {
+      if ((wm >> 1) == pass) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int r = (wm & 1) * WTM + i * 32 + fr;
+              const int c = (wn * WTN + j * 32 + 8 * q + 4 * fg) >> 2;
+              f32x4 v;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e];
+              *reinterpret_cast<f32x4*>(T + r * 1024 + ((c ^ (r & 31)) << 4)) = v;
+            }
+      }
+      __syncthreads();
+#pragma unroll 4
+      for (int it = 0; it < 16; ++it) {
+        const int u = it * NT + tid;  // 16-byte unit: row u / 64, chunk u % 64
+        const int r = u >> 6, c = u & 63;
+        const int gr = m0 + pass * 128 + r, col = tn * BN + c * 4;
+        if (gr >= M || col >= N) continue;
+        const f32x4 v = *reinterpret_cast<const f32x4*>(T + r * 1024 + ((c ^ (r & 31)) << 4));
+        int b;
+        float* dst = static_cast<float*>(P.C) + out_row_of(gr, b) * P.ldc + col;
+        if (epi == EPI_F32) {
+          *reinterpret_cast<f32x4*>(dst) = v;
+        } else {
+          const f32x4 g = *reinterpret_cast<const f32x4*>(P.gate + (int64_t)b * P.gate_bstride + col);
+          f32x4 x = *reinterpret_cast<f32x4*>(dst);
+          x += g * v;
+          *reinterpret_cast<f32x4*>(dst) = x;
+        }
+      }
+      __syncthreads();
+    }
+    return;
+  }
+
+  // bf16 results: phase A, values into the stage
+  if (epi == EPI_SWIGLU) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN / 2; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int col = tn * (BN / 2) + wn * (WTN / 2) + j * 32 + 8 * q + 4 * fg;
-          if (col >= N) continue;
           f32x4 v;
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             v[e] = silu_f(acc[i][j][4 * q + e]) * acc[i][j + FN / 2][4 * q + e];
-          store4(P, EPI_SWIGLU, out_row, col, b, v);
+          stage_bf16(wm * WTM + i * 32 + fr, wn * (WTN / 2) + j * 32 + 8 * q + 4 * fg, v);
         }
-    } else {
+  } else if (epi == EPI_QKV && tn * BN + wn * WTN < N && (tn * BN + wn * WTN) / args.qkv.D < 2) {
+    // q or k head (the wave's 128 columns): the row's 1 / rms (times q_scale
+    // for q) from the fp32 accumulators, kept per row in LDS; a row's 128
+    // values sit in lanes l and l ^ 32, so the sum of squares needs one
+    // cross-half exchange. The values are staged raw; gain and rotation are
+    // applied on the way out, where 16 lanes share a token row.
+    const QkvEpilogue& E = args.qkv;
+    const float sc = (tn * BN + wn * WTN) / E.D == 0 ? E.q_scale : 1.f;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      float ss = 0.f;
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) ss += acc[i][j][e] * acc[i][j][e];
+      ss = half_sum(ss);
+      if (fg == 0) row_scale[wn][wm * WTM + i * 32 + fr] = rsqrtf(ss * (1.f / 128.f) + E.eps) * sc;
 #pragma unroll
       for (int j = 0; j < FN; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int col = tn * BN + wn * WTN + j * 32 + 8 * q + 4 * fg;
-          if (col >= N) continue;
           f32x4 v;
 #pragma unroll
           for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e];
-          store4(P, epi, out_row, col, b, v);
+          stage_bf16(wm * WTM + i * 32 + fr, wn * WTN + j * 32 + 8 * q + 4 * fg, v);
         }
+    }
+  } else {
+    // plain bf16 (also the v heads of EPI_QKV)
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          f32x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e];
+          stage_bf16(wm * WTM + i * 32 + fr, wn * WTN + j * 32 + 8 * q + 4 * fg, v);
+        }
+  }
+  __syncthreads();
+
+  // phase B: whole rows out, 16 bytes per lane
+  if (epi != EPI_QKV) {
+    const int ncol = epi == EPI_SWIGLU ? BN / 2 : BN;  // output columns of the tile
+    const int upr = ncol / 8;                          // 16-byte units per row
+#pragma unroll 4
+    for (int it = 0; it < 256 * (BN / 8) / NT; ++it) {
+      const int u = it * NT + tid;
+      if (u >= 256 * upr) break;
+      const int r = u / upr, c = u - r * upr;
+      const int gr = m0 + r, col = tn * ncol + c * 8;
+      if (gr >= M || col >= N) continue;
+      int b;
+      *reinterpret_cast<u32x4*>(static_cast<bf16_t*>(P.C) + out_row_of(gr, b) * P.ldc + col) =
+          *reinterpret_cast<const u32x4*>(T + r * 512 + ((c ^ (r & 31)) << 4));
+    }
+    return;
+  }
+  // EPI_QKV: per 128-column head of the tile: q / k rows to [b, h, s, :]
+  // (16 lanes per token), v gathered 8 tokens per dim to v^T[b, h, d, s..s+7]
+  const QkvEpilogue& E = args.qkv;
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    const int col0 = tn * BN + hh * 128;
+    if (col0 >= N) break;
+    const int part = col0 / E.D;
+    const int h = (col0 - part * E.D) >> 7;
+    if (part < 2) {
+      // 16 lanes per token row, 8 columns (4 rotation pairs) per lane
+      bf16_t* base = part == 0 ? E.q : E.k;
+      const float* gain = part == 0 ? E.q_gain[pi] : E.k_gain[pi];
+      const int cl = (tid & 15) * 8;  // column within the head
+      const f32x4 g0 = *reinterpret_cast<const f32x4*>(gain + cl);
+      const f32x4 g1 = *reinterpret_cast<const f32x4*>(gain + cl + 4);
+#pragma unroll 4
+      for (int it = 0; it < 256 * 16 / NT; ++it) {
+        const int u = it * NT + tid;
+        const int r = u >> 4, c = hh * 16 + (u & 15);
+        const int gr = m0 + r;
+        if (gr >= M) continue;
+        const int b = gr / P.seg_len;
+        const int s = P.seg_off + (gr - b * P.seg_len);
+        const u32x4 raw = *reinterpret_cast<const u32x4*>(T + r * 512 + ((c ^ (r & 31)) << 4));
+        const float rsc = row_scale[hh][r];
+        const f32x4 co = *reinterpret_cast<const f32x4*>(E.cos_t + (int64_t)s * 64 + (cl >> 1));
+        const f32x4 si = *reinterpret_cast<const f32x4*>(E.sin_t + (int64_t)s * 64 + (cl >> 1));
+        f32x8 y;
+#pragma unroll
+        for (int pr = 0; pr < 4; ++pr) {
+          const float gx0 = pr < 2 ? g0[2 * pr] : g1[2 * pr - 4];
+          const float gx1 = pr < 2 ? g0[2 * pr + 1] : g1[2 * pr - 3];
+          const float x0 = bf16_to_f32(raw[pr] & 0xFFFFu) * rsc * gx0;
+          const float x1 = bf16_to_f32(raw[pr] >> 16) * rsc * gx1;
+          y[2 * pr] = x0 * co[pr] - x1 * si[pr];
+          y[2 * pr + 1] = x0 * si[pr] + x1 * co[pr];
+        }
+        *reinterpret_cast<bf16x8*>(base + (((int64_t)b * E.H + h) * E.S_pad + s) * 128 + cl) =
+            pack_bf16x8(y);
+      }
+    } else {
+#pragma unroll 2
+      for (int it = 0; it < 128 * 32 / NT; ++it) {
+        const int u = it * NT + tid;
+        const int d = u & 127, tg = u >> 7;  // dim, group of 8 tokens
+        const int colb = ((hh * 128 + d) >> 3), wb = (d & 7) << 1;
+        uint16_t tok[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int r = tg * 8 + e;
+          tok[e] = *reinterpret_cast<const uint16_t*>(T + r * 512 + ((colb ^ (r & 31)) << 4) + wb);
+        }
+        const int r0 = m0 + tg * 8;
+        if (r0 >= M) continue;
+        const int b0 = r0 / P.seg_len;
+        const int s0 = P.seg_off + (r0 - b0 * P.seg_len);
+        if (r0 + 7 < M && (r0 + 7) / P.seg_len == b0 && (s0 & 7) == 0) {
+          u32x4 pk;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) pk[e] = (uint32_t)tok[2 * e] | ((uint32_t)tok[2 * e + 1] << 16);
+          *reinterpret_cast<u32x4*>(E.vt + (((int64_t)b0 * E.H + h) * 128 + d) * E.S_pad + s0) = pk;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int gr = r0 + e;
+            if (gr >= M) break;
+            const int b = gr / P.seg_len;
+            const int s = P.seg_off + (gr - b * P.seg_len);
+            E.vt[(((int64_t)b * E.H + h) * 128 + d) * E.S_pad + s] = tok[e];
+          }
+        }
+      }
     }
   }
 }

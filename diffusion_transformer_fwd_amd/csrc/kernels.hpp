@@ -21,7 +21,14 @@ enum Epilogue : int32_t {
                    //   [0, N) are gate rows and [N, 2N) are up rows
   EPI_RESID = 2,   // C fp32: C[row, n] += gate[b * gate_bstride + n] * acc,
                    //   b = r / seg_len
-  EPI_F32 = 3      // C fp32: C[row, n] = acc
+  EPI_F32 = 3,     // C fp32: C[row, n] = acc
+  EPI_QKV = 4      // QK-RMSNorm + RoPE into the attention operands (C unused):
+                   //   N = 3D columns q | k | v, head h = columns 128h..128h+127
+                   //   of each third; row r is token s = seg_off + r % seg_len
+                   //   of batch row b = r / seg_len. q, k: per head vector
+                   //   x / sqrt(mean(x^2) + eps) * gain, rotated by the token's
+                   //   (cos, sin) per adjacent pair, q also times q_scale,
+                   //   stored bf16 at [b, h, s, :]; v stored bf16 at v^T[b, h, :, s]
 };
 
 struct GemmProblem {
@@ -37,13 +44,30 @@ struct GemmProblem {
 
 constexpr int kMaxGemmProblems = 4;
 
+// Operands of the EPI_QKV epilogue, shared by the problems of a launch; the
+// QK gains are per problem (text and image streams differ).
+struct QkvEpilogue {
+  bf16_t* q;             // [B, H, S_pad, 128]
+  bf16_t* k;             // [B, H, S_pad, 128]
+  bf16_t* vt;            // [B, H, 128, S_pad]
+  const float* cos_t;    // [S, 64]
+  const float* sin_t;
+  const float* q_gain[kMaxGemmProblems];  // [128] each
+  const float* k_gain[kMaxGemmProblems];
+  int64_t S_pad;
+  int32_t H, D;
+  float eps, q_scale;    // q_scale = log2(e) / sqrt(head_dim)
+};
+
 struct GemmBatch {
   GemmProblem p[kMaxGemmProblems];
   int32_t count;
   int32_t total_tiles;
+  QkvEpilogue qkv;
 };
 
-// Requirements checked by the caller: K % 64 == 0, N % 32 == 0,
+// Requirements checked by the caller: K % 64 == 0, N % 32 == 0 (EPI_QKV: N = 3D,
+// D % 128 == 0),
 // lda/ldw % 8 == 0, 16-byte aligned A and W; ldc % 4 == 0.
 constexpr int kGemmBM = 256, kGemmBN = 256, kGemmBK = 64;
 
@@ -69,33 +93,26 @@ struct NormArgs {
 };
 hipError_t modnorm_launch(const NormArgs& a, hipStream_t stream);
 
-// ------------------------------------------------------------------ QK-norm + RoPE
-// From the fused projection rows (q | k | v, each D wide, row stride ldu),
-// writes q, k: [B, H, S_pad, 128] and v^T: [B, H, 128, S_pad] (bf16); rows
-// s >= S of the padded outputs are zero. A token (b, s) is read from row
-//   stream_major ? (s < n_txt ? b*n_txt + s : B*n_txt + b*(S-n_txt) + s-n_txt)
-//                : b*S + s.
-// Text rows use gains [0], the rest gains [1].
-struct QkRopeArgs {
-  const bf16_t* u;
+// ------------------------------------------------------------------ padding
+// Zeroes rows s in [S, S_pad) of q and k [B, H, S_pad, 128] and columns
+// [S, S_pad) of v^T [B, H, 128, S_pad]: the attention kernel reads whole
+// 64-key tiles, and a padded V column must be finite (its probability is 0).
+struct QkvPadArgs {
   bf16_t* q;
   bf16_t* k;
   bf16_t* vt;
-  const float* cos_t;  // [S, 64]
-  const float* sin_t;
-  const float* q_gain[2];
-  const float* k_gain[2];
-  int64_t ldu, S, S_pad, n_txt;
-  int32_t B, H, D, stream_major;
-  float eps;
-  float q_scale;  // applied to q before rounding: log2(e) / sqrt(head_dim)
+  int64_t S, S_pad;
+  int32_t B, H;
 };
-hipError_t qk_rope_launch(const QkRopeArgs& a, hipStream_t stream);
+hipError_t qkv_pad_launch(const QkvPadArgs& a, hipStream_t stream);
 
 // ------------------------------------------------------------------ attention
 // O = softmax(q k^T / sqrt(128)) v for every (b, h), no mask, over S keys.
-// q, k [B, H, S_pad, 128], vt [B, H, 128, S_pad] (zero beyond S). Output row
-// of token (b, s) as in QkRopeArgs' mapping; written at o + row * ldo + h*128.
+// q (pre-scaled by log2(e) / sqrt(128)), k [B, H, S_pad, 128], vt [B, H, 128,
+// S_pad] (zero beyond S). The output row of token (b, s) is
+//   stream_major ? (s < n_txt ? b*n_txt + s : B*n_txt + b*(S-n_txt) + s-n_txt)
+//                : b*S + s,
+// written at o + row * ldo + h * 128.
 struct AttnArgs {
   const bf16_t* q;
   const bf16_t* k;

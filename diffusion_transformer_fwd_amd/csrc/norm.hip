@@ -1,6 +1,7 @@
 // Bandwidth-bound kernels of the step on gfx950:
 //   * modnorm: AdaLN pre-norm of the fp32 residual into a bf16 GEMM operand
-//   * qk_rope: per-head QK-RMSNorm + RoPE + relayout for attention
+//   * qkv_pad: zeros of the padded attention operand rows (QK-RMSNorm and
+//     RoPE themselves run in the QKV GEMM's epilogue)
 //   * rope_tables: cos/sin of every pair angle from integer positions
 //   * time_features + gemv: the global modulation vectors from sigma
 //
@@ -67,114 +68,21 @@ __global__ __launch_bounds__(256) void modnorm_kernel(const NormArgs a) {
   }
 }
 
-// ------------------------------------------------------------------ qk_rope
-// Workgroup = (64 tokens, one head, one batch row), 256 threads.
-//  q, k: each token's 128-wide head vector is handled by 16 lanes (8
-//   elements = 4 adjacent pairs each): fp32 RMS over the group of 16 lanes,
-//   times the gain, then each pair (x0, x1) -> (x0 c - x1 s, x0 s + x1 c)
-//   with the token's (c, s) for that pair; written token-major per head.
-//   q is also multiplied by q_scale = log2(e) / sqrt(head_dim), the softmax
-//   scale in base 2 that the attention kernel expects to find applied.
-//  v: the 64 x 128 block is transposed through LDS and written
-//   feature-major (v^T), the layout the attention kernel's PV product reads.
-//  Tokens s >= S of the padded outputs are written as zeros.
-__global__ __launch_bounds__(256) void qk_rope_kernel(const QkRopeArgs a) {
-  __shared__ uint16_t vtile[64][128 + 8];
-  const int tid = threadIdx.x;
-  const int h = blockIdx.y, b = blockIdx.z;
-  const int64_t s0 = (int64_t)blockIdx.x * 64;
-  const int D = a.D;
-  const int64_t bh = (int64_t)b * a.H + h;
-
-  auto src_row = [&](int64_t s) -> int64_t {
-    if (!a.stream_major) return (int64_t)b * a.S + s;
-    if (s < a.n_txt) return (int64_t)b * a.n_txt + s;
-    return (int64_t)a.B * a.n_txt + (int64_t)b * (a.S - a.n_txt) + (s - a.n_txt);
-  };
-
-  // q and k: 64 tokens x 2 tensors = 128 vectors, 16 lanes each -> 8 passes
-  const int g = tid >> 4, gl = tid & 15;  // group (16 per pass), lane in group
-#pragma unroll 2
-  for (int pass = 0; pass < 8; ++pass) {
-    const int vec = pass * 16 + g;         // 0..127
-    const int which = vec >> 6;            // 0 = q, 1 = k
-    const int64_t s = s0 + (vec & 63);
-    bf16_t* dst = (which ? a.k : a.q) + (bh * a.S_pad + s) * 128 + gl * 8;
-    if (s >= a.S) {
-      *reinterpret_cast<u32x4*>(dst) = u32x4{0u, 0u, 0u, 0u};
-      continue;
-    }
-    const bf16_t* src = a.u + src_row(s) * a.ldu + which * D + h * 128 + gl * 8;
-    const u32x4 raw = *reinterpret_cast<const u32x4*>(src);
-    float x[8];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      x[2 * e] = bf16_to_f32(raw[e] & 0xFFFFu);
-      x[2 * e + 1] = bf16_to_f32(raw[e] >> 16);
-    }
-    float ss = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
-    ss = group_sum<16>(ss);
-    const float rstd = rsqrtf(ss * (1.f / 128.f) + a.eps);
-    const int st = s < a.n_txt ? 0 : 1;
-    const float* gain = which ? a.k_gain[st] : a.q_gain[st];
-    const f32x4 g0 = *reinterpret_cast<const f32x4*>(gain + gl * 8);
-    const f32x4 g1 = *reinterpret_cast<const f32x4*>(gain + gl * 8 + 4);
-    const float gv[8] = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
-    const f32x4 c = *reinterpret_cast<const f32x4*>(a.cos_t + s * 64 + gl * 4);
-    const f32x4 sn = *reinterpret_cast<const f32x4*>(a.sin_t + s * 64 + gl * 4);
-    // q also takes the attention scale log2(e) / sqrt(head_dim) here, so
-    // that its single rounding to bf16 happens on the scaled value
-    const float sc = which ? rstd : rstd * a.q_scale;
-    f32x8 y;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const float x0 = x[2 * p] * sc * gv[2 * p];
-      const float x1 = x[2 * p + 1] * sc * gv[2 * p + 1];
-      y[2 * p] = x0 * c[p] - x1 * sn[p];
-      y[2 * p + 1] = x0 * sn[p] + x1 * c[p];
-    }
-    *reinterpret_cast<bf16x8*>(dst) = pack_bf16x8(y);
+// ------------------------------------------------------------------ qkv padding
+// Grid (B * H), 256 threads: zero q, k rows [S, S_pad) (128 bf16 each) and
+// v^T columns [S, S_pad) of its 128 rows, with 2-byte stores (the pad is at
+// most 255 tokens).
+__global__ __launch_bounds__(256) void qkv_pad_kernel(const QkvPadArgs a) {
+  const int64_t bh = blockIdx.x;
+  const int64_t pad = a.S_pad - a.S;
+  bf16_t* q = a.q + (bh * a.S_pad + a.S) * 128;
+  bf16_t* k = a.k + (bh * a.S_pad + a.S) * 128;
+  for (int64_t i = threadIdx.x; i < pad * 128; i += blockDim.x) {
+    q[i] = 0;
+    k[i] = 0;
   }
-
-  // v: stage 64 tokens x 128 features, then write 128 features x 64 tokens
-  {
-    const int t = tid >> 2, part = tid & 3;  // token, 32-feature quarter
-    const int64_t s = s0 + t;
-    u32x4 vals[4];
-    if (s < a.S) {
-      const bf16_t* src = a.u + src_row(s) * a.ldu + 2 * D + h * 128 + part * 32;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) vals[i] = reinterpret_cast<const u32x4*>(src)[i];
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) vals[i] = u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        vtile[t][part * 32 + i * 8 + 2 * e] = (uint16_t)(vals[i][e] & 0xFFFFu);
-        vtile[t][part * 32 + i * 8 + 2 * e + 1] = (uint16_t)(vals[i][e] >> 16);
-      }
-  }
-  __syncthreads();
-  {
-    // thread -> feature f = tid / 2, 32 tokens (half = tid & 1)
-    const int f = tid >> 1, half = tid & 1;
-    bf16_t* dst = a.vt + (bh * 128 + f) * a.S_pad + s0 + half * 32;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      u32x4 w;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = half * 32 + i * 8 + 2 * e;
-        w[e] = (uint32_t)vtile[t][f] | ((uint32_t)vtile[t + 1][f] << 16);
-      }
-      reinterpret_cast<u32x4*>(dst)[i] = w;
-    }
-  }
+  bf16_t* vt = a.vt + bh * 128 * a.S_pad + a.S;
+  for (int64_t i = threadIdx.x; i < pad * 128; i += blockDim.x) vt[(i / pad) * a.S_pad + i % pad] = 0;
 }
 
 // ------------------------------------------------------------------ rope tables
@@ -283,10 +191,9 @@ hipError_t modnorm_launch(const NormArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t qk_rope_launch(const QkRopeArgs& a, hipStream_t stream) {
-  if (a.S_pad == 0 || a.B == 0) return hipSuccess;
-  const dim3 grid((unsigned)(a.S_pad / 64), (unsigned)a.H, (unsigned)a.B);
-  hipLaunchKernelGGL(qk_rope_kernel, grid, dim3(256), 0, stream, a);
+hipError_t qkv_pad_launch(const QkvPadArgs& a, hipStream_t stream) {
+  if (a.S_pad <= a.S || a.B == 0) return hipSuccess;
+  hipLaunchKernelGGL(qkv_pad_kernel, dim3((unsigned)((int64_t)a.B * a.H)), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
