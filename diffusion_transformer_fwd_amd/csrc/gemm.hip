@@ -35,12 +35,16 @@
 //  * Up to four independent problems share one launch (text + image
 //    streams, or the single block's QKV part + SwiGLU part), so the small
 //    512-row text problem fills gaps instead of taking its own launch.
+//  * Launches without the SwiGLU / QKV epilogues may use 256 x 224 tiles
+//    when that takes fewer rounds of tiles over the CUs (the N = 3072
+//    projections at 4608 rows: 252 tiles in one round instead of 216 full
+//    ones leaving 40 CUs idle).
 //  * Tile order: launch index -> XCD-contiguous logical index -> groups of
 //    8 row tiles walked column by column, so co-resident tiles on one XCD
 //    share A and W panels in its L2.
 //  * The accumulation order of an output element depends only on K, never
-//    on M or the tile position, so a batch row's results are bitwise the
-//    same whatever else is in the batch.
+//    on M, the tile width or the tile position, so a batch row's results
+//    are bitwise the same whatever else is in the batch.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -74,16 +78,27 @@ __device__ __forceinline__ void tile_coords(int local, int tiles_m, int tiles_n,
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
+template <int V>
+struct count_t {
+  static constexpr int value = V;
+};
+
 // EPI_QKV for one wave tile (64 rows x 128 columns = one head of q, k or v):
 // a row's 128 accumulators sit in lanes l and l ^ 32 (64 each), so the RMS
 // is lane-local plus one cross-half exchange; each lane's runs of 4 columns
 // hold two whole rotation pairs.
+// BNT: output columns per tile, 256 or 224 (BF16 / F32 / RESID epilogues
+// only). At 224 the N = 1 waves run three 32-column blocks instead of four
+// and W tile rows 224..255 are never loaded; per output element nothing
+// changes (same MFMA, same k order), so the width may be picked per launch.
+template <int BNT>
 __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const GemmBatch args) {
   // two K-slice stages, then (EPI_QKV) 1 / rms of each tile row per wave column
   __shared__ u32x4 lds[2 * STAGE_U + 2 * BM * 4 / 16];
   float (*const row_scale)[BM] = reinterpret_cast<float (*)[BM]>(lds + 2 * STAGE_U);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int L = xcd_remap(blockIdx.x, gridDim.x);
   int pi = 0;
 #pragma unroll
@@ -131,7 +146,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const GemmBatch args) 
       if (epi == EPI_SWIGLU)
         wrow = tn * (BN / 2) + (wb >> 2) * 64 + 32 * (wb & 1) + lr + (((wb & 3) >= 2) ? N : 0);
       else
-        wrow = (int64_t)tn * BN + 32 * wb + lr;
+        wrow = (int64_t)tn * BNT + 32 * wb + lr;
       w_off[h][par] = (uint32_t)((wrow * P.ldw + c * 8) * 2);
     }
   const uint32_t a_istep = (uint32_t)(8 * P.lda * 2), w_istep = (uint32_t)(8 * P.ldw * 2);
@@ -145,6 +160,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const GemmBatch args) 
       for (int i = 0; i < 4; ++i)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_ptr_t)(base + i * 64), 16,
                                                  a_off[h][i & 1] + i * a_istep + ko, 0, 0, 0);
+      if (BNT == 224 && wave - 4 * h == 7) continue;  // W rows 224..255: not in the tile
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rsrc, (lds_ptr_t)(base + BM * ROW_U + i * 64),
@@ -159,14 +175,16 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const GemmBatch args) 
   const int w_rd = BM * ROW_U + (wn * WTN + fr) * ROW_U;
   const int sfr = swz(fr);
   bf16x8 af[2][FM], wf[2][FN];
-  auto fload = [&](int stage, int s, int buf) {
+  // FNA (a compile-time count): the wave's active 32-column blocks
+  auto fload = [&](auto fna, int stage, int s, int buf) {
+    constexpr int FNA = decltype(fna)::value;
     const u32x4* st = lds + stage * STAGE_U;
     const int ch = (2 * s + fg) ^ sfr;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
       af[buf][i] = __builtin_bit_cast(bf16x8, st[a_rd + i * 32 * ROW_U + ch]);
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
+    for (int j = 0; j < FNA; ++j)
       wf[buf][j] = __builtin_bit_cast(bf16x8, st[w_rd + j * 32 * ROW_U + ch]);
   };
   f32x16 acc[FM][FN];
@@ -174,11 +192,12 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const GemmBatch args) 
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
-  auto mfmas = [&](int buf) {
+  auto mfmas = [&](auto fna, int buf) {
+    constexpr int FNA = decltype(fna)::value;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
+      for (int j = 0; j < FNA; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[buf][j], af[buf][i], acc[i][j],
                                                             0, 0, 0);
   };
@@ -192,30 +211,36 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const GemmBatch args) 
   dma(0, 0);
   if (nk > 1) {
     dma(1, 1);
-    asm volatile("s_waitcnt vmcnt(16)" ::: "memory");  // a loader's 16 loads of slice 1 may fly
+    // a loader's loads of slice 1 may fly (16, or 12 for the wave that skips W rows 224..255)
+    if (BNT == 224 && wave == 7) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
   } else {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
   __syncthreads();
-  fload(0, 0, 0);
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
+  auto main_loop = [&](auto fna) {
+    fload(fna, 0, 0, 0);
+    for (int kt = 0; kt < nk; ++kt) {
+      const int cur = kt & 1;
 #pragma unroll
-    for (int s = 0; s < BK / 16 - 1; ++s) {
-      fload(cur, s + 1, (s + 1) & 1);
+      for (int s = 0; s < BK / 16 - 1; ++s) {
+        fload(fna, cur, s + 1, (s + 1) & 1);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(fna, s & 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // everyone is done with this stage and slice kt + 1 has landed
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (kt + 2 < nk) dma(kt + 2, cur);
+      if (kt + 1 < nk) fload(fna, cur ^ 1, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
-      mfmas(s & 1);
+      mfmas(fna, (BK / 16 - 1) & 1);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // everyone is done with this stage and slice kt + 1 has landed
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (kt + 2 < nk) dma(kt + 2, cur);
-    if (kt + 1 < nk) fload(cur ^ 1, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    mfmas((BK / 16 - 1) & 1);
-    __builtin_amdgcn_sched_barrier(0);
-  }
+  };
+  if (BNT == 224 && wn == 1) main_loop(count_t<FN - 1>{});
+  else main_loop(count_t<FN>{});
 
   // ---- epilogue. Lane holds row wm*64 + i*32 + fr of the tile, columns
   // (block j) wn*128 + j*32 + 8*q + 4*fg + 0..3 for q = 0..3. Results are
@@ -254,22 +279,36 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const GemmBatch args) 
             }
       }
       __syncthreads();
-#pragma unroll 4
-      for (int it = 0; it < 16; ++it) {
-        const int u = it * NT + tid;  // 16-byte unit: row u / 64, chunk u % 64
-        const int r = u >> 6, c = u & 63;
-        const int gr = m0 + pass * 128 + r, col = tn * BN + c * 4;
-        if (gr >= M || col >= N) continue;
-        const f32x4 v = *reinterpret_cast<const f32x4*>(T + r * 1024 + ((c ^ (r & 31)) << 4));
-        int b;
-        float* dst = static_cast<float*>(P.C) + out_row_of(gr, b) * P.ldc + col;
-        if (epi == EPI_F32) {
-          *reinterpret_cast<f32x4*>(dst) = v;
-        } else {
-          const f32x4 g = *reinterpret_cast<const f32x4*>(P.gate + (int64_t)b * P.gate_bstride + col);
-          f32x4 x = *reinterpret_cast<f32x4*>(dst);
-          x += g * v;
-          *reinterpret_cast<f32x4*>(dst) = x;
+      // 16-byte unit u = it * NT + tid: row u / 64 = 8 it + wave, chunk
+      // u % 64 = lane. The residual and gate reads of 8 rows are issued
+      // together before any store (a store could alias a later read, so the
+      // compiler would not move reads above it), one memory latency per 8 rows.
+      const int c = lane, col = tn * BNT + c * 4;
+      const bool col_ok = c * 4 < BNT && col < N;
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        float* dst[8];
+        f32x4 x[8], g[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int r = 8 * (8 * half + k) + wave;
+          const int gr = m0 + pass * 128 + r;
+          dst[k] = nullptr;
+          if (col_ok && gr < M) {
+            int b;
+            dst[k] = static_cast<float*>(P.C) + out_row_of(gr, b) * P.ldc + col;
+            if (epi == EPI_RESID) {
+              g[k] = *reinterpret_cast<const f32x4*>(P.gate + (int64_t)b * P.gate_bstride + col);
+              x[k] = *reinterpret_cast<const f32x4*>(dst[k]);
+            }
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int r = 8 * (8 * half + k) + wave;
+          if (dst[k] == nullptr) continue;
+          const f32x4 v = *reinterpret_cast<const f32x4*>(T + r * 1024 + ((c ^ (r & 31)) << 4));
+          *reinterpret_cast<f32x4*>(dst[k]) = epi == EPI_RESID ? x[k] + g[k] * v : v;
         }
       }
       __syncthreads();
@@ -336,7 +375,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const GemmBatch args) 
 
   // phase B: whole rows out, 16 bytes per lane
   if (epi != EPI_QKV) {
-    const int ncol = epi == EPI_SWIGLU ? BN / 2 : BN;  // output columns of the tile
+    const int ncol = epi == EPI_SWIGLU ? BN / 2 : BNT;  // output columns of the tile
     const int upr = ncol / 8;                          // 16-byte units per row
 #pragma unroll 4
     for (int it = 0; it < 256 * (BN / 8) / NT; ++it) {
@@ -428,22 +467,63 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const GemmBatch args) 
   }
 }
 
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// Tile counts of every problem for tile width bnt; returns the total.
+int64_t assign_tiles(GemmBatch& batch, int bnt) {
+  int64_t total = 0;
+  for (int i = 0; i < batch.count; ++i) {
+    GemmProblem& p = batch.p[i];
+    const int cols = p.epi == EPI_SWIGLU ? BN / 2 : bnt;
+    p.tiles_m = (p.M + BM - 1) / BM;
+    p.tiles_n = (p.N + cols - 1) / cols;
+    p.tile_begin = (int32_t)total;
+    total += (int64_t)p.tiles_m * p.tiles_n;
+  }
+  return total;
+}
+
 }  // namespace
 
 hipError_t gemm_launch(GemmBatch& batch, hipStream_t stream) {
-  int total = 0;
-  for (int i = 0; i < batch.count; ++i) {
-    GemmProblem& p = batch.p[i];
-    const int cols = p.epi == EPI_SWIGLU ? BN / 2 : BN;
-    p.tiles_m = (p.M + BM - 1) / BM;
-    p.tiles_n = (p.N + cols - 1) / cols;
-    p.tile_begin = total;
-    total += p.tiles_m * p.tiles_n;
-  }
   for (int i = batch.count; i < kMaxGemmProblems; ++i) batch.p[i] = GemmProblem{};
-  batch.total_tiles = total;
+  // Tile width: 224 instead of 256 when every epilogue allows it and the
+  // launch then takes fewer rounds x per-tile time. A 224-wide tile does 7/8
+  // of the MFMA work but loads 15/16 of the bytes, and the loads bound it,
+  // so its time counts as 15/16. E.g. N = 3072 at M = 4608: 216 tiles of 256
+  // leave 40 of 256 CUs idle for the whole launch, 252 tiles of 224 finish
+  // in one shorter round; N = 27648 keeps 256 (8 rounds against 9 x 15/16).
+  bool narrow_ok = true;
+  for (int i = 0; i < batch.count; ++i)
+    if (batch.p[i].epi == EPI_SWIGLU || batch.p[i].epi == EPI_QKV) narrow_ok = false;
+  int bnt = BN;
+  if (narrow_ok) {
+    const int64_t cus = device_cus();
+    const int64_t r256 = (assign_tiles(batch, 256) + cus - 1) / cus;
+    const int64_t r224 = (assign_tiles(batch, 224) + cus - 1) / cus;
+    if (r224 * 15 < r256 * 16) bnt = 224;
+  }
+  const int64_t total = assign_tiles(batch, bnt);
+  if (total > INT32_MAX) return hipErrorInvalidValue;
+  batch.total_tiles = (int32_t)total;
   if (total == 0) return hipSuccess;
-  hipLaunchKernelGGL(gemm_bf16_kernel, dim3(total), dim3(NT), 0, stream, batch);
+  if (bnt == 224)
+    hipLaunchKernelGGL(gemm_bf16_kernel<224>, dim3((unsigned)total), dim3(NT), 0, stream, batch);
+  else
+    hipLaunchKernelGGL(gemm_bf16_kernel<256>, dim3((unsigned)total), dim3(NT), 0, stream, batch);
   return hipGetLastError();
 }
 
