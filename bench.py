@@ -69,10 +69,17 @@ def summarize(d):
     for f in sorted(glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)):
         rows = list(csv.DictReader(open(f)))
         out.append("| kernel | calls | avg us | total ms | % |\n|---|---|---|---|---|")
+        g_calls, g_ns = 0, 0.0
         for r in rows:
             name = r["Name"].replace("dit::(anonymous namespace)::", "").split("(")[0]
             out.append(f"| {name} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                        f"{float(r['TotalDurationNs']) / 1e6:.2f} | {float(r['Percentage']):.2f} |")
+            if "gemm_bf16_kernel" in name:  # every tile-width instance
+                g_calls += int(r["Calls"])
+                g_ns += float(r["TotalDurationNs"])
+        if g_calls:
+            out.append(f"gemm_bf16_kernel, all instances: {g_calls} calls, "
+                       f"avg {g_ns / g_calls / 1e3:.1f} us")
     for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
         per = collections.defaultdict(lambda: collections.defaultdict(float))
         names = {}
@@ -95,7 +102,7 @@ def summarize(d):
             for c in sorted({c for x in lst for c in x}):
                 vals = [x[c] for x in lst if c in x]
                 out.append(f"| {k} | {len(vals)} | {c} | {sum(vals) / len(vals):.6g} |")
-        gemm = by_kernel.get("gemm_bf16_kernel", [])
+        gemm = [x for k, lst in by_kernel.items() if "gemm_bf16_kernel" in k for x in lst]
         for c in ("FETCH_SIZE", "WRITE_SIZE"):
             vals = [x[c] for x in gemm if c in x]
             if vals and c in cal:
