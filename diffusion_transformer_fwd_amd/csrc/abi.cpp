@@ -337,6 +337,75 @@ int run_gemm(dit::GemmBatch& g, hipStream_t st) {
   return DIT_OK;
 }
 
+// K split of a GEMM whose tiles alone would leave most CUs idle for the whole
+// launch: the final projection (N = 128, one column of tiles) and the text
+// embedding (K = 7680 on 2 B row tiles). The chunk count depends on N and K
+// only, never on M, and the chunks are summed in a fixed order, so a batch
+// row's result does not depend on the rest of the batch.
+int split_k_chunks(int64_t N, int64_t K) {
+  if (N <= 256) return (int)std::max<int64_t>(1, std::min<int64_t>(4, K / 256));
+  return (int)std::max<int64_t>(1, std::min<int64_t>(3, K / 2048));
+}
+
+// Appends p's K chunks (multiples of 64, at most G) to g: chunk 0 writes p's
+// output through p's row map, chunk j >= 1 writes fp32 partial j - 1 at
+// part + (j - 1) M N ([M, N], identity rows). Returns the number of chunks.
+int add_split_problems(dit::GemmBatch& g, const dit::GemmProblem& p, int G, float* part) {
+  const int64_t kc = round_up((p.K + G - 1) / G, 64);
+  int n = 0;
+  for (int64_t k0 = 0; k0 < p.K; k0 += kc, ++n) {
+    dit::GemmProblem q = p;
+    q.A = p.A + k0;
+    q.W = p.W + k0;
+    q.K = (int)std::min<int64_t>(kc, p.K - k0);
+    if (n > 0) {
+      q.C = part + (size_t)(n - 1) * p.M * p.N;
+      q.ldc = p.N;
+      q.seg_len = std::max(p.M, 1);
+      q.seg_stride = 0;
+      q.seg_off = 0;
+    }
+    g.p[g.count++] = q;
+  }
+  return n;
+}
+
+int run_split_sum(const dit::SplitSumArgs& a, hipStream_t st) {
+  const double bytes = (double)a.rows * a.cols * 4.0 * (2.0 + a.np);
+  DIT_TRY(timed(DIT_K_SPLIT_SUM, (double)a.rows * a.cols * a.np, bytes, st,
+                [&] { return dit::split_sum_launch(a, st); }));
+  return DIT_OK;
+}
+
+// Runs batch g in which p (an EPI_F32 problem) is split into K chunks when
+// split_k_chunks allows it, its partials fit in part_bytes at part, and g
+// has room; otherwise p runs whole. p goes last into g.
+int run_gemm_split_f32(dit::GemmBatch& g, const dit::GemmProblem& p, float* part,
+                       size_t part_bytes, hipStream_t st) {
+  int G = std::min(split_k_chunks(p.N, p.K), dit::kMaxGemmProblems - g.count);
+  const int64_t kc = round_up((p.K + G - 1) / std::max(G, 1), 64);
+  G = (int)((p.K + kc - 1) / kc);
+  if (G < 2 || (size_t)(G - 1) * p.M * p.N * 4 > part_bytes || p.epi != dit::EPI_F32 ||
+      (p.N & 3) || (p.ldc & 3)) {
+    g.p[g.count++] = p;
+    return run_gemm(g, st);
+  }
+  const int n = add_split_problems(g, p, G, part);
+  DIT_CHECK(run_gemm(g, st));
+  dit::SplitSumArgs ss{};
+  ss.c = static_cast<float*>(p.C);
+  for (int j = 0; j + 1 < n; ++j) ss.p[j] = part + (size_t)j * p.M * p.N;
+  ss.ldc = p.ldc;
+  ss.ldp = p.N;
+  ss.seg_stride = p.seg_stride;
+  ss.rows = p.M;
+  ss.cols = p.N;
+  ss.np = n - 1;
+  ss.seg_len = p.seg_len;
+  ss.seg_off = p.seg_off;
+  return run_split_sum(ss, st);
+}
+
 int run_norm(const dit::NormArgs& na, hipStream_t st) {
   double rows = 0;
   for (int i = 0; i < na.nseg; ++i) rows += (double)na.B * na.seg[i].seg_len;
@@ -796,21 +865,28 @@ int dit_step_forward(const dit_config* cfg, const dit_model_weights* w, const vo
   // 1. global modulation, once for the whole step
   DIT_CHECK(launch_modulation(c, *w, sigma_host, B, mod, at(ws, L.modws), st));
 
-  // 2. embeddings straight into the residual rows
+  // K-split partials of the embedding and the final projection live in the
+  // single block's d6 region, free before the first block and after the last
+  const BlockLayout SL = block_layout(c, 1, B, S);
+  float* part = reinterpret_cast<float*>(at(bws, SL.d6));
+  const size_t part_bytes = (size_t)SL.R * (size_t)(D + c.mlp_hidden) * 2;
+
+  // 2. embeddings straight into the residual rows (the text part K-split)
   {
     dit::GemmBatch g{};
-    if (n_txt > 0) {
-      dit::GemmProblem p = problem(txt, c.txt_channels, w->ctx_embed, c.txt_channels,
-                                   (int)(B * n_txt), (int)D, c.txt_channels, dit::EPI_F32, x, D);
-      set_rows(p, (int)n_txt, S, 0);
-      g.p[g.count++] = p;
-    }
     dit::GemmProblem p = problem(latents, c.in_channels, w->x_embed, c.in_channels,
                                  (int)(B * (n_img + n_ref)), (int)D, c.in_channels, dit::EPI_F32,
                                  x, D);
     set_rows(p, (int)(n_img + n_ref), S, (int)n_txt);
     g.p[g.count++] = p;
-    DIT_CHECK(run_gemm(g, st));
+    if (n_txt > 0) {
+      dit::GemmProblem t = problem(txt, c.txt_channels, w->ctx_embed, c.txt_channels,
+                                   (int)(B * n_txt), (int)D, c.txt_channels, dit::EPI_F32, x, D);
+      set_rows(t, (int)n_txt, S, 0);
+      DIT_CHECK(run_gemm_split_f32(g, t, part, part_bytes, st));
+    } else {
+      DIT_CHECK(run_gemm(g, st));
+    }
   }
 
   // 3. blocks, all reading the one modulation buffer
@@ -842,10 +918,9 @@ int dit_step_forward(const dit_config* cfg, const dit_model_weights* w, const vo
     na.seg[0].seg_len = (int)n_img;
     DIT_CHECK(run_norm(na, st));
     dit::GemmBatch g{};
-    g.count = 1;
-    g.p[0] = problem(h, D, w->proj_out, D, (int)(B * n_img), c.in_channels, (int)D,
-                     dit::EPI_F32, v_out, c.in_channels);
-    DIT_CHECK(run_gemm(g, st));
+    const dit::GemmProblem p = problem(h, D, w->proj_out, D, (int)(B * n_img), c.in_channels,
+                                       (int)D, dit::EPI_F32, v_out, c.in_channels);
+    DIT_CHECK(run_gemm_split_f32(g, p, part, part_bytes, st));
   }
   return DIT_OK;
 }

@@ -106,6 +106,19 @@ struct QkvPadArgs {
 };
 hipError_t qkv_pad_launch(const QkvPadArgs& a, hipStream_t stream);
 
+// ------------------------------------------------------------------ split-K sum
+// c[row(r), n] += p[0][r, n], then += p[1][r, n], ... (np partials in that
+// order), row(r) = (r / seg_len) * seg_stride + seg_off + r % seg_len: the
+// end of a GEMM whose K range ran as np + 1 chunk problems of one launch,
+// chunk 0 writing c and chunk k + 1 writing p[k] [rows, ldp]. cols % 4 == 0.
+struct SplitSumArgs {
+  float* c;
+  const float* p[3];
+  int64_t ldc, ldp, seg_stride;
+  int32_t rows, cols, np, seg_len, seg_off;
+};
+hipError_t split_sum_launch(const SplitSumArgs& a, hipStream_t stream);
+
 // ------------------------------------------------------------------ attention
 // O = softmax(q k^T / sqrt(128)) v for every (b, h), no mask, over S keys.
 // q (pre-scaled by log2(e) / sqrt(128)), k [B, H, S_pad, 128], vt [B, H, 128,

@@ -1,5 +1,6 @@
 // Bandwidth-bound kernels of the step on gfx950:
 //   * modnorm: AdaLN pre-norm of the fp32 residual into a bf16 GEMM operand
+//   * split_sum: the fixed-order sum of a K-split GEMM's partial results
 //   * qkv_pad: zeros of the padded attention operand rows (QK-RMSNorm and
 //     RoPE themselves run in the QKV GEMM's epilogue)
 //   * rope_tables: cos/sin of every pair angle from integer positions
@@ -85,6 +86,22 @@ __global__ __launch_bounds__(256) void qkv_pad_kernel(const QkvPadArgs a) {
   for (int64_t i = threadIdx.x; i < pad * 128; i += blockDim.x) vt[(i / pad) * a.S_pad + i % pad] = 0;
 }
 
+// ------------------------------------------------------------------ split-K sum
+// One thread per 4 columns of a row: c += p[0] + ... in a fixed order.
+__global__ __launch_bounds__(256) void split_sum_kernel(const SplitSumArgs a) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int c4 = a.cols >> 2;
+  if (i >= (int64_t)a.rows * c4) return;
+  const int r = (int)(i / c4), q = (int)(i - (int64_t)r * c4);
+  const int b = r / a.seg_len;
+  const int64_t row = (int64_t)b * a.seg_stride + a.seg_off + (r - b * a.seg_len);
+  f32x4* c = reinterpret_cast<f32x4*>(a.c + row * a.ldc) + q;
+  f32x4 v = *c;
+  for (int k = 0; k < a.np; ++k)
+    v += *(reinterpret_cast<const f32x4*>(a.p[k] + (int64_t)r * a.ldp) + q);
+  *c = v;
+}
+
 // ------------------------------------------------------------------ rope tables
 // cos/sin[s, j] of pos[s, axis(j)] * omega[j], angle and cos/sin in double.
 __global__ __launch_bounds__(256) void rope_tables_kernel(const RopeArgs a) {
@@ -118,18 +135,19 @@ __global__ __launch_bounds__(256) void time_features_kernel(const TimeArgs a) {
 // ------------------------------------------------------------------ gemv
 // y[b, out_off + n] = act_out(sum_k W[n, k] act_in(x[b, k])) for B <= 4
 // batch rows per launch. Workgroup = 4 waves, one weight row per wave per
-// iteration; the B input rows are staged in LDS (fp32, after act_in) and the
-// weight row is streamed once with 16-byte loads: the kernel reads each
-// weight byte exactly once.
+// iteration; the B input rows are staged in LDS (fp32, after act_in; B * K
+// floats of dynamic LDS, so a small batch leaves room for more workgroups
+// per CU and more weight loads in flight) and the weight row is streamed
+// once with 16-byte loads: the kernel reads each weight byte exactly once.
 constexpr int kGemvMaxB = 4;
 constexpr int kGemvMaxK = 4096;
 __global__ __launch_bounds__(256) void gemv_kernel(const GemvArgs a) {
-  __shared__ float xs[kGemvMaxB][kGemvMaxK];
+  extern __shared__ float xs_dyn[];  // [B][K]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int i = tid; i < a.B * a.K; i += 256) {
     const int b = i / a.K, k = i - b * a.K;
     float v = a.x[(int64_t)b * a.K + k];
-    xs[b][k] = a.act_in == ACT_SILU ? silu_f(v) : v;
+    xs_dyn[i] = a.act_in == ACT_SILU ? silu_f(v) : v;
   }
   __syncthreads();
   const int K8 = a.K >> 3;
@@ -142,18 +160,27 @@ __global__ __launch_bounds__(256) void gemv_kernel(const GemvArgs a) {
     const int n = row - sg.row_begin;
     const u32x4* w = reinterpret_cast<const u32x4*>(sg.W + (int64_t)n * a.K);
     float acc[kGemvMaxB] = {0.f, 0.f, 0.f, 0.f};
-    for (int c = lane; c < K8; c += 64) {
-      const u32x4 raw = w[c];
+    // all of the lane's chunks of the row (K <= 4096: at most 8) in flight at once
+    u32x4 raw[kGemvMaxK / 512];
+#pragma unroll
+    for (int t = 0; t < kGemvMaxK / 512; ++t) {
+      const int c = lane + 64 * t;
+      if (c < K8) raw[t] = w[c];
+    }
+#pragma unroll
+    for (int t = 0; t < kGemvMaxK / 512; ++t) {
+      const int c = lane + 64 * t;
+      if (c >= K8) break;
       float wv[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        wv[2 * e] = bf16_to_f32(raw[e] & 0xFFFFu);
-        wv[2 * e + 1] = bf16_to_f32(raw[e] >> 16);
+        wv[2 * e] = bf16_to_f32(raw[t][e] & 0xFFFFu);
+        wv[2 * e + 1] = bf16_to_f32(raw[t][e] >> 16);
       }
 #pragma unroll
       for (int b = 0; b < kGemvMaxB; ++b) {
         if (b < a.B) {
-          const float* xb = &xs[b][c * 8];
+          const float* xb = &xs_dyn[b * a.K + c * 8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) acc[b] += wv[e] * xb[e];
         }
@@ -197,6 +224,14 @@ hipError_t qkv_pad_launch(const QkvPadArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+hipError_t split_sum_launch(const SplitSumArgs& a, hipStream_t stream) {
+  if (a.np < 1 || a.np > 3 || (a.cols & 3) || a.seg_len < 1) return hipErrorInvalidValue;
+  const int64_t n = (int64_t)a.rows * (a.cols >> 2);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(split_sum_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
 hipError_t rope_tables_launch(const RopeArgs& a, hipStream_t stream) {
   const int64_t n = a.S * a.pairs;
   if (n == 0) return hipSuccess;
@@ -213,7 +248,8 @@ hipError_t time_features_launch(const TimeArgs& a, hipStream_t stream) {
 hipError_t gemv_launch(const GemvArgs& a, hipStream_t stream) {
   if (a.B > kGemvMaxB || a.K > kGemvMaxK || (a.K & 7)) return hipErrorInvalidValue;
   const int blocks = min(2048, (a.total_rows + 3) / 4);
-  hipLaunchKernelGGL(gemv_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  const size_t lds = (size_t)a.B * a.K * sizeof(float);
+  hipLaunchKernelGGL(gemv_kernel, dim3((unsigned)blocks), dim3(256), lds, stream, a);
   return hipGetLastError();
 }
 

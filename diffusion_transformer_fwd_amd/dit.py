@@ -26,8 +26,10 @@ EXPORTS = ("dit_position_ids", "dit_workspace_bytes", "dit_status_string", "dit_
            "dit_config_check", "dit_rope_tables_build", "dit_modulation_forward",
            "dit_dual_block_forward", "dit_single_block_forward", "dit_step_forward",
            "dit_profile_begin", "dit_profile_end")
-K_GEMM, K_ATTENTION, K_MODNORM, K_QKV_PAD, K_GEMV, K_ROPE_TABLES, K_TIME, K_COUNT = range(8)
-KERNEL_NAMES = ("gemm", "attention", "modnorm", "qkv_pad", "gemv", "rope_tables", "time_features")
+K_GEMM, K_ATTENTION, K_MODNORM, K_QKV_PAD, K_GEMV, K_ROPE_TABLES, K_TIME, K_SPLIT_SUM, K_COUNT = \
+    range(9)
+KERNEL_NAMES = ("gemm", "attention", "modnorm", "qkv_pad", "gemv", "rope_tables", "time_features",
+                "split_sum")
 
 
 class DitError(RuntimeError):

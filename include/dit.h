@@ -236,7 +236,8 @@ int dit_step_forward(const dit_config* cfg, const dit_model_weights* w,
 
 /* Kernel families, for dit_kernel_stats.kind. */
 enum { DIT_K_GEMM = 0, DIT_K_ATTENTION = 1, DIT_K_MODNORM = 2, DIT_K_QKV_PAD = 3,
-       DIT_K_GEMV = 4, DIT_K_ROPE_TABLES = 5, DIT_K_TIME = 6, DIT_K_COUNT = 7 };
+       DIT_K_GEMV = 4, DIT_K_ROPE_TABLES = 5, DIT_K_TIME = 6, DIT_K_SPLIT_SUM = 7,
+       DIT_K_COUNT = 8 };
 
 typedef struct dit_kernel_stats {
   int32_t kind;     /* DIT_K_* */

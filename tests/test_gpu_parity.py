@@ -256,6 +256,31 @@ def test_step_small(case):
     assert_close(to_np(v), want, what=f"step {name}")
 
 
+def test_step_split_k_parity_and_batch_invariance():
+    """The text embedding (K = 4096 here: 2 chunks) and the final projection
+    (N = 128, K = 1024: 4 chunks) run K-split, the chunks summed in a fixed
+    order: the step matches the oracle, and each batch row equals its solo
+    run bit for bit (the split depends on N and K, never on the batch)."""
+    cfg = small_cfg(hidden=1024, heads=8, mlp_hidden=3072, txt_channels=4096)
+    mw = synth.ModelWeights(cfg, 0, cache=True)
+    dw = dit.ModelWeights(mw)
+    wl = synth.Workload("s", 2, 48, (8, 8), (), 0.6)
+    pos = dit.position_ids(wl.n_txt, wl.img_grid, wl.ref_grids)
+    cos_d, sin_d = dit.rope_tables(cfg, pos)
+    v, ins = run_step(cfg, dw, wl, cos_d, sin_d)
+    both = to_np(v)
+    want = O.step(cfg, mw, np.stack([i["txt"] for i in ins]), np.stack([i["latents"] for i in ins]),
+                  np.full(wl.batch, wl.sigma), wl.n_img,
+                  O.position_ids(wl.n_txt, wl.img_grid, wl.ref_grids))
+    assert_close(both, want, what="step with K-split embedding and projection")
+    for b in range(wl.batch):
+        txt = dit.to_bf16_device(ins[b]["txt"][None])
+        lat = dit.to_bf16_device(ins[b]["latents"][None])
+        v1 = dit.step(cfg, dw, txt, lat, [wl.sigma], wl.n_img, cos_d, sin_d)
+        torch.cuda.synchronize()
+        assert np.array_equal(to_np(v1)[0], both[b]), f"row {b}"
+
+
 @pytest.fixture(scope="module")
 def klein():
     log("drawing and uploading FLUX.2-klein-size weights ...")
