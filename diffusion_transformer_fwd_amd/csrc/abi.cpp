@@ -382,6 +382,7 @@ int run_split_sum(const dit::SplitSumArgs& a, hipStream_t st) {
 // has room; otherwise p runs whole. p goes last into g.
 int run_gemm_split_f32(dit::GemmBatch& g, const dit::GemmProblem& p, float* part,
                        size_t part_bytes, hipStream_t st) {
+  if (g.count >= dit::kMaxGemmProblems) return fail(DIT_E_SHAPE, "GEMM batch full");
   int G = std::min(split_k_chunks(p.N, p.K), dit::kMaxGemmProblems - g.count);
   const int64_t kc = round_up((p.K + G - 1) / std::max(G, 1), 64);
   G = (int)((p.K + kc - 1) / kc);

@@ -83,14 +83,14 @@ struct count_t {
   static constexpr int value = V;
 };
 
-// EPI_QKV for one wave tile (64 rows x 128 columns = one head of q, k or v):
-// a row's 128 accumulators sit in lanes l and l ^ 32 (64 each), so the RMS
-// is lane-local plus one cross-half exchange; each lane's runs of 4 columns
-// hold two whole rotation pairs.
 // BNT: output columns per tile, 256 or 224 (BF16 / F32 / RESID epilogues
 // only). At 224 the N = 1 waves run three 32-column blocks instead of four
 // and W tile rows 224..255 are never loaded; per output element nothing
 // changes (same MFMA, same k order), so the width may be picked per launch.
+// EPI_QKV for one wave tile (64 rows x 128 columns = one head of q, k or v):
+// a row's 128 accumulators sit in lanes l and l ^ 32 (64 each), so the RMS
+// is lane-local plus one cross-half exchange; each lane's runs of 4 columns
+// hold two whole rotation pairs.
 template <int BNT>
 __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const GemmBatch args) {
   // two K-slice stages, then (EPI_QKV) 1 / rms of each tile row per wave column
