@@ -69,6 +69,66 @@ __global__ __launch_bounds__(256) void modnorm_kernel(const NormArgs a) {
   }
 }
 
+// One workgroup (4 waves) per output row, VPT float4 per thread (D <= 1024
+// VPT): the row's x, shift and scale loads are all issued before the first
+// reduction, and the sums go through LDS. Same arithmetic as modnorm_kernel,
+// with the reductions in another order.
+template <int VPT>
+__global__ __launch_bounds__(256) void modnorm_row_kernel(const NormArgs a) {
+  __shared__ float part[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t row = blockIdx.x;
+  const int si = (a.nseg > 1 && row >= a.seg[1].out_base) ? 1 : 0;
+  const NormSegment& sg = si ? a.seg[1] : a.seg[0];
+  const int64_t r = row - sg.out_base;
+  if (r < 0 || r >= (int64_t)a.B * sg.seg_len) return;  // uniform per workgroup
+  const int b = (int)(r / sg.seg_len);
+  const int64_t xrow = (int64_t)b * a.S + sg.seg_off + (r - (int64_t)b * sg.seg_len);
+  const int D = a.D, D4 = D >> 2;
+  const f32x4* xr = reinterpret_cast<const f32x4*>(a.x + xrow * D);
+  const f32x4* sh = reinterpret_cast<const f32x4*>(sg.shift + (int64_t)b * a.mod_bstride);
+  const f32x4* sc = reinterpret_cast<const f32x4*>(sg.scale + (int64_t)b * a.mod_bstride);
+  f32x4 v[VPT], vs[VPT], vh[VPT];
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const int c = i * 256 + tid;
+    const bool ok = c < D4;
+    v[i] = ok ? xr[c] : f32x4{0.f, 0.f, 0.f, 0.f};
+    vh[i] = ok ? sh[c] : f32x4{0.f, 0.f, 0.f, 0.f};
+    vs[i] = ok ? sc[c] : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  auto block_sum = [&](float t) {
+    t = wave_sum(t);
+    if (lane == 0) part[wave] = t;
+    __syncthreads();
+    const float total = (part[0] + part[1]) + (part[2] + part[3]);
+    __syncthreads();  // part is reused by the next sum
+    return total;
+  };
+  float mean = 0.f;
+  if (a.kind == 1) {
+    float s1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) s1 += v[i][0] + v[i][1] + v[i][2] + v[i][3];
+    mean = block_sum(s1) / D;
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    if (i * 256 + tid < D4) {
+      const f32x4 d = v[i] - mean;
+      ss += d[0] * d[0] + d[1] * d[1] + d[2] * d[2] + d[3] * d[3];
+    }
+  }
+  const float rstd = rsqrtf(block_sum(ss) / D + a.eps);
+  u32x2* out = reinterpret_cast<u32x2*>(a.h + row * D);
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const int c = i * 256 + tid;
+    if (c < D4) out[c] = pack_bf16x4((v[i] - mean) * rstd * (1.f + vs[i]) + vh[i]);
+  }
+}
+
 // ------------------------------------------------------------------ qkv padding
 // Grid (B * H), 256 threads: zero q, k rows [S, S_pad) (128 bf16 each) and
 // v^T columns [S, S_pad) of its 128 rows, with 2-byte stores (the pad is at
@@ -206,6 +266,14 @@ hipError_t modnorm_launch(const NormArgs& a, hipStream_t stream) {
   for (int i = 0; i < a.nseg; ++i)
     rows = max(rows, a.seg[i].out_base + (int64_t)a.B * a.seg[i].seg_len);
   if (rows == 0) return hipSuccess;
+  const int vpt = (a.D / 4 + 255) / 256;
+  if (vpt >= 2 && vpt <= 4) {  // wide rows: one workgroup per row
+    const dim3 rgrid((unsigned)rows);
+    if (vpt == 2) hipLaunchKernelGGL(modnorm_row_kernel<2>, rgrid, dim3(256), 0, stream, a);
+    else if (vpt == 3) hipLaunchKernelGGL(modnorm_row_kernel<3>, rgrid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL(modnorm_row_kernel<4>, rgrid, dim3(256), 0, stream, a);
+    return hipGetLastError();
+  }
   const dim3 grid((unsigned)((rows + 3) / 4));
   const int vpl = (a.D / 4 + 63) / 64;
   if (vpl <= 1) hipLaunchKernelGGL(modnorm_kernel<1>, grid, dim3(256), 0, stream, a);
