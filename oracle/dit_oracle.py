@@ -142,8 +142,8 @@ def linear(x: np.ndarray, w: np.ndarray) -> np.ndarray:
 def prenorm(x: np.ndarray, kind: int = PRENORM_RMS, eps: float = 1e-6) -> np.ndarray:
     """Affine-free pre-norm over the last axis.
 
-    RMS (default, the north star's "AdaLN-modulated RMSNorm"):
-    x / sqrt(mean(x^2) + eps). LAYER: (x - mean) / sqrt(var + eps).
+    RMS (the default reading; the pages name no norm kind for the AdaLN
+    pre-norm): x / sqrt(mean(x^2) + eps). LAYER: (x - mean) / sqrt(var + eps).
     """
     if kind == PRENORM_LAYER:
         mu = x.mean(axis=-1, keepdims=True)
@@ -206,8 +206,8 @@ def _merge(x: np.ndarray) -> np.ndarray:
 def _qkv_attention(qkv: np.ndarray, heads: int, q_gain, k_gain, cos, sin, eps):
     """Split [B, S, 3D] into q/k/v heads, QK-RMSNorm then RoPE, attend.
 
-    Reading: q/k norms come before the rotation (the benchmark spec's
-    "QK-RMSNorm"; RoPE acts on the normalized vectors).
+    Reading: the q/k RMS norms come before the rotation (RoPE acts on the
+    normalized vectors).
     Returns the attention output merged back to [B, S, D].
     """
     D = qkv.shape[-1] // 3
