@@ -97,7 +97,7 @@ __global__ __launch_bounds__(NT, 1) void attention_kernel(const AttnArgs a) {
   char* const lb = reinterpret_cast<char*>(lds);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const bool loader = wave < 4;  // waves 0-3 lead and load; 4-7 lag half an iteration
+  const bool leader = wave < 4;  // waves 0-3 lead; 4-7 lag half an iteration
   // XCD-contiguous work order: consecutive query blocks of one (b, h) run on
   // the same XCD, so that head's K and V^T stay in that XCD's L2.
   const int n_qb = (int)((a.S + QB - 1) / QB);
@@ -118,10 +118,11 @@ __global__ __launch_bounds__(NT, 1) void attention_kernel(const AttnArgs a) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // K / V^T tiles go straight from memory into LDS (buffer loads that write
-  // LDS at M0 + 16 * lane). Loader wave w fills K rows 16 w .. 16 w + 15
-  // (four instructions of 4 rows x 16 chunks) and V^T rows 32 w .. 32 w + 31
-  // (four of 8 rows x 8 chunks); each lane fetches the logical chunk whose
-  // swizzled position is its own.
+  // LDS at M0 + 16 * lane). With lw = wave % 4, a tile's K rows 16 lw ..
+  // 16 lw + 15 (four instructions of 4 rows x 16 chunks) come from wave lw + 4
+  // and its V^T rows 32 lw .. 32 lw + 31 (four of 8 rows x 8 chunks) from
+  // wave lw, except tiles 0 and 1, which waves 0-3 fetch whole; each lane
+  // fetches the logical chunk whose swizzled position is its own.
   const __amdgpu_buffer_rsrc_t k_rsrc =
       make_rsrc(a.k + bh * a.S_pad * 128, clamp_u32(a.S_pad * 128 * 2));
   const __amdgpu_buffer_rsrc_t v_rsrc =
@@ -185,8 +186,9 @@ __global__ __launch_bounds__(NT, 1) void attention_kernel(const AttnArgs a) {
 
   // Matrix phase of iteration t: S^T - m of tile t (2 + 16 MFMAs into sacc)
   // and O^T += V^T P^T of tile t - 1 (16 MFMAs into o), alternating, with
-  // the fragments read from LDS PF operations ahead; a loader wave issues
-  // its eight loads of tile t + 2 along the way. Every iteration runs both
+  // the fragments read from LDS PF operations ahead; no loads are issued
+  // here (a load instruction can hold its wave back, and this phase sets the
+  // pace of the workgroup). Every iteration runs both
   // products (one code path keeps the register allocation tight): at t = 0
   // the PV product reads a zeroed V^T stage with P = 0, and the scores
   // computed at t = n_tiles are never used.
@@ -194,7 +196,6 @@ __global__ __launch_bounds__(NT, 1) void attention_kernel(const AttnArgs a) {
     constexpr int STG = decltype(stage)::value;
     constexpr int PSTG = (STG + NSTAGE - 1) % NSTAGE;
     constexpr int N = 32, PF = 4;
-    const bool load = loader && t + 2 < n_tiles;
     // op i: even -> score block (ks, kb) = (i / 4, (i / 2) % 2);
     //        odd  -> PV block (s, db) = (i / 8, (i / 2) % 4)
     auto frag = [&](int i) -> u32x4 {
@@ -219,7 +220,6 @@ __global__ __launch_bounds__(NT, 1) void attention_kernel(const AttnArgs a) {
         sacc[j & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, qf[j >> 1], sacc[j & 1], 0, 0, 0);
       else
         o[j & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, pf[j >> 2], o[j & 3], 0, 0, 0);
-      if ((i & 3) == 1 && load) dma_part(t + 2, stage_t<(STG + 2) % NSTAGE>{}, i >> 2);
       __builtin_amdgcn_sched_barrier(0);  // keep the read-ahead distance
     }
   };
@@ -271,7 +271,7 @@ __global__ __launch_bounds__(NT, 1) void attention_kernel(const AttnArgs a) {
       m = m_new;
       qaug[0] = (__bf16)(g == 0 ? -m : 0.f);
     }
-    // materialise the results here, ahead of the loader's wait that follows
+    // materialise the results here, ahead of the load wait that follows
 #pragma unroll
     for (int s = 0; s < 4; ++s) asm volatile("" : "+v"(pf[s]));
     asm volatile("" : "+v"(l));
@@ -283,19 +283,36 @@ __global__ __launch_bounds__(NT, 1) void attention_kernel(const AttnArgs a) {
     matrix_phase(t, stage);
     wg_barrier();
     if (t < n_tiles) {
-      softmax_phase(t);
-      // the leading waves' loads of tile t + 1 have landed
-      if (loader) {
-        __builtin_amdgcn_sched_barrier(0);
-        if (t + 2 < n_tiles) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      // The softmax phase has slack against the other half's matrix phase,
+      // so it carries the tile loads. Waves 0-3 request the V^T rows of tile
+      // t + 2 (stage (t + 2) % 4: its last V^T reads, the PV of tile t - 2,
+      // ended two phases ago), waves 4-7 the K rows of tile t + 3 (stage
+      // (t + 3) % 4: its last K reads, the scores of tile t - 1, ended in the
+      // previous phase).
+      constexpr int STG = decltype(stage)::value;
+      if (leader) {
+        if (t + 2 < n_tiles) {
+#pragma unroll
+          for (int j = 4; j < 8; ++j) dma_part(t + 2, stage_t<(STG + 2) % NSTAGE>{}, j);
+        }
+      } else if (t + 3 < n_tiles) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dma_part(t + 3, stage_t<(STG + 3) % NSTAGE>{}, j);
       }
+      softmax_phase(t);
+      // this wave's older loads have landed (the four just issued may fly):
+      // V^T of tile t + 1 (waves 0-3, needed from phase 2t + 4 on) or K of
+      // tile t + 2 (waves 4-7, needed from phase 2t + 4 on); the barrier
+      // below publishes them
+      __builtin_amdgcn_sched_barrier(0);
+      if (t + (leader ? 2 : 3) < n_tiles) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
     wg_barrier();
     return t == n_tiles;
   };
 
-  if (loader) {
+  if (leader) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) dma_part(0, stage_t<0>{}, j);
     if (n_tiles > 1) {
@@ -307,14 +324,21 @@ __global__ __launch_bounds__(NT, 1) void attention_kernel(const AttnArgs a) {
     }
   }
   __syncthreads();  // tiles 0 (and 1) requested, tile 0 landed, zero stage written
-  if (!loader) wg_barrier();  // lag by one phase
+  if (!leader) {
+    // K rows of tile 2 (their first reader is phase 4), then lag by one phase
+    if (n_tiles > 2) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dma_part(2, stage_t<2>{}, j);
+    }
+    wg_barrier();
+  }
   for (int t = 0;; t += NSTAGE) {
     if (iteration(t, stage_t<0>{})) break;
     if (iteration(t + 1, stage_t<1>{})) break;
     if (iteration(t + 2, stage_t<2>{})) break;
     if (iteration(t + 3, stage_t<3>{})) break;
   }
-  if (loader) wg_barrier();  // match the lagging waves' barrier count
+  if (leader) wg_barrier();  // match the lagging waves' barrier count
 
   // normalise and store: lane holds query q0 + qi, dims db*32 + 8 j + 4 g + 0..3
   l = half_sum(l);
