@@ -102,6 +102,20 @@ def summarize(d):
             for c in sorted({c for x in lst for c in x}):
                 vals = [x[c] for x in lst if c in x]
                 out.append(f"| {k} | {len(vals)} | {c} | {sum(vals) / len(vals):.6g} |")
+        mfma = [(k, lst) for k, lst in sorted(by_kernel.items())
+                if any("SQ_INSTS_VALU_MFMA_MOPS_BF16" in x for x in lst)]
+        if mfma:
+            # MOPS count 512 flops each; MFMA busy cycles are per SIMD (1024 on
+            # the chip) and GRBM_GUI_ACTIVE is summed over the 8 XCDs here
+            out.append("| kernel | dispatches | counted GFLOP per dispatch | MFMA busy % | "
+                       "GUI-active cycles per dispatch |\n|---|---|---|---|---|")
+            for k, lst in mfma:
+                n = len(lst)
+                fl = sum(x.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) for x in lst) * 512 / n
+                gui = sum(x.get("GRBM_GUI_ACTIVE", 0.0) for x in lst) / n / 8
+                busy = sum(x.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) for x in lst) / n
+                pct = 100.0 * busy / (gui * 1024) if gui else float("nan")
+                out.append(f"| {k} | {n} | {fl / 1e9:.2f} | {pct:.1f} | {gui:.0f} |")
         gemm = [x for k, lst in by_kernel.items() if "gemm_bf16_kernel" in k for x in lst]
         for c in ("FETCH_SIZE", "WRITE_SIZE"):
             vals = [x[c] for x in gemm if c in x]
@@ -145,6 +159,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--profile-steps", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--denoise-reps", type=int, default=3,
+                    help="timed runs of the 4-step sampling loop, eager and graph-replayed")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="end with three device copies of COPY_CAL_BYTES (counter calibration)")
     ap.add_argument("--summarize", metavar="DIR",
@@ -206,6 +222,53 @@ def main():
     log(f"{K} steps: {ms:.3f} ms/step (wall), events median {np.median(per):.3f} "
         f"p95 {np.percentile(per, 95):.3f}")
     assert np.all(np.isfinite(out.cpu().numpy())), "non-finite output"
+
+    # the 4-step sampling loop on the device (Euler between steps), eager and
+    # captured once as a HIP graph and replayed
+    den = None
+    if args.denoise_reps > 0:
+        sched = np.array([[1.0, 0.75, 0.5, 0.25, 0.0]], np.float32)
+        z0 = dit.to_f32_device(ins["latents"][None, :wl.n_img])
+        z = z0.clone()
+        dws = dit.Workspace()
+        dws.get(dit.workspace_bytes(cfg, dit.WS_DENOISE, 1, wl.seq))
+
+        def loop():
+            dit.denoise(cfg, dw, txt, z, None, sched, cos, sin, ws=dws)
+
+        loop()
+        torch.cuda.synchronize()
+        t_e = []
+        for _ in range(args.denoise_reps):
+            z.copy_(z0)
+            torch.cuda.synchronize()
+            t1 = time.perf_counter()
+            loop()
+            torch.cuda.synchronize()
+            t_e.append(time.perf_counter() - t1)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            loop()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            loop()
+        t_g = []
+        for _ in range(args.denoise_reps):
+            z.copy_(z0)
+            torch.cuda.synchronize()
+            t1 = time.perf_counter()
+            graph.replay()
+            torch.cuda.synchronize()
+            t_g.append(time.perf_counter() - t1)
+        assert np.all(np.isfinite(z.cpu().numpy())), "non-finite latent"
+        del graph
+        den = {"steps": 4, "schedule": sched[0].tolist(),
+               "eager_ms": round(1000.0 * float(np.median(t_e)), 3),
+               "graph_ms": round(1000.0 * float(np.median(t_g)), 3)}
+        log(f"4-step loop: eager {den['eager_ms']} ms, graph {den['graph_ms']} ms")
 
     # per-kernel pass (event pair around every launch)
     P = max(1, args.profile_steps)
@@ -280,6 +343,7 @@ def main():
                      "alg_bytes_per_launch": round(g["bytes"] / g["launches"]),
                      "per_launch_flop": gemm_per_launch, "avg_launch_us": gemm_avg_s * 1e6},
         "kernels": kern,
+        "denoise_loop": den,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

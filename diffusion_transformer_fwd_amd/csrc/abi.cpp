@@ -167,6 +167,28 @@ StepLayout step_layout(const dit_config& c, int64_t B, int64_t S) {
   return L;
 }
 
+// The sampling loop: the step's workspace, then its latent operand
+// lat bf16 [B, S, C] and velocity v fp32 [B, S, C] (sized for S rows, so the
+// workspace query needs no split of S into image and reference tokens).
+struct DenoiseLayout {
+  size_t step = 0, lat = 0, v = 0, total = 0;
+};
+
+DenoiseLayout denoise_layout(const dit_config& c, int64_t B, int64_t S) {
+  DenoiseLayout L;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  L.step = take(step_layout(c, B, S).total);
+  L.lat = take((size_t)B * S * c.in_channels * 2);
+  L.v = take((size_t)B * S * c.in_channels * 4);
+  L.total = off;
+  return L;
+}
+
 // ---------------------------------------------------------------- validation
 
 int check_config(const dit_config* c) {
@@ -690,6 +712,103 @@ int check_block_common(const dit_config* cfg, float* x, int32_t B, int64_t S,
   return DIT_OK;
 }
 
+// The step after validation: enqueues modulation, embeddings, blocks and
+// the final layer on st, using the step workspace at ws.
+int launch_step(const dit_config& c, const dit_model_weights& wr, const void* txt,
+                const void* latents, const float* sigma_host, int32_t B, int64_t n_txt,
+                int64_t n_img, int64_t n_ref, const float* cos_dev, const float* sin_dev,
+                float* v_out, void* ws, hipStream_t st) {
+  const dit_model_weights* w = &wr;
+  const int64_t S = n_txt + n_img + n_ref;
+  const StepLayout L = step_layout(c, B, S);
+  const int64_t D = c.hidden;
+  float* x = reinterpret_cast<float*>(at(ws, L.x));
+  float* mod = reinterpret_cast<float*>(at(ws, L.mod));
+  void* bws = at(ws, L.block);
+  const int64_t mbs = DIT_MOD_ROWS * D;
+
+  // 1. global modulation, once for the whole step
+  DIT_CHECK(launch_modulation(c, *w, sigma_host, B, mod, at(ws, L.modws), st));
+
+  // K-split partials of the embedding and the final projection live in the
+  // single block's d6 region, free before the first block and after the last
+  const BlockLayout SL = block_layout(c, 1, B, S);
+  float* part = reinterpret_cast<float*>(at(bws, SL.d6));
+  const size_t part_bytes = (size_t)SL.R * (size_t)(D + c.mlp_hidden) * 2;
+
+  // 2. embeddings straight into the residual rows (the text part K-split)
+  {
+    dit::GemmBatch g{};
+    dit::GemmProblem p = problem(latents, c.in_channels, w->x_embed, c.in_channels,
+                                 (int)(B * (n_img + n_ref)), (int)D, c.in_channels, dit::EPI_F32,
+                                 x, D);
+    set_rows(p, (int)(n_img + n_ref), S, (int)n_txt);
+    g.p[g.count++] = p;
+    if (n_txt > 0) {
+      dit::GemmProblem t = problem(txt, c.txt_channels, w->ctx_embed, c.txt_channels,
+                                   (int)(B * n_txt), (int)D, c.txt_channels, dit::EPI_F32, x, D);
+      set_rows(t, (int)n_txt, S, 0);
+      DIT_CHECK(run_gemm_split_f32(g, t, part, part_bytes, st));
+    } else {
+      DIT_CHECK(run_gemm(g, st));
+    }
+  }
+
+  // 3. blocks, all reading the one modulation buffer
+  for (int i = 0; i < c.n_dual; ++i)
+    DIT_CHECK(launch_dual(c, w->dual[i], x, B, S, n_txt, mod + DIT_MOD_DUAL_TXT * D,
+                          mod + DIT_MOD_DUAL_IMG * D, mbs, cos_dev, sin_dev, bws, st));
+  for (int i = 0; i < c.n_single; ++i)
+    DIT_CHECK(launch_single(c, w->single[i], x, B, S, mod + DIT_MOD_SINGLE * D, mbs, cos_dev,
+                            sin_dev, bws, st));
+
+  // 4. final AdaLN of the image rows + projection to the latent width
+  {
+    const BlockLayout BL = block_layout(c, 1, B, S);
+    bf16_t* h = bf(at(bws, BL.h));
+    dit::NormArgs na{};
+    na.x = x;
+    na.h = h;
+    na.S = S;
+    na.mod_bstride = mbs;
+    na.D = (int)D;
+    na.B = B;
+    na.kind = c.prenorm;
+    na.eps = c.eps;
+    na.nseg = 1;
+    na.seg[0].shift = mod + DIT_MOD_FINAL * D;
+    na.seg[0].scale = mod + (DIT_MOD_FINAL + 1) * D;
+    na.seg[0].out_base = 0;
+    na.seg[0].seg_off = (int)n_txt;
+    na.seg[0].seg_len = (int)n_img;
+    DIT_CHECK(run_norm(na, st));
+    dit::GemmBatch g{};
+    const dit::GemmProblem p = problem(h, D, w->proj_out, D, (int)(B * n_img), c.in_channels,
+                                       (int)D, dit::EPI_F32, v_out, c.in_channels);
+    DIT_CHECK(run_gemm_split_f32(g, p, part, part_bytes, st));
+  }
+  return DIT_OK;
+}
+
+// Checks shared by the step and the sampling loop (everything but the
+// latent, sigma, output and workspace arguments).
+int check_step_args(const dit_config* cfg, const dit_model_weights* w, const void* txt,
+                    int32_t B, int64_t n_txt, int64_t n_img, int64_t n_ref,
+                    const float* cos_dev, const float* sin_dev) {
+  DIT_CHECK(check_config(cfg));
+  if (n_txt < 0 || n_img < 1 || n_ref < 0)
+    return fail(DIT_E_SHAPE, "token counts n_txt %lld, n_img %lld, n_ref %lld invalid",
+                (long long)n_txt, (long long)n_img, (long long)n_ref);
+  const int64_t S = n_txt + n_img + n_ref;
+  DIT_CHECK(check_batch_seq(B, S));
+  DIT_CHECK(check_operand_sizes(*cfg, (int64_t)B * S));
+  DIT_CHECK(check_model_weights(*cfg, w, true));
+  if (n_txt > 0) DIT_CHECK(check_ptr(txt, "txt"));
+  DIT_CHECK(check_ptr(cos_dev, "cos"));
+  DIT_CHECK(check_ptr(sin_dev, "sin"));
+  return DIT_OK;
+}
+
 }  // namespace
 
 // ======================================================================= ABI
@@ -760,6 +879,7 @@ size_t dit_workspace_bytes(const dit_config* cfg, int32_t kind, int32_t B, int64
     case DIT_WS_DUAL: return block_layout(*cfg, 0, B, S).total;
     case DIT_WS_SINGLE: return block_layout(*cfg, 1, B, S).total;
     case DIT_WS_STEP: return step_layout(*cfg, B, S).total;
+    case DIT_WS_DENOISE: return denoise_layout(*cfg, B, S).total;
     default: fail(DIT_E_VALUE, "unknown workspace kind %d", kind); return 0;
   }
 }
@@ -838,90 +958,59 @@ int dit_step_forward(const dit_config* cfg, const dit_model_weights* w, const vo
                      const void* latents, const float* sigma_host, int32_t B, int64_t n_txt,
                      int64_t n_img, int64_t n_ref, const float* cos_dev, const float* sin_dev,
                      float* v_out, void* ws, size_t ws_bytes, dit_stream_t stream) {
-  DIT_CHECK(check_config(cfg));
-  if (n_txt < 0 || n_img < 1 || n_ref < 0)
-    return fail(DIT_E_SHAPE, "token counts n_txt %lld, n_img %lld, n_ref %lld invalid",
-                (long long)n_txt, (long long)n_img, (long long)n_ref);
-  const int64_t S = n_txt + n_img + n_ref;
-  DIT_CHECK(check_batch_seq(B, S));
-  DIT_CHECK(check_operand_sizes(*cfg, (int64_t)B * S));
-  DIT_CHECK(check_model_weights(*cfg, w, true));
-  if (n_txt > 0) DIT_CHECK(check_ptr(txt, "txt"));
+  DIT_CHECK(check_step_args(cfg, w, txt, B, n_txt, n_img, n_ref, cos_dev, sin_dev));
   DIT_CHECK(check_ptr(latents, "latents"));
   DIT_CHECK(check_sigmas(sigma_host, B));
-  DIT_CHECK(check_ptr(cos_dev, "cos"));
-  DIT_CHECK(check_ptr(sin_dev, "sin"));
   DIT_CHECK(check_ptr(v_out, "v_out"));
-  const StepLayout L = step_layout(*cfg, B, S);
+  DIT_CHECK(check_ws(ws, ws_bytes, step_layout(*cfg, B, n_txt + n_img + n_ref).total));
+  return launch_step(*cfg, *w, txt, latents, sigma_host, B, n_txt, n_img, n_ref, cos_dev,
+                     sin_dev, v_out, ws, reinterpret_cast<hipStream_t>(stream));
+}
+
+int dit_denoise_forward(const dit_config* cfg, const dit_model_weights* w, const void* txt,
+                        float* z, const void* ref, const float* sigmas_host, int32_t n_steps,
+                        int32_t B, int64_t n_txt, int64_t n_img, int64_t n_ref,
+                        const float* cos_dev, const float* sin_dev, void* ws, size_t ws_bytes,
+                        dit_stream_t stream) {
+  DIT_CHECK(check_step_args(cfg, w, txt, B, n_txt, n_img, n_ref, cos_dev, sin_dev));
+  if (n_steps < 1 || n_steps > DIT_MAX_STEPS)
+    return fail(DIT_E_SHAPE, "n_steps %d out of range [1, %d]", n_steps, (int)DIT_MAX_STEPS);
+  if (cfg->in_channels % 4)
+    return fail(DIT_E_UNSUPPORTED, "in_channels %d is not a multiple of 4", cfg->in_channels);
+  DIT_CHECK(check_ptr(z, "z"));
+  if (n_ref > 0) DIT_CHECK(check_ptr(ref, "ref", 8));
+  if (!sigmas_host) return fail(DIT_E_NULL, "sigmas is NULL");
+  for (int64_t i = 0; i < (int64_t)B * (n_steps + 1); ++i)
+    if (!std::isfinite(sigmas_host[i]))
+      return fail(DIT_E_VALUE, "sigmas[%lld] is not finite", (long long)i);
+  const int64_t S = n_txt + n_img + n_ref;
+  const DenoiseLayout L = denoise_layout(*cfg, B, S);
   DIT_CHECK(check_ws(ws, ws_bytes, L.total));
 
   const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const dit_config& c = *cfg;
-  const int64_t D = c.hidden;
-  float* x = reinterpret_cast<float*>(at(ws, L.x));
-  float* mod = reinterpret_cast<float*>(at(ws, L.mod));
-  void* bws = at(ws, L.block);
-  const int64_t mbs = DIT_MOD_ROWS * D;
-
-  // 1. global modulation, once for the whole step
-  DIT_CHECK(launch_modulation(c, *w, sigma_host, B, mod, at(ws, L.modws), st));
-
-  // K-split partials of the embedding and the final projection live in the
-  // single block's d6 region, free before the first block and after the last
-  const BlockLayout SL = block_layout(c, 1, B, S);
-  float* part = reinterpret_cast<float*>(at(bws, SL.d6));
-  const size_t part_bytes = (size_t)SL.R * (size_t)(D + c.mlp_hidden) * 2;
-
-  // 2. embeddings straight into the residual rows (the text part K-split)
-  {
-    dit::GemmBatch g{};
-    dit::GemmProblem p = problem(latents, c.in_channels, w->x_embed, c.in_channels,
-                                 (int)(B * (n_img + n_ref)), (int)D, c.in_channels, dit::EPI_F32,
-                                 x, D);
-    set_rows(p, (int)(n_img + n_ref), S, (int)n_txt);
-    g.p[g.count++] = p;
-    if (n_txt > 0) {
-      dit::GemmProblem t = problem(txt, c.txt_channels, w->ctx_embed, c.txt_channels,
-                                   (int)(B * n_txt), (int)D, c.txt_channels, dit::EPI_F32, x, D);
-      set_rows(t, (int)n_txt, S, 0);
-      DIT_CHECK(run_gemm_split_f32(g, t, part, part_bytes, st));
-    } else {
-      DIT_CHECK(run_gemm(g, st));
+  const int64_t C = cfg->in_channels;
+  float* v = reinterpret_cast<float*>(at(ws, L.v));
+  dit::LatentArgs la{};
+  la.z = z;
+  la.v = v;
+  la.ref = static_cast<const bf16_t*>(ref);
+  la.lat = bf(at(ws, L.lat));
+  la.n_img = n_img;
+  la.n_ref = n_ref;
+  la.B = B;
+  la.C = (int32_t)C;
+  DIT_TRY(timed(DIT_K_LATENT, 0.0, (double)B * (n_img * C * 6.0 + n_ref * C * 4.0), st,
+                [&] { return dit::latent_pack_launch(la, st); }));
+  std::vector<float> sig(B);
+  for (int i = 0; i < n_steps; ++i) {
+    for (int b = 0; b < B; ++b) {
+      sig[b] = sigmas_host[(int64_t)b * (n_steps + 1) + i];
+      la.dsig[b] = sigmas_host[(int64_t)b * (n_steps + 1) + i + 1] - sig[b];
     }
-  }
-
-  // 3. blocks, all reading the one modulation buffer
-  for (int i = 0; i < c.n_dual; ++i)
-    DIT_CHECK(launch_dual(c, w->dual[i], x, B, S, n_txt, mod + DIT_MOD_DUAL_TXT * D,
-                          mod + DIT_MOD_DUAL_IMG * D, mbs, cos_dev, sin_dev, bws, st));
-  for (int i = 0; i < c.n_single; ++i)
-    DIT_CHECK(launch_single(c, w->single[i], x, B, S, mod + DIT_MOD_SINGLE * D, mbs, cos_dev,
-                            sin_dev, bws, st));
-
-  // 4. final AdaLN of the image rows + projection to the latent width
-  {
-    const BlockLayout BL = block_layout(c, 1, B, S);
-    bf16_t* h = bf(at(bws, BL.h));
-    dit::NormArgs na{};
-    na.x = x;
-    na.h = h;
-    na.S = S;
-    na.mod_bstride = mbs;
-    na.D = (int)D;
-    na.B = B;
-    na.kind = c.prenorm;
-    na.eps = c.eps;
-    na.nseg = 1;
-    na.seg[0].shift = mod + DIT_MOD_FINAL * D;
-    na.seg[0].scale = mod + (DIT_MOD_FINAL + 1) * D;
-    na.seg[0].out_base = 0;
-    na.seg[0].seg_off = (int)n_txt;
-    na.seg[0].seg_len = (int)n_img;
-    DIT_CHECK(run_norm(na, st));
-    dit::GemmBatch g{};
-    const dit::GemmProblem p = problem(h, D, w->proj_out, D, (int)(B * n_img), c.in_channels,
-                                       (int)D, dit::EPI_F32, v_out, c.in_channels);
-    DIT_CHECK(run_gemm_split_f32(g, p, part, part_bytes, st));
+    DIT_CHECK(launch_step(*cfg, *w, txt, la.lat, sig.data(), B, n_txt, n_img, n_ref, cos_dev,
+                          sin_dev, v, at(ws, L.step), st));
+    DIT_TRY(timed(DIT_K_LATENT, 0.0, (double)B * n_img * C * 14.0, st,
+                  [&] { return dit::euler_launch(la, st); }));
   }
   return DIT_OK;
 }

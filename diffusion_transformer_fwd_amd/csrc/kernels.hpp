@@ -174,4 +174,23 @@ struct GemvArgs {
 };
 hipError_t gemv_launch(const GemvArgs& a, hipStream_t stream);
 
+// ------------------------------------------------------------------ sampler loop
+// Latent state of the on-device sampling loop: z fp32 [B, n_img, C] (image
+// tokens), the step's bf16 operand lat [B, n_img + n_ref, C] (image rows, then
+// the reference rows copied from ref [B, n_ref, C]), and the step's velocity
+// v fp32 [B, n_img, C]. C % 4 == 0.
+//   latent_pack: lat[b, r] = bf16(z[b, r]) for r < n_img, ref rows copied.
+//   euler:       z[b, r] += dsig[b] * v[b, r]; lat[b, r] = bf16(z[b, r]).
+struct LatentArgs {
+  float* z;
+  const float* v;
+  const bf16_t* ref;
+  bf16_t* lat;
+  int64_t n_img, n_ref;
+  int32_t B, C;
+  float dsig[64];
+};
+hipError_t latent_pack_launch(const LatentArgs& a, hipStream_t stream);
+hipError_t euler_launch(const LatentArgs& a, hipStream_t stream);
+
 }  // namespace dit

@@ -5,6 +5,8 @@
 //     RoPE themselves run in the QKV GEMM's epilogue)
 //   * rope_tables: cos/sin of every pair angle from integer positions
 //   * time_features + gemv: the global modulation vectors from sigma
+//   * latent_pack + euler: the latent state of the sampling loop between
+//     steps (flow-matching Euler update, bf16 operand of the next step)
 //
 // The maths each one follows is stated at its kernel; the pages it comes
 // from are "flux2-klein-p100a" (Caveats: modulation global per step) and
@@ -259,6 +261,44 @@ __global__ __launch_bounds__(256) void gemv_kernel(const GemvArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ sampler loop
+// One thread per 4 channels of a latent row; 16-byte fp32 loads and 8-byte
+// bf16 stores, rows of a batch sample contiguous.
+__global__ __launch_bounds__(256) void latent_pack_kernel(const LatentArgs a) {
+  const int c4 = a.C >> 2;
+  const int64_t rows = a.n_img + a.n_ref;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)a.B * rows * c4) return;
+  const int64_t br = i / c4;
+  const int q = (int)(i - br * c4);
+  const int64_t b = br / rows, r = br - b * rows;
+  u32x2* out = reinterpret_cast<u32x2*>(a.lat + br * a.C) + q;
+  if (r < a.n_img) {
+    *out = pack_bf16x4(*(reinterpret_cast<const f32x4*>(a.z + (b * a.n_img + r) * a.C) + q));
+  } else {
+    *out = *(reinterpret_cast<const u32x2*>(a.ref + (b * a.n_ref + (r - a.n_img)) * a.C) + q);
+  }
+}
+
+// z += dsig[b] * v (one fp32 fma per element), and the bf16 copy of the new
+// z into the image rows of the next step's operand.
+__global__ __launch_bounds__(256) void euler_kernel(const LatentArgs a) {
+  const int c4 = a.C >> 2;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)a.B * a.n_img * c4) return;
+  const int64_t br = i / c4;
+  const int q = (int)(i - br * c4);
+  const int64_t b = br / a.n_img, r = br - b * a.n_img;
+  f32x4* zp = reinterpret_cast<f32x4*>(a.z + br * a.C) + q;
+  const f32x4 v = *(reinterpret_cast<const f32x4*>(a.v + br * a.C) + q);
+  const float d = a.dsig[b];
+  f32x4 z = *zp;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) z[e] = fmaf(d, v[e], z[e]);
+  *zp = z;
+  *(reinterpret_cast<u32x2*>(a.lat + (b * (a.n_img + a.n_ref) + r) * a.C) + q) = pack_bf16x4(z);
+}
+
 }  // namespace
 
 hipError_t modnorm_launch(const NormArgs& a, hipStream_t stream) {
@@ -318,6 +358,23 @@ hipError_t gemv_launch(const GemvArgs& a, hipStream_t stream) {
   const int blocks = min(2048, (a.total_rows + 3) / 4);
   const size_t lds = (size_t)a.B * a.K * sizeof(float);
   hipLaunchKernelGGL(gemv_kernel, dim3((unsigned)blocks), dim3(256), lds, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t latent_pack_launch(const LatentArgs& a, hipStream_t stream) {
+  if ((a.C & 3) || a.B < 0 || a.B > 64) return hipErrorInvalidValue;
+  const int64_t n = (int64_t)a.B * (a.n_img + a.n_ref) * (a.C >> 2);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(latent_pack_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+
+hipError_t euler_launch(const LatentArgs& a, hipStream_t stream) {
+  if ((a.C & 3) || a.B < 0 || a.B > 64) return hipErrorInvalidValue;
+  const int64_t n = (int64_t)a.B * a.n_img * (a.C >> 2);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(euler_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -19,17 +19,18 @@ _lib: Optional[C.CDLL] = None
 
 DIT_OK, DIT_E_NULL, DIT_E_SHAPE, DIT_E_UNSUPPORTED, DIT_E_WORKSPACE, DIT_E_HIP, DIT_E_VALUE = (
     0, -1, -2, -3, -4, -5, -6)
-WS_DUAL, WS_SINGLE, WS_STEP, WS_MOD = 0, 1, 2, 3
+WS_DUAL, WS_SINGLE, WS_STEP, WS_MOD, WS_DENOISE = 0, 1, 2, 3, 4
 MOD_DUAL_IMG, MOD_DUAL_TXT, MOD_SINGLE, MOD_FINAL, MOD_ROWS = 0, 6, 12, 15, 17
 MAX_BATCH = 64
 EXPORTS = ("dit_position_ids", "dit_workspace_bytes", "dit_status_string", "dit_last_error",
            "dit_config_check", "dit_rope_tables_build", "dit_modulation_forward",
            "dit_dual_block_forward", "dit_single_block_forward", "dit_step_forward",
-           "dit_profile_begin", "dit_profile_end")
-K_GEMM, K_ATTENTION, K_MODNORM, K_QKV_PAD, K_GEMV, K_ROPE_TABLES, K_TIME, K_SPLIT_SUM, K_COUNT = \
-    range(9)
+           "dit_denoise_forward", "dit_profile_begin", "dit_profile_end")
+(K_GEMM, K_ATTENTION, K_MODNORM, K_QKV_PAD, K_GEMV, K_ROPE_TABLES, K_TIME, K_SPLIT_SUM, K_LATENT,
+ K_COUNT) = range(10)
 KERNEL_NAMES = ("gemm", "attention", "modnorm", "qkv_pad", "gemv", "rope_tables", "time_features",
-                "split_sum")
+                "split_sum", "latent")
+MAX_STEPS = 64
 
 
 class DitError(RuntimeError):
@@ -108,6 +109,9 @@ def lib() -> C.CDLL:
     L.dit_step_forward.restype = C.c_int
     L.dit_step_forward.argtypes = [pc, C.POINTER(ModelWeightsC), vp, vp, vp, i32, i64, i64, i64,
                                    vp, vp, vp, vp, sz, vp]
+    L.dit_denoise_forward.restype = C.c_int
+    L.dit_denoise_forward.argtypes = [pc, C.POINTER(ModelWeightsC), vp, vp, vp, vp, i32, i32, i64,
+                                      i64, i64, vp, vp, vp, sz, vp]
     L.dit_profile_begin.restype = C.c_int
     L.dit_profile_begin.argtypes = []
     L.dit_profile_end.restype = C.c_int
@@ -336,3 +340,25 @@ def step(cfg: synth.DitConfig, w: ModelWeights, txt, latents, sigma: Sequence[fl
         C.byref(c), C.byref(w.c), txt.data_ptr(), latents.data_ptr(), sig.ctypes.data, B, n_txt,
         n_img, n_ref, cos.data_ptr(), sin.data_ptr(), out.data_ptr(), p, n, _stream()))
     return out
+
+
+def denoise(cfg: synth.DitConfig, w: ModelWeights, txt, z, ref, sigmas, cos, sin,
+            ws: Optional[Workspace] = None):
+    """The sampling loop, in place on z (fp32 [B, n_img, C_in]).
+
+    txt bf16 [B, n_txt, C_txt]; ref bf16 [B, n_ref, C_in] or None; sigmas
+    [B, n_steps + 1] (host values). Returns z."""
+    B, n_img = z.shape[0], z.shape[1]
+    n_txt = txt.shape[1]
+    n_ref = 0 if ref is None else ref.shape[1]
+    sig = np.ascontiguousarray(np.broadcast_to(np.asarray(sigmas, dtype=np.float32),
+                                               (B, np.shape(sigmas)[-1])))
+    n_steps = sig.shape[1] - 1
+    S = n_txt + n_img + n_ref
+    ws = ws or Workspace()
+    p, n = ws.get(workspace_bytes(cfg, WS_DENOISE, B, S))
+    c = config(cfg)
+    _check(lib().dit_denoise_forward(
+        C.byref(c), C.byref(w.c), txt.data_ptr(), z.data_ptr(), _ptr(ref), sig.ctypes.data,
+        n_steps, B, n_txt, n_img, n_ref, cos.data_ptr(), sin.data_ptr(), p, n, _stream()))
+    return z

@@ -241,6 +241,13 @@ W_SINGLE_1024 = Workload("single_block_1024px_s4608", 1, 512, (64, 64), (), 0.75
 W_STEP_1024 = Workload("step_1024px_s4608", 1, 512, (64, 64), (), 0.75)
 W_STEP_1024_REF = Workload("step_1024px_1ref_s8704", 1, 512, (64, 64), ((64, 64),), 0.75)
 W_STEP_1920x1088_B4 = Workload("step_1920x1088_b4_s8672", 4, 512, (68, 120), (), 0.75)
+# non-square output (848x624 -> 39 x 53 patches, no tile-aligned size) with
+# three references at their own aspect (1024x1024, 1184x880, 512x768 px)
+W_STEP_848x624_3REF = Workload("step_848x624_3ref_s12281", 1, 512, (39, 53),
+                               ((64, 64), (55, 74), (48, 32)), 0.75)
+# the longest sequence: 1920x1088 output with three 1024x1024 references
+W_SINGLE_MAX = Workload("single_block_1920x1088_3ref_s20960", 1, 512, (68, 120),
+                        ((64, 64), (64, 64), (64, 64)), 0.75)
 
 
 def step_inputs(cfg: DitConfig, wl: Workload, batch_row: int = 0,

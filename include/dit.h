@@ -121,10 +121,14 @@ enum { DIT_MOD_DUAL_IMG = 0, DIT_MOD_DUAL_TXT = 6, DIT_MOD_SINGLE = 12,
        DIT_MOD_FINAL = 15, DIT_MOD_ROWS = 17 };
 
 /* Workspace kinds for dit_workspace_bytes. */
-enum { DIT_WS_DUAL = 0, DIT_WS_SINGLE = 1, DIT_WS_STEP = 2, DIT_WS_MOD = 3 };
+enum { DIT_WS_DUAL = 0, DIT_WS_SINGLE = 1, DIT_WS_STEP = 2, DIT_WS_MOD = 3,
+       DIT_WS_DENOISE = 4 };
 
 /* Largest batch a call accepts (sigma values travel as kernel arguments). */
 enum { DIT_MAX_BATCH = 64 };
+
+/* Largest number of steps of one dit_denoise_forward call. */
+enum { DIT_MAX_STEPS = 64 };
 
 /* ------------------------------------------------------------------ host */
 
@@ -144,7 +148,8 @@ int64_t dit_position_ids(int64_t n_txt, int32_t hp, int32_t wp, int32_t n_ref,
 /* Bytes of device workspace a call needs (0 on invalid arguments, with
  * dit_last_error set). kind: DIT_WS_DUAL / DIT_WS_SINGLE for one block call
  * on B samples of S tokens, DIT_WS_STEP for dit_step_forward (S = n_txt +
- * n_img + n_ref), DIT_WS_MOD for dit_modulation_forward. */
+ * n_img + n_ref), DIT_WS_MOD for dit_modulation_forward, DIT_WS_DENOISE
+ * for dit_denoise_forward (S = n_txt + n_img + n_ref). */
 size_t dit_workspace_bytes(const dit_config* cfg, int32_t kind, int32_t B, int64_t S);
 
 const char* dit_status_string(int status);
@@ -232,12 +237,37 @@ int dit_step_forward(const dit_config* cfg, const dit_model_weights* w,
                      const float* cos_dev, const float* sin_dev, float* v_out,
                      void* ws, size_t ws_bytes, dit_stream_t stream);
 
+/* The sampling loop on the device: n_steps denoise steps with the flow-
+ * matching Euler update between them ("flux2-klein-p100a", Tasks table:
+ * 4 steps, one DiT call each, no CFG; the card's header puts the scheduler
+ * on the host, so the sigma schedule is an input here). For i < n_steps and
+ * every batch row b:
+ *   v = dit_step(txt, [bf16(z) ; ref], sigma[b][i]);
+ *   z += (sigma[b][i + 1] - sigma[b][i]) * v        (fp32, one fma).
+ *   z: dev fp32 [B, n_img, in_channels], in place: the starting latent (the
+ *      noise) in, the latent after the last update out;
+ *   ref: dev bf16 [B, n_ref, in_channels] reference tokens (never updated;
+ *      NULL when n_ref = 0);
+ *   sigmas_host: host fp32 [B, n_steps + 1], finite; 1 <= n_steps <=
+ *      DIT_MAX_STEPS;
+ *   txt, cos/sin, B, n_txt, n_img, n_ref: as for dit_step_forward.
+ * The step's latent operand is bf16(z) (the GEMM rounds its operands).
+ * The sigmas travel as kernel arguments, so the enqueued work for one shape
+ * and schedule can be captured once in a HIP graph and replayed.
+ * ws: dit_workspace_bytes(cfg, DIT_WS_DENOISE, B, S) bytes, 256-byte aligned. */
+int dit_denoise_forward(const dit_config* cfg, const dit_model_weights* w,
+                        const void* txt, float* z, const void* ref,
+                        const float* sigmas_host, int32_t n_steps, int32_t B,
+                        int64_t n_txt, int64_t n_img, int64_t n_ref,
+                        const float* cos_dev, const float* sin_dev, void* ws,
+                        size_t ws_bytes, dit_stream_t stream);
+
 /* ------------------------------------------------------------- profiling */
 
 /* Kernel families, for dit_kernel_stats.kind. */
 enum { DIT_K_GEMM = 0, DIT_K_ATTENTION = 1, DIT_K_MODNORM = 2, DIT_K_QKV_PAD = 3,
        DIT_K_GEMV = 4, DIT_K_ROPE_TABLES = 5, DIT_K_TIME = 6, DIT_K_SPLIT_SUM = 7,
-       DIT_K_COUNT = 8 };
+       DIT_K_LATENT = 8, DIT_K_COUNT = 9 };
 
 typedef struct dit_kernel_stats {
   int32_t kind;     /* DIT_K_* */

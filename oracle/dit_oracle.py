@@ -329,6 +329,35 @@ def single_block(x: np.ndarray, w: Dict[str, np.ndarray], mod: np.ndarray,
     return x + mod[:, None, 2] * y
 
 
+def single_block_rows(x: np.ndarray, w: Dict[str, np.ndarray], mod: np.ndarray,
+                      cos: np.ndarray, sin: np.ndarray, heads: int, rows: np.ndarray,
+                      eps: float = 1e-6, prenorm_kind: int = PRENORM_RMS,
+                      dtype=np.float64) -> np.ndarray:
+    """single_block's output at the token rows `rows` only, [B, len(rows), D].
+
+    The same definition restricted to the queries asked for: keys and values
+    come from every row (attention sees the whole sequence), while q, the
+    SwiGLU branch and the output projection are formed for the listed rows.
+    This is what lets a long sequence be checked row by row.
+    """
+    x = np.asarray(x, dtype=dtype)
+    mod = np.asarray(mod, dtype)
+    rows = np.asarray(rows)
+    D = x.shape[-1]
+    w_in = w["w_in"].astype(dtype)
+    h = modulate(x, mod[:, None, 0], mod[:, None, 1], prenorm_kind, eps)
+    kv = linear(h, w_in[D:3 * D])
+    u = linear(h[:, rows], w_in)
+    q = apply_rope(qk_rmsnorm(_heads(u[..., :D], heads), w["q_gain"].astype(dtype), eps),
+                   cos[rows], sin[rows])
+    k = apply_rope(qk_rmsnorm(_heads(kv[..., :D], heads), w["k_gain"].astype(dtype), eps),
+                   cos, sin)
+    o = _merge(attention(q, k, _heads(kv[..., D:], heads)))
+    a = swiglu(u[..., 3 * D:])
+    y = linear(np.concatenate([o, a], axis=-1), w["w_out"].astype(dtype))
+    return x[:, rows] + mod[:, None, 2] * y
+
+
 # ------------------------------------------------------------ step
 
 def embed(gw: Dict[str, np.ndarray], txt: np.ndarray, lat: np.ndarray,
@@ -397,3 +426,35 @@ def euler(z: np.ndarray, v: np.ndarray, sigma: float, sigma_next: float) -> np.n
     [card] header: the scheduler stays on the host.
     """
     return z + (sigma_next - sigma) * v
+
+
+def denoise(velocity: Callable[[np.ndarray, np.ndarray], np.ndarray], z: np.ndarray,
+            sigmas: np.ndarray) -> np.ndarray:
+    """The sampling loop: for i = 0 .. n-1, v = velocity(z, sigma[:, i]) and
+    z <- euler(z, v, sigma[:, i], sigma[:, i + 1]), per batch row.
+
+    [card] Tasks table: 4 steps, one DiT call each (no CFG); header: the
+    scheduler runs on the host, so the schedule sigmas [B, n + 1] is given.
+    z [B, ...]; returns the latent after the last update.
+    """
+    sigmas = np.asarray(sigmas, dtype=np.float64)
+    z = np.array(z, dtype=np.float64)
+    for i in range(sigmas.shape[1] - 1):
+        v = velocity(z, sigmas[:, i])
+        shape = (-1,) + (1,) * (z.ndim - 1)
+        z = euler(z, v, sigmas[:, i].reshape(shape), sigmas[:, i + 1].reshape(shape))
+    return z
+
+
+def denoise_dit(cfg, weights, txt: np.ndarray, z: np.ndarray, ref: Optional[np.ndarray],
+                sigmas: np.ndarray, pos: np.ndarray, dtype=np.float64) -> np.ndarray:
+    """The sampling loop with the DiT step as the velocity: each step sees the
+    image latents z [B, n_img, C_in] followed by the fixed reference tokens
+    ref [B, n_ref, C_in] (or None)."""
+    n_img = z.shape[1]
+
+    def velocity(zc, sig):
+        lat = zc if ref is None else np.concatenate([zc, ref], axis=1)
+        return step(cfg, weights, txt, lat, sig, n_img, pos, dtype)
+
+    return denoise(velocity, z, sigmas)

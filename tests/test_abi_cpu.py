@@ -32,7 +32,7 @@ def header_functions():
 
 def test_exports_every_declared_function(L):
     names = header_functions()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     assert sorted(dit.EXPORTS) == names
     for n in names:
         assert hasattr(L, n), f"{n} not exported"
@@ -118,7 +118,7 @@ def test_position_ids_errors(L):
 
 def test_workspace_bytes(L):
     cfg = synth.FLUX2_KLEIN
-    for kind in (dit.WS_DUAL, dit.WS_SINGLE, dit.WS_STEP):
+    for kind in (dit.WS_DUAL, dit.WS_SINGLE, dit.WS_STEP, dit.WS_DENOISE):
         a = dit.workspace_bytes(cfg, kind, 1, 4608)
         b = dit.workspace_bytes(cfg, kind, 1, 8704)
         c = dit.workspace_bytes(cfg, kind, 4, 8672)
@@ -128,6 +128,8 @@ def test_workspace_bytes(L):
     step = dit.workspace_bytes(cfg, dit.WS_STEP, 1, 4608)
     assert step >= 4608 * 3072 * 4 + 17 * 3072 * 4 + dit.workspace_bytes(cfg, dit.WS_SINGLE, 1, 4608)
     assert dit.workspace_bytes(cfg, dit.WS_MOD, 4, 0) > 0
+    # the sampling loop adds its bf16 latent operand and fp32 velocity to a step's
+    assert dit.workspace_bytes(cfg, dit.WS_DENOISE, 1, 4608) >= step + 4608 * 128 * 6
     c = dit.config(cfg)
     assert L.dit_workspace_bytes(C.byref(c), dit.WS_STEP, 0, 10) == 0
     assert L.dit_workspace_bytes(C.byref(c), dit.WS_STEP, 65, 10) == 0
@@ -188,6 +190,29 @@ def test_step_validation_errors(L):
     m.dual[3].mlp_out[1] = 0
     assert _step(L, cfg, m, [0.5]) == dit.DIT_E_NULL
     assert "mlp_out" in dit.last_error()
+
+
+def _denoise(L, cfg, m, sig, n_steps, B=1, n_txt=512, n_img=4096, n_ref=0, z=FAKE, ref=FAKE,
+             ws_bytes=1 << 40, in_channels=None):
+    c = dit.config(cfg)
+    sig = np.ascontiguousarray(sig, np.float32)
+    return L.dit_denoise_forward(C.byref(c), C.byref(m), FAKE, z, ref, sig.ctypes.data, n_steps,
+                                 B, n_txt, n_img, n_ref, FAKE, FAKE, FAKE, ws_bytes, None)
+
+
+def test_denoise_validation_errors(L):
+    cfg = synth.FLUX2_KLEIN
+    m, _d, _s = _fake_model(cfg)
+    sig = [1.0, 0.75, 0.5, 0.25, 0.0]
+    assert _denoise(L, cfg, m, sig, 0) == dit.DIT_E_SHAPE
+    assert _denoise(L, cfg, m, sig * 20, 65) == dit.DIT_E_SHAPE
+    assert _denoise(L, cfg, m, [1.0, float("inf"), 0.5, 0.25, 0.0], 4) == dit.DIT_E_VALUE
+    # the second batch row's schedule is read too
+    assert _denoise(L, cfg, m, sig + [1.0, 0.5, float("nan"), 0.2, 0.0], 4, B=2) == dit.DIT_E_VALUE
+    assert _denoise(L, cfg, m, sig, 4, z=0) == dit.DIT_E_NULL
+    assert _denoise(L, cfg, m, sig, 4, n_ref=4096, ref=0) == dit.DIT_E_NULL
+    assert _denoise(L, cfg, m, sig, 4, ws_bytes=1 << 20) == dit.DIT_E_WORKSPACE
+    assert _denoise(L, synth.DitConfig(in_channels=130), m, sig, 4) == dit.DIT_E_UNSUPPORTED
 
 
 def test_block_validation_errors(L):

@@ -188,6 +188,29 @@ def test_single_block_1024px():
     check_block(xs, got, want, "single 1024px")
 
 
+def test_single_block_longest_sequence_sampled_rows():
+    """One single-stream block at the longest sequence the pages allow:
+    1920x1088 output (8160 tokens) with three 1024x1024 references, S = 20960.
+    The oracle forms sampled query rows (text, every image/reference block
+    boundary region, the ragged end) against all keys."""
+    cfg = synth.FLUX2_KLEIN
+    wl = synth.W_SINGLE_MAX
+    pos, S, xs, mod_d, cos_d, sin_d, mod_o, cos_o, sin_o = setup_block(
+        cfg, wl.n_txt, wl.img_grid, wl.ref_grids, 1, [wl.sigma])
+    assert S == 20960
+    w = synth.single_weights(cfg, 0, 0)
+    x_d = torch.from_numpy(xs).cuda()
+    log(f"single block S={S}")
+    dit.single_block(cfg, dit.SingleWeights(w), x_d, mod_d, cos_d, sin_d)
+    rows = np.unique(np.concatenate([np.arange(0, S, 97), [511, 512, 8671, 8672, 12767, 12768,
+                                                          16863, 16864, 20735, S - 1]]))
+    got = to_np(x_d)[:, rows]
+    log(f"oracle: {rows.size} sampled rows against all {S} keys ...")
+    want = O.single_block_rows(xs, w, mod_o["single"], cos_o, sin_o, cfg.heads, rows, cfg.eps,
+                               cfg.prenorm)
+    check_block(xs[:, rows], got, want, f"single S={S} (sampled rows)")
+
+
 def test_zero_gate_leaves_residual_bitwise():
     cfg = small_cfg()
     pos, S, xs, mod_d, cos_d, sin_d, *_ = setup_block(cfg, 32, (8, 8), (), 2, [0.5, 0.6])
@@ -256,6 +279,75 @@ def test_step_small(case):
     assert_close(to_np(v), want, what=f"step {name}")
 
 
+# ---------------------------------------------------------------- sampling loop
+
+def _denoise_case():
+    cfg = small_cfg(n_dual=2, n_single=2)
+    mw = synth.ModelWeights(cfg, 0, cache=True)
+    wl = synth.Workload("s", 2, 32, (6, 10), ((4, 8),), 1.0)
+    ins = [synth.step_inputs(cfg, wl, batch_row=b) for b in range(wl.batch)]
+    txt = np.stack([i["txt"] for i in ins])
+    lat = np.stack([i["latents"] for i in ins])
+    # per-row schedules of 4 steps ending at 0, fp32 values on both sides
+    sig = np.array([[1.0, 0.75, 0.5, 0.25, 0.0], [0.9, 0.7, 0.45, 0.2, 0.0]], np.float32)
+    pos = O.position_ids(wl.n_txt, wl.img_grid, wl.ref_grids)
+    return cfg, mw, wl, txt, lat, sig, pos
+
+
+def test_denoise_small_against_oracle():
+    cfg, mw, wl, txt, lat, sig, pos = _denoise_case()
+    dw = dit.ModelWeights(mw)
+    cos_d, sin_d = dit.rope_tables(cfg, pos.astype(np.int32))
+    z0, ref = lat[:, :wl.n_img], lat[:, wl.n_img:]
+    z = dit.to_f32_device(z0)
+    log(f"denoise: B={wl.batch} S={wl.seq} steps={sig.shape[1] - 1}")
+    dit.denoise(cfg, dw, dit.to_bf16_device(txt), z, dit.to_bf16_device(ref), sig, cos_d, sin_d)
+    torch.cuda.synchronize()
+    want = O.denoise_dit(cfg, mw, txt, z0, ref, sig.astype(np.float64), pos)
+    assert_close(to_np(z), want, what="denoise 4 steps")
+    # each row followed its own schedule: the rows differ from a shared one
+    z2 = dit.to_f32_device(z0)
+    dit.denoise(cfg, dw, dit.to_bf16_device(txt), z2, dit.to_bf16_device(ref),
+                np.repeat(sig[:1], 2, axis=0), cos_d, sin_d)
+    assert torch.equal(z2[0], z[0]) and not torch.equal(z2[1], z[1])
+
+
+def test_denoise_graph_replays_match_eager():
+    """The loop captured once in a HIP graph (through torch.cuda.graph) and
+    replayed three times, with eager library work and synchronisations in
+    between: every replay equals the eager loop bit for bit."""
+    cfg, mw, wl, txt, lat, sig, pos = _denoise_case()
+    dw = dit.ModelWeights(mw)
+    cos_d, sin_d = dit.rope_tables(cfg, pos.astype(np.int32))
+    txt_d, ref_d = dit.to_bf16_device(txt), dit.to_bf16_device(lat[:, wl.n_img:])
+    z0 = dit.to_f32_device(lat[:, :wl.n_img])
+    z_e = z0.clone()
+    dit.denoise(cfg, dw, txt_d, z_e, ref_d, sig, cos_d, sin_d)
+    torch.cuda.synchronize()
+    ws = dit.Workspace()
+    ws.get(dit.workspace_bytes(cfg, dit.WS_DENOISE, wl.batch, wl.seq))
+    z_g = z0.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        dit.denoise(cfg, dw, txt_d, z_g, ref_d, sig, cos_d, sin_d, ws=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dit.denoise(cfg, dw, txt_d, z_g, ref_d, sig, cos_d, sin_d, ws=ws)
+    for rep in range(3):
+        z_g.copy_(z0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(z_g, z_e), f"replay {rep} differs from the eager loop"
+        # eager library work on the same weights between replays
+        z_x = z0.clone()
+        dit.denoise(cfg, dw, txt_d, z_x, ref_d, sig[:, ::-1].copy(), cos_d, sin_d)
+        torch.cuda.synchronize()
+
+
 def test_step_split_k_parity_and_batch_invariance():
     """The text embedding (K = 4096 here: 2 chunks) and the final projection
     (N = 128, K = 1024: 4 chunks) run K-split, the chunks summed in a fixed
@@ -289,7 +381,8 @@ def klein():
     return dw
 
 
-GOLDEN_CASES = [synth.W_STEP_1024, synth.W_STEP_1024_REF, synth.W_STEP_1920x1088_B4]
+GOLDEN_CASES = [synth.W_STEP_1024, synth.W_STEP_1024_REF, synth.W_STEP_1920x1088_B4,
+                synth.W_STEP_848x624_3REF]
 
 
 @pytest.mark.slow

@@ -419,6 +419,70 @@ def test_euler_update():
     assert np.array_equal(O.euler(z, v, 1.0, 0.75), np.array([0.875, -3.0]))
 
 
+def test_single_block_rows_equals_full_block():
+    """The row-restricted block (used where the whole block is too long for the
+    oracle) gives the full block's rows, including the first and last."""
+    cfg = synth.DitConfig(hidden=256, heads=2, head_dim=128, mlp_hidden=768)
+    pos = O.position_ids(16, (5, 7), ((3, 2),))
+    S = pos.shape[0]
+    x = np.stack([synth.residual(cfg, b, S) for b in range(2)])
+    w = synth.single_weights(cfg, 0, 0)
+    mod = O.modulation(synth.global_weights(cfg, 0), np.array([0.75, 0.3]))["single"]
+    cos, sin = O.rope_tables(pos)
+    full = O.single_block(x, w, mod, cos, sin, cfg.heads)
+    rows = np.array([0, 3, 15, 16, 40, S - 1])
+    got = O.single_block_rows(x, w, mod, cos, sin, cfg.heads, rows)
+    np.testing.assert_allclose(got, full[:, rows], rtol=0, atol=1e-12)
+
+
+def test_denoise_linear_field_closed_form():
+    """v = a z is a linear ODE; each Euler step multiplies z by
+    1 + a (sigma_{i+1} - sigma_i), so n steps give the product of those
+    factors (per batch row, with its own schedule)."""
+    rng = np.random.default_rng(3)
+    z0 = rng.standard_normal((2, 5, 4))
+    sig = np.array([[1.0, 0.75, 0.5, 0.25, 0.0], [0.9, 0.6, 0.35, 0.1, 0.0]])
+    a = -1.7
+    got = O.denoise(lambda z, s: a * z, z0, sig)
+    fac = np.prod(1.0 + a * np.diff(sig, axis=1), axis=1)
+    np.testing.assert_allclose(got, z0 * fac[:, None, None], rtol=1e-14, atol=0)
+
+
+def test_denoise_straight_path_is_exact():
+    """On the straight path z(sigma) = (1 - sigma) x0 + sigma n the velocity
+    n - x0 is constant, so Euler lands on x0 at sigma = 0 for any schedule
+    (the rectified-flow property the update is built on)."""
+    rng = np.random.default_rng(4)
+    x0, n = rng.standard_normal((2, 1, 3, 8))
+    sig = np.array([[1.0, 0.8, 0.3, 0.05, 0.0]])
+    seen = []
+
+    def vel(z, s):
+        seen.append(s.copy())
+        np.testing.assert_allclose(z, (1 - s[0]) * x0 + s[0] * n, atol=1e-12)
+        return n - x0
+
+    got = O.denoise(vel, (1 - sig[0, 0]) * x0 + sig[0, 0] * n, sig)
+    np.testing.assert_allclose(got, x0, atol=1e-12)
+    assert [float(x[0]) for x in seen] == [1.0, 0.8, 0.3, 0.05]
+
+
+def test_denoise_dit_keeps_references_fixed():
+    """The DiT loop passes the reference tokens unchanged to every step and
+    updates only the image latents: with one step it is one step plus Euler."""
+    cfg = synth.DitConfig(hidden=256, heads=2, head_dim=128, mlp_hidden=768, n_dual=1,
+                          n_single=1, in_channels=128, txt_channels=256)
+    mw = synth.ModelWeights(cfg, 0, cache=True)
+    wl = synth.Workload("s", 1, 8, (2, 3), ((2, 2),), 0.75)
+    ins = synth.step_inputs(cfg, wl)
+    pos = O.position_ids(wl.n_txt, wl.img_grid, wl.ref_grids)
+    z = ins["latents"][None, :wl.n_img]
+    ref = ins["latents"][None, wl.n_img:]
+    got = O.denoise_dit(cfg, mw, ins["txt"][None], z, ref, np.array([[0.75, 0.4]]), pos)
+    v = O.step(cfg, mw, ins["txt"][None], ins["latents"][None], np.array([0.75]), wl.n_img, pos)
+    np.testing.assert_allclose(got, z + (0.4 - 0.75) * v, rtol=0, atol=1e-12)
+
+
 # ---------------------------------------------------------------- planted mistakes
 
 def _mutants():
