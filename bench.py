@@ -128,8 +128,12 @@ def log(msg):
     print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
 
-def cpu_baseline(cfg, wl, seconds_hint=True):
-    """Time the oracle on one single-stream block of the workload (float64)."""
+def cpu_baseline(cfg, wl):
+    """Time the oracle (float64 NumPy) on a bounded sample of the step: one
+    dual-stream block and two single-stream blocks of the workload, with the
+    step's own modulation and RoPE tables. Returns (seconds for a whole step
+    extrapolated as n_dual x dual + n_single x mean(single), plus the
+    embedding and final layer scaled by FLOPs; sample seconds; threads)."""
     from oracle import dit_oracle as O
     from diffusion_transformer_fwd_amd import synth
     try:
@@ -143,13 +147,25 @@ def cpu_baseline(cfg, wl, seconds_hint=True):
     gw = synth.global_weights(cfg, 0)
     mod = O.modulation(gw, np.array([wl.sigma]), cfg.time_channels)
     cos, sin = O.rope_tables(pos, cfg.axes_dim, cfg.theta)
-    w = synth.single_weights(cfg, 0, 0)
+    wd = synth.dual_weights(cfg, 0, 0)
     t0 = time.perf_counter()
-    O.single_block(x, w, mod["single"], cos, sin, cfg.heads, cfg.eps, cfg.prenorm)
-    dt = time.perf_counter() - t0
+    O.dual_block(x, wl.n_txt, wd, mod["dual_txt"], mod["dual_img"], cos, sin, cfg.heads,
+                 cfg.eps, cfg.prenorm)
+    t_dual = time.perf_counter() - t0
+    t_single = []
+    for i in range(2):
+        ws = synth.single_weights(cfg, 0, i)
+        t0 = time.perf_counter()
+        O.single_block(x, ws, mod["single"], cos, sin, cfg.heads, cfg.eps, cfg.prenorm)
+        t_single.append(time.perf_counter() - t0)
     D, F = cfg.hidden, cfg.mlp_hidden
     blk_flops = 2.0 * S * D * (3 * D + 2 * F) + 2.0 * S * (D + F) * D + 4.0 * S * S * D
-    return dt, blk_flops, threads
+    blocks_s = cfg.n_dual * t_dual + cfg.n_single * float(np.mean(t_single))
+    # embeddings and final layer at the blocks' FLOP rate
+    rest_flops = 2.0 * (wl.n_txt * cfg.txt_channels + (wl.n_img + wl.n_ref) * cfg.in_channels
+                        ) * D + 2.0 * wl.n_img * D * cfg.in_channels
+    rate = 3 * blk_flops / (t_dual + sum(t_single))
+    return blocks_s + rest_flops / rate, t_dual + sum(t_single), threads
 
 
 def main():
@@ -299,14 +315,15 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        log("CPU baseline: oracle single-stream block (float64)")
-        dt, blk_flops, threads = cpu_baseline(cfg, wl)
-        cpu_ms = dt * 1000.0 * step_flops / blk_flops
+        log("CPU baseline: oracle, one dual and two single-stream blocks (float64)")
+        step_s, sample_s, threads = cpu_baseline(cfg, wl)
+        cpu_ms = step_s * 1000.0
         cpu = {"value": round(cpu_ms, 1), "unit": "ms", "cores": threads, "kind": "oracle",
-               "sample": f"one single-stream block of the 1024px step (S=4608) in float64 "
-                         f"NumPy, {dt:.1f} s, scaled to the 25-block step by FLOP count "
-                         f"({blk_flops / 1e12:.3f} of {step_flops / 1e12:.2f} TFLOP)"}
-        log(f"CPU baseline {cpu_ms:.0f} ms/step ({dt:.1f} s per block, {threads} threads)")
+               "sample": f"one dual-stream and two single-stream blocks of the 1024px step "
+                         f"(S={wl.seq}) in float64 NumPy, {sample_s:.1f} s; step = "
+                         f"{cfg.n_dual} x dual + {cfg.n_single} x mean single, plus the "
+                         f"embeddings and final layer at the blocks' FLOP rate"}
+        log(f"CPU baseline {cpu_ms:.0f} ms/step ({sample_s:.1f} s sample, {threads} threads)")
 
     if args.copy_calibration:
         # a fill (writes COPY_CAL_BYTES) and elementwise negations (read and

@@ -361,12 +361,14 @@ int run_gemm(dit::GemmBatch& g, hipStream_t st) {
 
 // K split of a GEMM whose tiles alone would leave most CUs idle for the whole
 // launch: the final projection (N = 128, one column of tiles) and the text
-// embedding (K = 7680 on 2 B row tiles). The chunk count depends on N and K
-// only, never on M, and the chunks are summed in a fixed order, so a batch
-// row's result does not depend on the rest of the batch.
+// embedding (K = 7680 on 2 B row tiles). With so few tiles a launch is bound
+// by the latency of each tile's own K loop, so the chunks are short (about
+// 384 to 1152 of K). The chunk count depends on N and K only, never on M,
+// and the chunks are summed in a fixed order, so a batch row's result does
+// not depend on the rest of the batch.
 int split_k_chunks(int64_t N, int64_t K) {
-  if (N <= 256) return (int)std::max<int64_t>(1, std::min<int64_t>(4, K / 256));
-  return (int)std::max<int64_t>(1, std::min<int64_t>(3, K / 2048));
+  if (N <= 256) return (int)std::max<int64_t>(1, std::min<int64_t>(8, K / 384));
+  return (int)std::max<int64_t>(1, std::min<int64_t>(7, K / 1024));
 }
 
 // Appends p's K chunks (multiples of 64, at most G) to g: chunk 0 writes p's
@@ -406,10 +408,13 @@ int run_gemm_split_f32(dit::GemmBatch& g, const dit::GemmProblem& p, float* part
                        size_t part_bytes, hipStream_t st) {
   if (g.count >= dit::kMaxGemmProblems) return fail(DIT_E_SHAPE, "GEMM batch full");
   int G = std::min(split_k_chunks(p.N, p.K), dit::kMaxGemmProblems - g.count);
+  // partials that fit in part_bytes (a multiple of the batch size, like M,
+  // so the count does not depend on B either)
+  const size_t one = (size_t)std::max(p.M, 1) * p.N * 4;
+  G = (int)std::min<size_t>((size_t)G, 1 + part_bytes / one);
   const int64_t kc = round_up((p.K + G - 1) / std::max(G, 1), 64);
   G = (int)((p.K + kc - 1) / kc);
-  if (G < 2 || (size_t)(G - 1) * p.M * p.N * 4 > part_bytes || p.epi != dit::EPI_F32 ||
-      (p.N & 3) || (p.ldc & 3)) {
+  if (G < 2 || p.epi != dit::EPI_F32 || (p.N & 3) || (p.ldc & 3)) {
     g.p[g.count++] = p;
     return run_gemm(g, st);
   }

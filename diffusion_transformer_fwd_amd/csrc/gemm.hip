@@ -107,10 +107,16 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const GemmBatch args) 
   pi = __builtin_amdgcn_readfirstlane(pi);
   // Constant-index copies keep every field in scalar registers.
   GemmProblem P;
-  if (pi == 0) P = args.p[0];
-  else if (pi == 1) P = args.p[1];
-  else if (pi == 2) P = args.p[2];
-  else P = args.p[3];
+  switch (pi) {
+    case 0: P = args.p[0]; break;
+    case 1: P = args.p[1]; break;
+    case 2: P = args.p[2]; break;
+    case 3: P = args.p[3]; break;
+    case 4: P = args.p[4]; break;
+    case 5: P = args.p[5]; break;
+    case 6: P = args.p[6]; break;
+    default: P = args.p[7]; break;
+  }
   const int M = P.M, N = P.N, K = P.K, epi = P.epi;
   int tm, tn;
   tile_coords(L - P.tile_begin, P.tiles_m, P.tiles_n, tm, tn);

@@ -42,7 +42,7 @@ struct GemmProblem {
   int32_t tiles_m, tiles_n, tile_begin, pad_;
 };
 
-constexpr int kMaxGemmProblems = 4;
+constexpr int kMaxGemmProblems = 8;
 
 // Operands of the EPI_QKV epilogue, shared by the problems of a launch; the
 // QK gains are per problem (text and image streams differ).
@@ -108,12 +108,12 @@ hipError_t qkv_pad_launch(const QkvPadArgs& a, hipStream_t stream);
 
 // ------------------------------------------------------------------ split-K sum
 // c[row(r), n] += p[0][r, n], then += p[1][r, n], ... (np partials in that
-// order), row(r) = (r / seg_len) * seg_stride + seg_off + r % seg_len: the
+// order, np <= 7), row(r) = (r / seg_len) * seg_stride + seg_off + r % seg_len: the
 // end of a GEMM whose K range ran as np + 1 chunk problems of one launch,
 // chunk 0 writing c and chunk k + 1 writing p[k] [rows, ldp]. cols % 4 == 0.
 struct SplitSumArgs {
   float* c;
-  const float* p[3];
+  const float* p[7];
   int64_t ldc, ldp, seg_stride;
   int32_t rows, cols, np, seg_len, seg_off;
 };

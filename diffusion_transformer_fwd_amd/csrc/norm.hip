@@ -333,7 +333,7 @@ hipError_t qkv_pad_launch(const QkvPadArgs& a, hipStream_t stream) {
 }
 
 hipError_t split_sum_launch(const SplitSumArgs& a, hipStream_t stream) {
-  if (a.np < 1 || a.np > 3 || (a.cols & 3) || a.seg_len < 1) return hipErrorInvalidValue;
+  if (a.np < 1 || a.np > 7 || (a.cols & 3) || a.seg_len < 1) return hipErrorInvalidValue;
   const int64_t n = (int64_t)a.rows * (a.cols >> 2);
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(split_sum_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, a);

@@ -349,8 +349,8 @@ def test_denoise_graph_replays_match_eager():
 
 
 def test_step_split_k_parity_and_batch_invariance():
-    """The text embedding (K = 4096 here: 2 chunks) and the final projection
-    (N = 128, K = 1024: 4 chunks) run K-split, the chunks summed in a fixed
+    """The text embedding (K = 4096 here: 4 chunks) and the final projection
+    (N = 128, K = 1024: 2 chunks) run K-split, the chunks summed in a fixed
     order: the step matches the oracle, and each batch row equals its solo
     run bit for bit (the split depends on N and K, never on the batch)."""
     cfg = small_cfg(hidden=1024, heads=8, mlp_hidden=3072, txt_channels=4096)
