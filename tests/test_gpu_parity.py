@@ -373,6 +373,34 @@ def test_step_split_k_parity_and_batch_invariance():
         assert np.array_equal(to_np(v1)[0], both[b]), f"row {b}"
 
 
+def test_step_largest_batch():
+    """B = 64, the largest batch a call accepts, each row with its own sigma
+    and inputs: sampled rows match the oracle and the last row equals its
+    solo run bit for bit."""
+    cfg = small_cfg()
+    mw = synth.ModelWeights(cfg, 0, cache=True)
+    dw = dit.ModelWeights(mw)
+    B = dit.MAX_BATCH
+    wl = synth.Workload("s", B, 16, (4, 6), ((2, 2),), 0.5)
+    ins = [synth.step_inputs(cfg, wl, batch_row=b) for b in range(B)]
+    sig = np.linspace(1.0, 0.05, B).astype(np.float32)
+    pos = dit.position_ids(wl.n_txt, wl.img_grid, wl.ref_grids)
+    cos_d, sin_d = dit.rope_tables(cfg, pos)
+    txt = np.stack([i["txt"] for i in ins])
+    lat = np.stack([i["latents"] for i in ins])
+    log(f"step B={B} S={wl.seq}")
+    v = to_np(dit.step(cfg, dw, dit.to_bf16_device(txt), dit.to_bf16_device(lat), sig,
+                       wl.n_img, cos_d, sin_d))
+    posn = O.position_ids(wl.n_txt, wl.img_grid, wl.ref_grids)
+    for b in (0, 37, B - 1):
+        want = O.step(cfg, mw, txt[b:b + 1], lat[b:b + 1], sig[b:b + 1].astype(np.float64),
+                      wl.n_img, posn)
+        assert_close(v[b:b + 1], want, what=f"step B={B} row {b}")
+    v1 = to_np(dit.step(cfg, dw, dit.to_bf16_device(txt[-1:]), dit.to_bf16_device(lat[-1:]),
+                        sig[-1:], wl.n_img, cos_d, sin_d))
+    assert np.array_equal(v1[0], v[-1])
+
+
 @pytest.fixture(scope="module")
 def klein():
     log("drawing and uploading FLUX.2-klein-size weights ...")
