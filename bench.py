@@ -175,6 +175,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--profile-steps", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", default="step_1024px_s4608",
+                    help="step workload to time (the default is the headline one; the others "
+                         "are the reference-image, batch-4 and three-reference steps)")
     ap.add_argument("--denoise-reps", type=int, default=3,
                     help="timed runs of the 4-step sampling loop, eager and graph-replayed")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -199,19 +202,22 @@ def main():
     dit.lib()
     torch.cuda.set_device(0)
     cfg = synth.FLUX2_KLEIN
-    wl = synth.W_STEP_1024
+    wl = {w.name: w for w in (synth.W_STEP_1024, synth.W_STEP_1024_REF, synth.W_STEP_1920x1088_B4,
+                              synth.W_STEP_848x624_3REF)}[args.workload]
+    B = wl.batch
 
     log("drawing weights and inputs")
     t0 = time.time()
     dw = dit.ModelWeights(synth.ModelWeights(cfg, 0))
-    ins = synth.step_inputs(cfg, wl)
-    txt = dit.to_bf16_device(ins["txt"][None])
-    lat = dit.to_bf16_device(ins["latents"][None])
+    ins_b = [synth.step_inputs(cfg, wl, batch_row=b) for b in range(B)]
+    ins = ins_b[0]
+    txt = dit.to_bf16_device(np.stack([i["txt"] for i in ins_b]))
+    lat = dit.to_bf16_device(np.stack([i["latents"] for i in ins_b]))
     pos = dit.position_ids(wl.n_txt, wl.img_grid, wl.ref_grids)
     cos, sin = dit.rope_tables(cfg, pos)
     ws = dit.Workspace()
-    out = torch.empty((1, wl.n_img, cfg.in_channels), dtype=torch.float32, device="cuda")
-    sigma = [wl.sigma]
+    out = torch.empty((B, wl.n_img, cfg.in_channels), dtype=torch.float32, device="cuda")
+    sigma = [wl.sigma] * B
     torch.cuda.synchronize()
     log(f"setup {time.time() - t0:.1f}s")
 
@@ -242,7 +248,7 @@ def main():
     # the 4-step sampling loop on the device (Euler between steps), eager and
     # captured once as a HIP graph and replayed
     den = None
-    if args.denoise_reps > 0:
+    if args.denoise_reps > 0 and B == 1 and wl.n_ref == 0:
         sched = np.array([[1.0, 0.75, 0.5, 0.25, 0.0]], np.float32)
         z0 = dit.to_f32_device(ins["latents"][None, :wl.n_img])
         z = z0.clone()
@@ -317,12 +323,13 @@ def main():
     if not args.no_cpu_baseline:
         log("CPU baseline: oracle, one dual and two single-stream blocks (float64)")
         step_s, sample_s, threads = cpu_baseline(cfg, wl)
-        cpu_ms = step_s * 1000.0
+        cpu_ms = step_s * 1000.0 * B  # batch rows are independent
         cpu = {"value": round(cpu_ms, 1), "unit": "ms", "cores": threads, "kind": "oracle",
-               "sample": f"one dual-stream and two single-stream blocks of the 1024px step "
-                         f"(S={wl.seq}) in float64 NumPy, {sample_s:.1f} s; step = "
+               "sample": f"one dual-stream and two single-stream blocks of one sample of "
+                         f"{wl.name} (S={wl.seq}) in float64 NumPy, {sample_s:.1f} s; step = "
                          f"{cfg.n_dual} x dual + {cfg.n_single} x mean single, plus the "
-                         f"embeddings and final layer at the blocks' FLOP rate"}
+                         f"embeddings and final layer at the blocks' FLOP rate"
+                         + (f", times {B} batch rows" if B > 1 else "")}
         log(f"CPU baseline {cpu_ms:.0f} ms/step ({sample_s:.1f} s sample, {threads} threads)")
 
     if args.copy_calibration:
@@ -340,11 +347,11 @@ def main():
     rec = {
         "metric": METRIC, "value": round(ms, 4), "unit": "ms", "n_gpus": 1, "steps": K,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": False,
-        "scaling": "weak", "vs_baseline": round(ms / P100A_STEP_MS, 5),
+        "scaling": "weak", "vs_baseline": round(ms / P100A_STEP_MS, 5) if wl is synth.W_STEP_1024 else None,
         "baseline": {"value": P100A_STEP_MS, "unit": "ms",
                      "source": "per DiT step at 1024^2 on a Tenstorrent p100a (context only)"},
         "dtype": "bf16", "data": "synthetic (seeded N(0,1/fan_in) weights, N(0,1) inputs)",
-        "config": {"workload": wl.name, "batch": 1, "seq_len": wl.seq, "n_txt": wl.n_txt,
+        "config": {"workload": wl.name, "batch": B, "seq_len": wl.seq, "n_txt": wl.n_txt,
                    "n_img": wl.n_img, "blocks": "5 dual + 20 single", "hidden": cfg.hidden,
                    "heads": cfg.heads, "parallelism": "none (1 GPU)"},
         "ms_median": round(float(np.median(per)), 4),
