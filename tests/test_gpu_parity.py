@@ -112,6 +112,10 @@ DUAL_CASES = [
     ("refs_b3", {}, 17, (6, 6), ((3, 5), (2, 2)), 3),
     ("layernorm", {"prenorm": 1}, 32, (8, 8), (), 2),
     ("d3072_s600", {"hidden": 3072, "heads": 24, "mlp_hidden": 9216}, 88, (16, 32), (), 1),
+    # the 1024x1024 shape (512 text + 64 x 64 image rows), both pre-norm readings
+    ("d3072_1024px", {"hidden": 3072, "heads": 24, "mlp_hidden": 9216}, 512, (64, 64), (), 1),
+    ("d3072_1024px_layernorm", {"hidden": 3072, "heads": 24, "mlp_hidden": 9216, "prenorm": 1},
+     512, (64, 64), (), 1),
 ]
 
 
@@ -137,6 +141,9 @@ SINGLE_CASES = [
     ("refs_b3", {}, 17, (6, 6), ((3, 5), (2, 2)), 3),
     ("layernorm", {"prenorm": 1}, 32, (8, 8), (), 1),
     ("d3072_s600", {"hidden": 3072, "heads": 24, "mlp_hidden": 9216}, 88, (16, 32), (), 1),
+    # the 1024x1024 shape with the LayerNorm reading (RMS: test_single_block_1024px)
+    ("d3072_1024px_layernorm", {"hidden": 3072, "heads": 24, "mlp_hidden": 9216, "prenorm": 1},
+     512, (64, 64), (), 1),
 ]
 
 
