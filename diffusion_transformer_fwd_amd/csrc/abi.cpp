@@ -980,8 +980,6 @@ int dit_denoise_forward(const dit_config* cfg, const dit_model_weights* w, const
   DIT_CHECK(check_step_args(cfg, w, txt, B, n_txt, n_img, n_ref, cos_dev, sin_dev));
   if (n_steps < 1 || n_steps > DIT_MAX_STEPS)
     return fail(DIT_E_SHAPE, "n_steps %d out of range [1, %d]", n_steps, (int)DIT_MAX_STEPS);
-  if (cfg->in_channels % 4)
-    return fail(DIT_E_UNSUPPORTED, "in_channels %d is not a multiple of 4", cfg->in_channels);
   DIT_CHECK(check_ptr(z, "z"));
   if (n_ref > 0) DIT_CHECK(check_ptr(ref, "ref", 8));
   if (!sigmas_host) return fail(DIT_E_NULL, "sigmas is NULL");
