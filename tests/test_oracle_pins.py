@@ -529,3 +529,18 @@ def test_planted_mistake_is_caught(name, monkeypatch):
     monkeypatch.setattr(O, attr, _mutants()[name])
     got = O.dual_block(x, 3, w, mod["dual_txt"], mod["dual_img"], cos, sin, cfg.heads)
     assert not np.allclose(got[0], want, rtol=0, atol=1e-6)
+
+
+def test_planted_euler_mistakes_are_caught(monkeypatch):
+    """Slips in the update are caught by the straight-path pin: Euler then
+    no longer lands on x0."""
+    rng = np.random.default_rng(5)
+    x0, n = rng.standard_normal((2, 1, 4, 8))
+    sig = np.array([[1.0, 0.6, 0.2, 0.0]])
+    z0 = (1 - sig[0, 0]) * x0 + sig[0, 0] * n
+    for bad in (lambda z, v, s, s1: z - (s1 - s) * v,   # sign of the step
+                lambda z, v, s, s1: z + s1 * v,         # sigma instead of its change
+                lambda z, v, s, s1: v + (s1 - s) * z):  # latent and velocity swapped
+        monkeypatch.setattr(O, "euler", bad)
+        got = O.denoise(lambda z, s: n - x0, z0, sig)
+        assert not np.allclose(got, x0, atol=1e-6)
