@@ -355,6 +355,31 @@ def test_denoise_graph_replays_match_eager():
         torch.cuda.synchronize()
 
 
+STEP_EDGE = [
+    # (name, cfg kwargs, workload): block schedules with one kind of block
+    # only, a one-token sequence, and another head count
+    ("dual_only", {"n_dual": 3, "n_single": 0}, synth.Workload("s", 1, 24, (4, 5), (), 0.8)),
+    ("single_only", {"n_dual": 0, "n_single": 3}, synth.Workload("s", 2, 24, (4, 5), ((2, 3),), 0.4)),
+    ("one_token", {"n_dual": 1, "n_single": 1}, synth.Workload("s", 1, 0, (1, 1), (), 0.9)),
+    ("h12_d1536", {"hidden": 1536, "heads": 12, "mlp_hidden": 4608, "n_dual": 1, "n_single": 2},
+     synth.Workload("s", 1, 64, (12, 20), ((6, 4),), 0.6)),
+]
+
+
+@pytest.mark.parametrize("case", STEP_EDGE, ids=[c[0] for c in STEP_EDGE])
+def test_step_edge(case):
+    name, kw, wl = case
+    cfg = small_cfg(**kw)
+    mw = synth.ModelWeights(cfg, 0, cache=True)
+    dw = dit.ModelWeights(mw)
+    log(f"step {name}: S={wl.seq} B={wl.batch}")
+    v, ins = run_step(cfg, dw, wl)
+    pos = O.position_ids(wl.n_txt, wl.img_grid, wl.ref_grids)
+    want = O.step(cfg, mw, np.stack([i["txt"] for i in ins]), np.stack([i["latents"] for i in ins]),
+                  np.full(wl.batch, wl.sigma), wl.n_img, pos)
+    assert_close(to_np(v), want, what=f"step {name}")
+
+
 def test_step_split_k_parity_and_batch_invariance():
     """The text embedding (K = 4096 here: 4 chunks) and the final projection
     (N = 128, K = 1024: 2 chunks) run K-split, the chunks summed in a fixed
