@@ -177,7 +177,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="step_1024px_s4608",
                     help="step workload to time (the default is the headline one; the others "
-                         "are the reference-image, batch-4 and three-reference steps)")
+                         "are the reference-image, batch-4, three-reference and 512px "
+                         "reference steps)")
     ap.add_argument("--denoise-reps", type=int, default=3,
                     help="timed runs of the 4-step sampling loop, eager and graph-replayed")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -203,7 +204,7 @@ def main():
     torch.cuda.set_device(0)
     cfg = synth.FLUX2_KLEIN
     wl = {w.name: w for w in (synth.W_STEP_1024, synth.W_STEP_1024_REF, synth.W_STEP_1920x1088_B4,
-                              synth.W_STEP_848x624_3REF)}[args.workload]
+                              synth.W_STEP_848x624_3REF, synth.W_STEP_512_REF)}[args.workload]
     B = wl.batch
 
     log("drawing weights and inputs")

@@ -245,6 +245,8 @@ W_STEP_1920x1088_B4 = Workload("step_1920x1088_b4_s8672", 4, 512, (68, 120), (),
 # three references at their own aspect (1024x1024, 1184x880, 512x768 px)
 W_STEP_848x624_3REF = Workload("step_848x624_3ref_s12281", 1, 512, (39, 53),
                                ((64, 64), (55, 74), (48, 32)), 0.75)
+# the smallest listed size with a reference: 512x512 output, one 512x512 reference
+W_STEP_512_REF = Workload("step_512px_1ref_s2560", 1, 512, (32, 32), ((32, 32),), 0.75)
 # the longest sequence: 1920x1088 output with three 1024x1024 references
 W_SINGLE_MAX = Workload("single_block_1920x1088_3ref_s20960", 1, 512, (68, 120),
                         ((64, 64), (64, 64), (64, 64)), 0.75)

@@ -28,6 +28,7 @@ WORKLOADS = {
     synth.W_STEP_1024_REF.name: (synth.W_STEP_1024_REF, 8),
     synth.W_STEP_1920x1088_B4.name: (synth.W_STEP_1920x1088_B4, 32),
     synth.W_STEP_848x624_3REF.name: (synth.W_STEP_848x624_3REF, 8),
+    synth.W_STEP_512_REF.name: (synth.W_STEP_512_REF, 4),
 }
 
 

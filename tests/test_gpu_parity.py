@@ -442,7 +442,7 @@ def klein():
 
 
 GOLDEN_CASES = [synth.W_STEP_1024, synth.W_STEP_1024_REF, synth.W_STEP_1920x1088_B4,
-                synth.W_STEP_848x624_3REF]
+                synth.W_STEP_848x624_3REF, synth.W_STEP_512_REF]
 
 
 @pytest.mark.slow
