@@ -32,15 +32,16 @@
 //    columns are one head), so the fused projection never round-trips HBM.
 //    Output rows go through a (segment length, stride, offset) map, so
 //    stream-major operands scatter back into x[B, S, D] in place.
-//  * Up to four independent problems share one launch (text + image
-//    streams, or the single block's QKV part + SwiGLU part), so the small
-//    512-row text problem fills gaps instead of taking its own launch.
+//  * Up to eight independent problems share one launch (text + image
+//    streams, the single block's QKV part + SwiGLU part, or the K chunks of
+//    a split contraction), so the small 512-row text problem fills gaps
+//    instead of taking its own launch.
 //  * Launches without the SwiGLU / QKV epilogues may use 256 x 224 tiles
 //    when that takes fewer rounds of tiles over the CUs (the N = 3072
 //    projections at 4608 rows: 252 tiles in one round instead of 216 full
 //    ones leaving 40 CUs idle).
 //  * Tile order: launch index -> XCD-contiguous logical index -> groups of
-//    8 row tiles walked column by column, so co-resident tiles on one XCD
+//    7 row tiles walked column by column, so co-resident tiles on one XCD
 //    share A and W panels in its L2.
 //  * The accumulation order of an output element depends only on K, never
 //    on M, the tile width or the tile position, so a batch row's results
