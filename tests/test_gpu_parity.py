@@ -380,6 +380,33 @@ def test_step_edge(case):
     assert_close(to_np(v), want, what=f"step {name}")
 
 
+def _random_workloads(n, seed=11):
+    """Seeded ragged shapes: text rows 0-80, image grids up to 20 x 20, 0-3
+    references of their own grids, 1-3 batch rows."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        grid = (int(rng.integers(1, 21)), int(rng.integers(1, 21)))
+        refs = tuple((int(rng.integers(1, 13)), int(rng.integers(1, 13)))
+                     for _ in range(int(rng.integers(0, 4))))
+        out.append(synth.Workload(f"rand{i}", int(rng.integers(1, 4)), int(rng.integers(0, 81)),
+                                  grid, refs, float(rng.uniform(0.05, 1.0))))
+    return out
+
+
+@pytest.mark.parametrize("wl", _random_workloads(6), ids=lambda w: f"{w.name}_s{w.seq}_b{w.batch}")
+def test_step_random_shapes(wl):
+    cfg = small_cfg(n_dual=1, n_single=2)
+    mw = synth.ModelWeights(cfg, 0, cache=True)
+    dw = dit.ModelWeights(mw)
+    log(f"step {wl.name}: S={wl.seq} B={wl.batch} grid={wl.img_grid} refs={wl.ref_grids}")
+    v, ins = run_step(cfg, dw, wl)
+    pos = O.position_ids(wl.n_txt, wl.img_grid, wl.ref_grids)
+    want = O.step(cfg, mw, np.stack([i["txt"] for i in ins]), np.stack([i["latents"] for i in ins]),
+                  np.full(wl.batch, wl.sigma), wl.n_img, pos)
+    assert_close(to_np(v), want, what=f"step {wl.name}")
+
+
 def test_step_split_k_parity_and_batch_invariance():
     """The text embedding (K = 4096 here: 4 chunks) and the final projection
     (N = 128, K = 1024: 2 chunks) run K-split, the chunks summed in a fixed
