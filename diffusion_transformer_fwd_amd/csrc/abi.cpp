@@ -170,8 +170,13 @@ StepLayout step_layout(const dit_config& c, int64_t B, int64_t S) {
 // The sampling loop: the step's workspace, then its latent operand
 // lat bf16 [B, S, C] and velocity v fp32 [B, S, C] (sized for S rows, so the
 // workspace query needs no split of S into image and reference tokens).
+// Steps whose modulation vectors one pass over the modulation weights
+// computes in the sampling loop (the GEMV takes four rows per pass, so at
+// B = 1 the pages' four steps cost one pass instead of four).
+constexpr int kModSteps = 4;
+
 struct DenoiseLayout {
-  size_t step = 0, lat = 0, v = 0, total = 0;
+  size_t step = 0, lat = 0, v = 0, mods = 0, modws = 0, total = 0;
 };
 
 DenoiseLayout denoise_layout(const dit_config& c, int64_t B, int64_t S) {
@@ -185,6 +190,8 @@ DenoiseLayout denoise_layout(const dit_config& c, int64_t B, int64_t S) {
   L.step = take(step_layout(c, B, S).total);
   L.lat = take((size_t)B * S * c.in_channels * 2);
   L.v = take((size_t)B * S * c.in_channels * 4);
+  L.mods = take((size_t)kModSteps * B * DIT_MOD_ROWS * c.hidden * 4);
+  L.modws = take(mod_layout(c, (int64_t)kModSteps * B).total);
   L.total = off;
   return L;
 }
@@ -718,22 +725,24 @@ int check_block_common(const dit_config* cfg, float* x, int32_t B, int64_t S,
 }
 
 // The step after validation: enqueues modulation, embeddings, blocks and
-// the final layer on st, using the step workspace at ws.
+// the final layer on st, using the step workspace at ws. With mod_pre set,
+// the step's modulation vectors [B, 17, D] are taken from there instead of
+// computed from sigma_host.
 int launch_step(const dit_config& c, const dit_model_weights& wr, const void* txt,
                 const void* latents, const float* sigma_host, int32_t B, int64_t n_txt,
                 int64_t n_img, int64_t n_ref, const float* cos_dev, const float* sin_dev,
-                float* v_out, void* ws, hipStream_t st) {
+                float* v_out, void* ws, hipStream_t st, const float* mod_pre = nullptr) {
   const dit_model_weights* w = &wr;
   const int64_t S = n_txt + n_img + n_ref;
   const StepLayout L = step_layout(c, B, S);
   const int64_t D = c.hidden;
   float* x = reinterpret_cast<float*>(at(ws, L.x));
-  float* mod = reinterpret_cast<float*>(at(ws, L.mod));
+  float* mod = mod_pre ? const_cast<float*>(mod_pre) : reinterpret_cast<float*>(at(ws, L.mod));
   void* bws = at(ws, L.block);
   const int64_t mbs = DIT_MOD_ROWS * D;
 
   // 1. global modulation, once for the whole step
-  DIT_CHECK(launch_modulation(c, *w, sigma_host, B, mod, at(ws, L.modws), st));
+  if (!mod_pre) DIT_CHECK(launch_modulation(c, *w, sigma_host, B, mod, at(ws, L.modws), st));
 
   // K-split partials of the embedding and the final projection live in the
   // single block's d6 region, free before the first block and after the last
@@ -1004,16 +1013,25 @@ int dit_denoise_forward(const dit_config* cfg, const dit_model_weights* w, const
   la.C = (int32_t)C;
   DIT_TRY(timed(DIT_K_LATENT, 0.0, (double)B * (n_img * C * 6.0 + n_ref * C * 4.0), st,
                 [&] { return dit::latent_pack_launch(la, st); }));
-  std::vector<float> sig(B);
-  for (int i = 0; i < n_steps; ++i) {
-    for (int b = 0; b < B; ++b) {
-      sig[b] = sigmas_host[(int64_t)b * (n_steps + 1) + i];
-      la.dsig[b] = sigmas_host[(int64_t)b * (n_steps + 1) + i + 1] - sig[b];
+  // the modulation of up to kModSteps steps at a time: rows [step][b]
+  float* mods = reinterpret_cast<float*>(at(ws, L.mods));
+  const int64_t step_mod = (int64_t)B * DIT_MOD_ROWS * cfg->hidden;
+  std::vector<float> sig((size_t)kModSteps * B);
+  for (int i0 = 0; i0 < n_steps; i0 += kModSteps) {
+    const int G = std::min(kModSteps, n_steps - i0);
+    for (int j = 0; j < G; ++j)
+      for (int b = 0; b < B; ++b) sig[(size_t)j * B + b] = sigmas_host[(int64_t)b * (n_steps + 1) + i0 + j];
+    DIT_CHECK(launch_modulation(*cfg, *w, sig.data(), G * B, mods, at(ws, L.modws), st));
+    for (int j = 0; j < G; ++j) {
+      const int i = i0 + j;
+      for (int b = 0; b < B; ++b)
+        la.dsig[b] = sigmas_host[(int64_t)b * (n_steps + 1) + i + 1] -
+                     sigmas_host[(int64_t)b * (n_steps + 1) + i];
+      DIT_CHECK(launch_step(*cfg, *w, txt, la.lat, nullptr, B, n_txt, n_img, n_ref, cos_dev,
+                            sin_dev, v, at(ws, L.step), st, mods + j * step_mod));
+      DIT_TRY(timed(DIT_K_LATENT, 0.0, (double)B * n_img * C * 14.0, st,
+                    [&] { return dit::euler_launch(la, st); }));
     }
-    DIT_CHECK(launch_step(*cfg, *w, txt, la.lat, sig.data(), B, n_txt, n_img, n_ref, cos_dev,
-                          sin_dev, v, at(ws, L.step), st));
-    DIT_TRY(timed(DIT_K_LATENT, 0.0, (double)B * n_img * C * 14.0, st,
-                  [&] { return dit::euler_launch(la, st); }));
   }
   return DIT_OK;
 }

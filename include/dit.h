@@ -251,7 +251,9 @@ int dit_step_forward(const dit_config* cfg, const dit_model_weights* w,
  *   sigmas_host: host fp32 [B, n_steps + 1], finite; 1 <= n_steps <=
  *      DIT_MAX_STEPS;
  *   txt, cos/sin, B, n_txt, n_img, n_ref: as for dit_step_forward.
- * The step's latent operand is bf16(z) (the GEMM rounds its operands).
+ * The step's latent operand is bf16(z) (the GEMM rounds its operands). The
+ * modulation vectors of up to four steps come from one pass over the
+ * modulation weights (each step's still depends on its own sigma only).
  * The sigmas travel as kernel arguments, so the enqueued work for one shape
  * and schedule can be captured once in a HIP graph and replayed.
  * ws: dit_workspace_bytes(cfg, DIT_WS_DENOISE, B, S) bytes, 256-byte aligned. */
