@@ -176,7 +176,7 @@ StepLayout step_layout(const dit_config& c, int64_t B, int64_t S) {
 constexpr int kModSteps = 4;
 
 struct DenoiseLayout {
-  size_t step = 0, lat = 0, v = 0, mods = 0, modws = 0, total = 0;
+  size_t step = 0, lat = 0, v = 0, mods = 0, modws = 0, txt = 0, total = 0;
 };
 
 DenoiseLayout denoise_layout(const dit_config& c, int64_t B, int64_t S) {
@@ -192,6 +192,7 @@ DenoiseLayout denoise_layout(const dit_config& c, int64_t B, int64_t S) {
   L.v = take((size_t)B * S * c.in_channels * 4);
   L.mods = take((size_t)kModSteps * B * DIT_MOD_ROWS * c.hidden * 4);
   L.modws = take(mod_layout(c, (int64_t)kModSteps * B).total);
+  L.txt = take((size_t)B * S * c.hidden * 4);  // embedded text rows (n_txt <= S)
   L.total = off;
   return L;
 }
@@ -727,11 +728,14 @@ int check_block_common(const dit_config* cfg, float* x, int32_t B, int64_t S,
 // The step after validation: enqueues modulation, embeddings, blocks and
 // the final layer on st, using the step workspace at ws. With mod_pre set,
 // the step's modulation vectors [B, 17, D] are taken from there instead of
-// computed from sigma_host.
+// computed from sigma_host. The text rows' embedding depends on the prompt
+// only: txt_save (fp32 [B, n_txt, D]) receives it, or with txt_pre it is
+// copied from there instead of computed.
 int launch_step(const dit_config& c, const dit_model_weights& wr, const void* txt,
                 const void* latents, const float* sigma_host, int32_t B, int64_t n_txt,
                 int64_t n_img, int64_t n_ref, const float* cos_dev, const float* sin_dev,
-                float* v_out, void* ws, hipStream_t st, const float* mod_pre = nullptr) {
+                float* v_out, void* ws, hipStream_t st, const float* mod_pre = nullptr,
+                float* txt_save = nullptr, const float* txt_pre = nullptr) {
   const dit_model_weights* w = &wr;
   const int64_t S = n_txt + n_img + n_ref;
   const StepLayout L = step_layout(c, B, S);
@@ -758,13 +762,25 @@ int launch_step(const dit_config& c, const dit_model_weights& wr, const void* tx
                                  x, D);
     set_rows(p, (int)(n_img + n_ref), S, (int)n_txt);
     g.p[g.count++] = p;
-    if (n_txt > 0) {
+    if (n_txt > 0 && !txt_pre) {
       dit::GemmProblem t = problem(txt, c.txt_channels, w->ctx_embed, c.txt_channels,
                                    (int)(B * n_txt), (int)D, c.txt_channels, dit::EPI_F32, x, D);
       set_rows(t, (int)n_txt, S, 0);
       DIT_CHECK(run_gemm_split_f32(g, t, part, part_bytes, st));
     } else {
       DIT_CHECK(run_gemm(g, st));
+    }
+    if (n_txt > 0 && (txt_pre || txt_save)) {
+      dit::RowsCopyArgs rc{};
+      rc.src = txt_pre ? txt_pre : x;
+      rc.dst = txt_pre ? x : txt_save;
+      rc.n = n_txt;
+      rc.src_bstride = txt_pre ? n_txt : S;
+      rc.dst_bstride = txt_pre ? S : n_txt;
+      rc.B = B;
+      rc.D = (int)D;
+      DIT_TRY(timed(DIT_K_LATENT, 0.0, 8.0 * B * n_txt * D, st,
+                    [&] { return dit::rows_copy_launch(rc, st); }));
     }
   }
 
@@ -1027,8 +1043,11 @@ int dit_denoise_forward(const dit_config* cfg, const dit_model_weights* w, const
       for (int b = 0; b < B; ++b)
         la.dsig[b] = sigmas_host[(int64_t)b * (n_steps + 1) + i + 1] -
                      sigmas_host[(int64_t)b * (n_steps + 1) + i];
+      // the text embedding is computed by the first step and kept for the rest
+      float* txt_rows = reinterpret_cast<float*>(at(ws, L.txt));
       DIT_CHECK(launch_step(*cfg, *w, txt, la.lat, nullptr, B, n_txt, n_img, n_ref, cos_dev,
-                            sin_dev, v, at(ws, L.step), st, mods + j * step_mod));
+                            sin_dev, v, at(ws, L.step), st, mods + j * step_mod,
+                            i == 0 ? txt_rows : nullptr, i == 0 ? nullptr : txt_rows));
       DIT_TRY(timed(DIT_K_LATENT, 0.0, (double)B * n_img * C * 14.0, st,
                     [&] { return dit::euler_launch(la, st); }));
     }

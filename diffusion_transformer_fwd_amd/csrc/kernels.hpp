@@ -191,6 +191,17 @@ struct LatentArgs {
   float dsig[64];
 };
 hipError_t latent_pack_launch(const LatentArgs& a, hipStream_t stream);
+
+// dst[b * dst_bstride + r, :] = src[b * src_bstride + r, :] for rows r < n of
+// each of B batch rows (fp32, D % 4 == 0): the embedded text rows kept
+// across the steps of the sampling loop.
+struct RowsCopyArgs {
+  const float* src;
+  float* dst;
+  int64_t n, src_bstride, dst_bstride;  // strides in rows
+  int32_t B, D;
+};
+hipError_t rows_copy_launch(const RowsCopyArgs& a, hipStream_t stream);
 hipError_t euler_launch(const LatentArgs& a, hipStream_t stream);
 
 }  // namespace dit

@@ -6,7 +6,8 @@
 //   * rope_tables: cos/sin of every pair angle from integer positions
 //   * time_features + gemv: the global modulation vectors from sigma
 //   * latent_pack + euler: the latent state of the sampling loop between
-//     steps (flow-matching Euler update, bf16 operand of the next step)
+//     steps (flow-matching Euler update, bf16 operand of the next step);
+//     rows_copy: the embedded text rows the loop keeps across steps
 //
 // The maths each one follows is stated at its kernel; the pages it comes
 // from are "flux2-klein-p100a" (Caveats: modulation global per step) and
@@ -299,6 +300,18 @@ __global__ __launch_bounds__(256) void euler_kernel(const LatentArgs a) {
   *(reinterpret_cast<u32x2*>(a.lat + (b * (a.n_img + a.n_ref) + r) * a.C) + q) = pack_bf16x4(z);
 }
 
+// One thread per 4 columns of a row.
+__global__ __launch_bounds__(256) void rows_copy_kernel(const RowsCopyArgs a) {
+  const int c4 = a.D >> 2;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)a.B * a.n * c4) return;
+  const int64_t br = i / c4;
+  const int q = (int)(i - br * c4);
+  const int64_t b = br / a.n, r = br - b * a.n;
+  *(reinterpret_cast<f32x4*>(a.dst + (b * a.dst_bstride + r) * a.D) + q) =
+      *(reinterpret_cast<const f32x4*>(a.src + (b * a.src_bstride + r) * a.D) + q);
+}
+
 }  // namespace
 
 hipError_t modnorm_launch(const NormArgs& a, hipStream_t stream) {
@@ -375,6 +388,14 @@ hipError_t euler_launch(const LatentArgs& a, hipStream_t stream) {
   const int64_t n = (int64_t)a.B * a.n_img * (a.C >> 2);
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(euler_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t rows_copy_launch(const RowsCopyArgs& a, hipStream_t stream) {
+  if ((a.D & 3) || a.B < 0 || a.n < 0) return hipErrorInvalidValue;
+  const int64_t n = (int64_t)a.B * a.n * (a.D >> 2);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(rows_copy_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

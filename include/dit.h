@@ -253,7 +253,9 @@ int dit_step_forward(const dit_config* cfg, const dit_model_weights* w,
  *   txt, cos/sin, B, n_txt, n_img, n_ref: as for dit_step_forward.
  * The step's latent operand is bf16(z) (the GEMM rounds its operands). The
  * modulation vectors of up to four steps come from one pass over the
- * modulation weights (each step's still depends on its own sigma only).
+ * modulation weights (each step's still depends on its own sigma only), and
+ * the text rows' embedding, which depends on the prompt only, is computed by
+ * the first step and reused by the others.
  * The sigmas travel as kernel arguments, so the enqueued work for one shape
  * and schedule can be captured once in a HIP graph and replayed.
  * ws: dit_workspace_bytes(cfg, DIT_WS_DENOISE, B, S) bytes, 256-byte aligned. */
