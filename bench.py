@@ -10,9 +10,11 @@ Prints one JSON line (rank 0). Timing: W untimed warm-up steps, then K steps
 bracketed by device synchronisation, per-step HIP events on the launch
 stream. A second, separate pass records HIP events around every kernel
 launch (dit_profile_begin/end) to give per-kernel durations for the
-roofline; the headline number comes from the clean pass. The CPU baseline
-times the oracle (float64 NumPy) on one single-stream block of the same
-workload and scales it by FLOP count to a full step.
+roofline; the headline number comes from the clean pass. The same run also
+times the step with one reference image (S = 8704) and the 1920x1088 batch-4
+step (S = 8672 per sample) under "workloads". The CPU baseline times the
+oracle in fp32 NumPy on one whole step of the workload's first sample, after
+a one-block warm-up.
 """
 import argparse
 import collections
@@ -128,12 +130,12 @@ def log(msg):
     print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
 
-def cpu_baseline(cfg, wl):
-    """Time the oracle (float64 NumPy) on a bounded sample of the step: one
-    dual-stream block and two single-stream blocks of the workload, with the
-    step's own modulation and RoPE tables. Returns (seconds for a whole step
-    extrapolated as n_dual x dual + n_single x mean(single), plus the
-    embedding and final layer scaled by FLOPs; sample seconds; threads)."""
+def cpu_baseline(cfg, mw, wl):
+    """Time the oracle as it stands, in fp32 NumPy (its dtype switch), on one
+    whole step of one sample of the workload, after a one-block warm-up.
+    mw: the synth.ModelWeights the GPU run uploaded (blocks cached in host
+    memory, so drawing weights is not timed). Returns (seconds for the step,
+    threads, algorithmic FLOPs of the step)."""
     from oracle import dit_oracle as O
     from diffusion_transformer_fwd_amd import synth
     try:
@@ -141,31 +143,74 @@ def cpu_baseline(cfg, wl):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = len(os.sched_getaffinity(0))
+    ins = synth.step_inputs(cfg, wl, batch_row=0)
+    txt, lat = ins["txt"][None], ins["latents"][None]
     pos = O.position_ids(wl.n_txt, wl.img_grid, wl.ref_grids)
     S = pos.shape[0]
-    x = synth.residual(cfg, 0, S)[None]
-    gw = synth.global_weights(cfg, 0)
-    mod = O.modulation(gw, np.array([wl.sigma]), cfg.time_channels)
+    # warm-up: one single-stream block on the step's own shapes
+    mod = O.modulation(mw.glob, np.array([wl.sigma]), cfg.time_channels, np.float32)
     cos, sin = O.rope_tables(pos, cfg.axes_dim, cfg.theta)
-    wd = synth.dual_weights(cfg, 0, 0)
+    x = synth.residual(cfg, 0, S)[None]
+    O.single_block(x, mw.single(0), mod["single"], cos.astype(np.float32),
+                   sin.astype(np.float32), cfg.heads, cfg.eps, cfg.prenorm, np.float32)
     t0 = time.perf_counter()
-    O.dual_block(x, wl.n_txt, wd, mod["dual_txt"], mod["dual_img"], cos, sin, cfg.heads,
-                 cfg.eps, cfg.prenorm)
-    t_dual = time.perf_counter() - t0
-    t_single = []
-    for i in range(2):
-        ws = synth.single_weights(cfg, 0, i)
-        t0 = time.perf_counter()
-        O.single_block(x, ws, mod["single"], cos, sin, cfg.heads, cfg.eps, cfg.prenorm)
-        t_single.append(time.perf_counter() - t0)
+    v = O.step(cfg, mw, txt, lat, np.array([wl.sigma]), wl.n_img, pos, dtype=np.float32)
+    sec = time.perf_counter() - t0
+    assert np.all(np.isfinite(v))
     D, F = cfg.hidden, cfg.mlp_hidden
-    blk_flops = 2.0 * S * D * (3 * D + 2 * F) + 2.0 * S * (D + F) * D + 4.0 * S * S * D
-    blocks_s = cfg.n_dual * t_dual + cfg.n_single * float(np.mean(t_single))
-    # embeddings and final layer at the blocks' FLOP rate
-    rest_flops = 2.0 * (wl.n_txt * cfg.txt_channels + (wl.n_img + wl.n_ref) * cfg.in_channels
-                        ) * D + 2.0 * wl.n_img * D * cfg.in_channels
-    rate = 3 * blk_flops / (t_dual + sum(t_single))
-    return blocks_s + rest_flops / rate, t_dual + sum(t_single), threads
+    blk = 2.0 * S * D * (3 * D + 2 * F) + 2.0 * S * (D + F) * D + 4.0 * S * S * D
+    flops = (cfg.n_dual + cfg.n_single) * blk + 2.0 * D * (
+        wl.n_txt * cfg.txt_channels + (wl.n_img + wl.n_ref) * cfg.in_channels
+        + wl.n_img * cfg.in_channels)
+    return sec, threads, flops
+
+
+def time_workload(dit, synth, torch, cfg, dw, wl, steps=10, warmup=2):
+    """Median / p95 ms of one step of workload wl (HIP events on the launch
+    stream), its algorithmic TFLOP/s, and the GEMM + attention fraction of
+    the bf16 peak from one per-kernel event pass."""
+    ins_b = [synth.step_inputs(cfg, wl, batch_row=b) for b in range(wl.batch)]
+    txt = dit.to_bf16_device(np.stack([i["txt"] for i in ins_b]))
+    lat = dit.to_bf16_device(np.stack([i["latents"] for i in ins_b]))
+    pos = dit.position_ids(wl.n_txt, wl.img_grid, wl.ref_grids)
+    cos, sin = dit.rope_tables(cfg, pos)
+    ws = dit.Workspace()
+    out = torch.empty((wl.batch, wl.n_img, cfg.in_channels), dtype=torch.float32, device="cuda")
+    sigma = [wl.sigma] * wl.batch
+
+    def one():
+        dit.step(cfg, dw, txt, lat, sigma, wl.n_img, cos, sin, ws=ws, out=out)
+
+    for _ in range(warmup):
+        one()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for e0, e1 in evs:
+        e0.record()
+        one()
+        e1.record()
+    torch.cuda.synchronize()
+    per = np.array([a.elapsed_time(b) for a, b in evs])
+    assert np.all(np.isfinite(out.cpu().numpy())), f"{wl.name}: non-finite output"
+    dit.profile_begin()
+    one()
+    k = dit.profile_end()
+    g, a = k["gemm"], k["attention"]
+    flops = sum(s["flops"] for s in k.values())
+    ga = (g["flops"] + a["flops"]) / ((g["total_ms"] + a["total_ms"]) * 1e-3) / 1e12
+    med = float(np.median(per))
+    res = {"batch": wl.batch, "seq_len": wl.seq, "n_img": wl.n_img, "n_ref": wl.n_ref,
+           "ms_median": round(med, 3), "ms_p95": round(float(np.percentile(per, 95)), 3),
+           "step_tflop": round(flops / 1e12, 3),
+           "step_tflops": round(flops / (med * 1e-3) / 1e12, 1),
+           "gemm_tflops": round(g["flops"] / (g["total_ms"] * 1e-3) / 1e12, 1),
+           "attention_tflops": round(a["flops"] / (a["total_ms"] * 1e-3) / 1e12, 1),
+           "gemm_attn_tflops": round(ga, 1),
+           "gemm_attn_frac_of_peak": round(ga / PEAK_BF16_TFLOPS, 4)}
+    del ws, out, txt, lat
+    torch.cuda.empty_cache()
+    return res
 
 
 def main():
@@ -175,6 +220,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--profile-steps", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra-workloads", action="store_true",
+                    help="skip the reference-image and batch-4 steps timed after the headline")
     ap.add_argument("--workload", default="step_1024px_s4608",
                     help="step workload to time (the default is the headline one; the others "
                          "are the reference-image, batch-4, three-reference and 512px "
@@ -209,7 +256,9 @@ def main():
 
     log("drawing weights and inputs")
     t0 = time.time()
-    dw = dit.ModelWeights(synth.ModelWeights(cfg, 0))
+    # blocks stay cached in host memory when the CPU baseline will reuse them
+    mw = synth.ModelWeights(cfg, 0, cache=not args.no_cpu_baseline)
+    dw = dit.ModelWeights(mw)
     ins_b = [synth.step_inputs(cfg, wl, batch_row=b) for b in range(B)]
     ins = ins_b[0]
     txt = dit.to_bf16_device(np.stack([i["txt"] for i in ins_b]))
@@ -320,18 +369,27 @@ def main():
     achieved = gemm_per_launch / gemm_avg_s / 1e12
     log("kernels: " + json.dumps(kern))
 
+    extra = None
+    if not args.no_extra_workloads:
+        extra = {}
+        for xw in (synth.W_STEP_1024_REF, synth.W_STEP_1920x1088_B4):
+            if xw is wl:
+                continue
+            log(f"workload {xw.name}")
+            extra[xw.name] = time_workload(dit, synth, torch, cfg, dw, xw)
+            log(f"  {json.dumps(extra[xw.name])}")
+
     cpu = None
     if not args.no_cpu_baseline:
-        log("CPU baseline: oracle, one dual and two single-stream blocks (float64)")
-        step_s, sample_s, threads = cpu_baseline(cfg, wl)
-        cpu_ms = step_s * 1000.0 * B  # batch rows are independent
-        cpu = {"value": round(cpu_ms, 1), "unit": "ms", "cores": threads, "kind": "oracle",
-               "sample": f"one dual-stream and two single-stream blocks of one sample of "
-                         f"{wl.name} (S={wl.seq}) in float64 NumPy, {sample_s:.1f} s; step = "
-                         f"{cfg.n_dual} x dual + {cfg.n_single} x mean single, plus the "
-                         f"embeddings and final layer at the blocks' FLOP rate"
-                         + (f", times {B} batch rows" if B > 1 else "")}
-        log(f"CPU baseline {cpu_ms:.0f} ms/step ({sample_s:.1f} s sample, {threads} threads)")
+        log("CPU baseline: the oracle in fp32 NumPy, one whole step after a one-block warm-up")
+        sec, threads, cflops = cpu_baseline(cfg, mw, wl)
+        cpu = {"value": round(sec * 1000.0, 1), "unit": "ms", "cores": threads, "kind": "oracle",
+               "gflops": round(cflops / sec / 1e9, 1),
+               "sample": f"one whole step (5 dual + 20 single blocks, embeddings, final "
+                         f"layer) of batch row 0 of {wl.name} (S={wl.seq}), oracle in fp32 "
+                         f"NumPy, timed once after a one-block warm-up"
+                         + (f"; the GPU step covers {B} such rows" if B > 1 else "")}
+        log(f"CPU baseline {sec:.1f} s/step ({threads} threads, {cpu['gflops']} GFLOP/s)")
 
     if args.copy_calibration:
         # a fill (writes COPY_CAL_BYTES) and elementwise negations (read and
@@ -368,6 +426,7 @@ def main():
                      "alg_bytes_per_launch": round(g["bytes"] / g["launches"]),
                      "per_launch_flop": gemm_per_launch, "avg_launch_us": gemm_avg_s * 1e6},
         "kernels": kern,
+        "workloads": extra,
         "denoise_loop": den,
         "cpu_baseline": cpu,
     }

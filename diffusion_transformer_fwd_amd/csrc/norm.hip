@@ -10,9 +10,9 @@
 //     rows_copy: the embedded text rows the loop keeps across steps
 //
 // The maths each one follows is stated at its kernel; the pages it comes
-// from are "flux2-klein-p100a" (Caveats: modulation global per step) and
-// "tt_flux2_klein - Python reference" (Things that are easy to get wrong:
-// RoPE of 32 dims per axis, theta 2000, adjacent pairs).
+// from are "flux2-klein-p100a" (Caveats: one modulation result per step for
+// every block) and "tt_flux2_klein - Python reference" (Things that are easy
+// to get wrong: RoPE of 32 dims per axis, theta 2000, adjacent pairs).
 #include <math.h>
 
 #include "common.hpp"

@@ -7,12 +7,12 @@
  *     steps is one DiT call (distilled, no CFG); the scheduler stays on the
  *     host (card header). Caveats: all 512 padded text rows enter the DiT
  *     unmasked, as the concatenation of three encoder layers ([512, 7680]);
- *     modulation is global per step.
+ *     one modulation result per step serves every block.
  *   - "tt_flux2_klein - Python reference", Modules: the DiT is 5 dual-stream
  *     blocks then 20 single-stream blocks; host maths builds token ids and
- *     RoPE. "Things that are easy to get wrong": modulation global per step,
- *     unmasked text rows, RoPE of 32 dims per axis with theta 2000 on
- *     adjacent pairs, reference image i at t = 10 + 10 i.
+ *     RoPE. "Things that are easy to get wrong": one modulation per step
+ *     for all blocks, unmasked text rows, RoPE of 32 dims per axis with
+ *     theta 2000 on adjacent pairs, reference image i at t = 10 + 10 i.
  *   - Readings where the pages are open (hidden 3072 = 24 heads x 128,
  *     SwiGLU MLP of ratio 3, QK-RMSNorm before RoPE, no biases, AdaLN with
  *     (1 + scale) and shift, gated residuals, RMS pre-norm by default) are

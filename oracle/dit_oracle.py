@@ -13,7 +13,8 @@ Sources (the pages this follows):
   [card]   "flux2-klein-p100a" model card: header (scheduler on the host,
            DiT on the card), the Tasks/Size/Steps/References table, and
            "Caveats" (all 512 padded text rows, no mask; layers 9/18/27
-           concatenated to [512, 7680]; modulation global per step).
+           concatenated to [512, 7680]; one modulation result per step for
+           all blocks).
   [py]     "tt_flux2_klein - Python reference": "Lower-level entry points"
            (encode -> [512, 7680]), "Modules" (host.py: token ids, RoPE;
            tt_dit.py: 5 dual-stream + 20 single-stream blocks) and "Things
@@ -231,8 +232,9 @@ def modulation(gw: Dict[str, np.ndarray], sigma: np.ndarray, channels: int = 256
                dtype=np.float64) -> Dict[str, np.ndarray]:
     """Per-step AdaLN parameters, computed once and shared by every block.
 
-    [card] "Caveats" and [py] "Things that are easy to get wrong": modulation
-    is global per step, not per block. Reading: temb = W_out SiLU(W_in e(sigma)),
+    [card] "Caveats" and [py] "Things that are easy to get wrong": one set of
+    AdaLN vectors per step, which every block reuses (no block computes its
+    own). Reading: temb = W_out SiLU(W_in e(sigma)),
     m = SiLU(temb), then four projections of m:
       dual_img [B, 6, D] and dual_txt [B, 6, D]: shift1, scale1, gate1,
         shift2, scale2, gate2 (attention branch, then MLP branch);

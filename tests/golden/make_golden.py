@@ -3,13 +3,19 @@
 Calls only ``oracle/`` (and the seeded input generator). The full step mixes
 every row through attention in every block, so a sampled output cannot be
 computed on its own; the oracle runs the whole step once here (float64, tens
-of minutes on a few cores) and a fixed subset of output rows is stored:
-every ``stride``-th image token of every batch row, plus the last one, all
-channels.
+of minutes on a few cores) and stores the velocity:
+
+* the whole tensor v [B, n_img, C_in] (rounded to float32, far below the
+  comparison tolerance) for the single-sample workloads — the 1024x1024 step,
+  the step with one reference, the 848x624 step with three references and
+  the 512x512 step with one reference — so every output element is compared;
+* every 32nd image-token row (plus the last) for the 1920x1088 batch-4 step,
+  whose whole tensor would be 17 MB; there the whole-tensor check is the sum
+  of squares per batch row.
 
 Usage: python tests/golden/make_golden.py [step_1024px_s4608 ...]
-Output: tests/golden/<workload>.npz with rows, v (float64 [B, n_rows, C_in]),
-        and the oracle's full-tensor sum of squares per batch row.
+Output: tests/golden/<workload>.npz with rows (int64), v ([B, len(rows), C]),
+        and the oracle's full-tensor sum of squares and max-abs per batch row.
 """
 import os
 import sys
@@ -23,12 +29,13 @@ sys.path.insert(0, ROOT)
 from oracle import dit_oracle as O  # noqa: E402
 from diffusion_transformer_fwd_amd import synth  # noqa: E402
 
+# workload -> row stride of the stored velocity (1 = whole tensor, stored fp32)
 WORKLOADS = {
-    synth.W_STEP_1024.name: (synth.W_STEP_1024, 8),
-    synth.W_STEP_1024_REF.name: (synth.W_STEP_1024_REF, 8),
+    synth.W_STEP_1024.name: (synth.W_STEP_1024, 1),
+    synth.W_STEP_1024_REF.name: (synth.W_STEP_1024_REF, 1),
     synth.W_STEP_1920x1088_B4.name: (synth.W_STEP_1920x1088_B4, 32),
-    synth.W_STEP_848x624_3REF.name: (synth.W_STEP_848x624_3REF, 8),
-    synth.W_STEP_512_REF.name: (synth.W_STEP_512_REF, 4),
+    synth.W_STEP_848x624_3REF.name: (synth.W_STEP_848x624_3REF, 1),
+    synth.W_STEP_512_REF.name: (synth.W_STEP_512_REF, 1),
 }
 
 
@@ -55,8 +62,11 @@ def run(name: str) -> None:
 
     v = O.step(cfg, weights, txt, lat, sigma, wl.n_img, pos, on_block=tick)
     rows = sample_rows(wl.n_img, stride)
+    vs = v[:, rows]
+    if stride == 1:
+        vs = vs.astype(np.float32)
     out = os.path.join(os.path.dirname(os.path.abspath(__file__)), f"{name}.npz")
-    np.savez(out, rows=rows, v=v[:, rows], sumsq=(v * v).sum(axis=(1, 2)),
+    np.savez(out, rows=rows, v=vs, sumsq=(v * v).sum(axis=(1, 2)),
              maxabs=np.abs(v).max(axis=(1, 2)), seconds=time.time() - t0)
     print(f"wrote {out} in {time.time() - t0:.0f}s", flush=True)
 

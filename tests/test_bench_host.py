@@ -74,11 +74,15 @@ def test_more_than_one_gpu_is_refused():
     assert "one GPU" in r.stderr
 
 
-def test_cpu_baseline_extrapolates_from_three_blocks():
+def test_cpu_baseline_times_one_whole_fp32_step():
     cfg = synth.DitConfig(hidden=256, heads=2, head_dim=128, mlp_hidden=768, n_dual=2,
                           n_single=6, in_channels=128, txt_channels=256)
     wl = synth.Workload("s", 1, 16, (4, 4), (), 0.75)
-    step_s, sample_s, threads = bench.cpu_baseline(cfg, wl)
-    assert threads >= 1 and sample_s > 0
-    # 8 blocks extrapolated from 3 timed ones, plus a little for the embeddings
-    assert step_s > sample_s * 8 / 3 * 0.5
+    mw = synth.ModelWeights(cfg, 0, cache=True)
+    sec, threads, flops = bench.cpu_baseline(cfg, mw, wl)
+    assert threads >= 1 and sec > 0
+    # algorithmic FLOPs of the whole step: 8 blocks + embeddings + final layer
+    S, D, F = wl.seq, cfg.hidden, cfg.mlp_hidden
+    blk = 2 * S * D * (3 * D + 2 * F) + 2 * S * (D + F) * D + 4 * S * S * D
+    rest = 2 * D * (16 * 256 + 16 * 128 + 16 * 128)
+    assert flops == 8 * blk + rest

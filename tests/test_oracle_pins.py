@@ -376,7 +376,9 @@ def test_batch_rows_independent():
 
 def test_step_uses_one_global_modulation():
     # The step equals its blocks composed by hand with the single modulation
-    # result computed from sigma (global per step, not per block).
+    # result computed from sigma: one set of AdaLN vectors per step, shared by
+    # every block ("tt_flux2_klein - Python reference", Things that are easy
+    # to get wrong).
     cfg = tiny_cfg(n_dual=2, n_single=2)
     wl = synth.Workload("t", 1, 3, (2, 2), (), 0.6)
     pos = O.position_ids(wl.n_txt, wl.img_grid)
