@@ -197,6 +197,40 @@ DenoiseLayout denoise_layout(const dit_config& c, int64_t B, int64_t S) {
   return L;
 }
 
+// ---------------------------------------------------------------- fixed scratch
+// Scratch of dit_modulation_forward_noalloc: the modulation's intermediate
+// vectors (features e, hidden t1, SiLU input m; mod_layout) for up to
+// DIT_MAX_BATCH rows at the largest time_channels and hidden that
+// check_config accepts (4096 each), plus the alignment slack of its three
+// regions. Every GPU the library runs on holds one copy until the process
+// ends. In host code `scratch` names a host-side stand-in: kernels get the
+// device address from scratch_address(), never the array's name.
+constexpr size_t kScratchBytes = (size_t)DIT_MAX_BATCH * (4096 + 2 * 4096) * 4 + 3 * kAlign;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+static_assert(kScratchBytes == DIT_NOALLOC_SCRATCH_BYTES, "dit.h states the scratch size");
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+int scratch_address(void** out) {
+  int dev = -1;
+  DIT_TRY(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(DIT_E_UNSUPPORTED, "device %d: at most %d devices are supported", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    DIT_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p) return fail(DIT_E_HIP, "hipGetSymbolAddress returned NULL for the scratch array");
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return DIT_OK;
+}
+
 // ---------------------------------------------------------------- validation
 
 int check_config(const dit_config* c) {
@@ -951,6 +985,24 @@ int dit_modulation_forward(const dit_config* cfg, const dit_model_weights* w,
   DIT_CHECK(check_sigmas(sigma_host, B));
   DIT_CHECK(check_ptr(mod_dev, "mod"));
   DIT_CHECK(check_ws(ws, ws_bytes, mod_layout(*cfg, B).total));
+  return launch_modulation(*cfg, *w, sigma_host, B, mod_dev, ws,
+                           reinterpret_cast<hipStream_t>(stream));
+}
+
+int dit_modulation_forward_noalloc(const dit_config* cfg, const dit_model_weights* w,
+                                   const float* sigma_host, int32_t B, float* mod_dev,
+                                   dit_stream_t stream) {
+  DIT_CHECK(check_config(cfg));
+  if (B < 1 || B > DIT_MAX_BATCH) return fail(DIT_E_SHAPE, "B %d out of range", B);
+  DIT_CHECK(check_model_weights(*cfg, w, false));
+  DIT_CHECK(check_sigmas(sigma_host, B));
+  DIT_CHECK(check_ptr(mod_dev, "mod"));
+  const size_t need = mod_layout(*cfg, B).total;
+  if (need > kScratchBytes)
+    return fail(DIT_E_UNSUPPORTED, "modulation scratch of %zu bytes exceeds the fixed %zu",
+                need, kScratchBytes);
+  void* ws = nullptr;
+  DIT_CHECK(scratch_address(&ws));
   return launch_modulation(*cfg, *w, sigma_host, B, mod_dev, ws,
                            reinterpret_cast<hipStream_t>(stream));
 }

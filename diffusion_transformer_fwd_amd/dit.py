@@ -25,7 +25,8 @@ MAX_BATCH = 64
 EXPORTS = ("dit_position_ids", "dit_workspace_bytes", "dit_status_string", "dit_last_error",
            "dit_config_check", "dit_rope_tables_build", "dit_modulation_forward",
            "dit_dual_block_forward", "dit_single_block_forward", "dit_step_forward",
-           "dit_denoise_forward", "dit_profile_begin", "dit_profile_end")
+           "dit_denoise_forward", "dit_profile_begin", "dit_profile_end",
+           "dit_modulation_forward_noalloc")
 (K_GEMM, K_ATTENTION, K_MODNORM, K_QKV_PAD, K_GEMV, K_ROPE_TABLES, K_TIME, K_SPLIT_SUM, K_LATENT,
  K_COUNT) = range(10)
 KERNEL_NAMES = ("gemm", "attention", "modnorm", "qkv_pad", "gemv", "rope_tables", "time_features",
@@ -100,6 +101,8 @@ def lib() -> C.CDLL:
     L.dit_rope_tables_build.argtypes = [pc, vp, i64, vp, vp, vp]
     L.dit_modulation_forward.restype = C.c_int
     L.dit_modulation_forward.argtypes = [pc, C.POINTER(ModelWeightsC), vp, i32, vp, vp, sz, vp]
+    L.dit_modulation_forward_noalloc.restype = C.c_int
+    L.dit_modulation_forward_noalloc.argtypes = [pc, C.POINTER(ModelWeightsC), vp, i32, vp, vp]
     L.dit_dual_block_forward.restype = C.c_int
     L.dit_dual_block_forward.argtypes = [pc, C.POINTER(DualWeightsC), vp, i32, i64, i64, vp, vp,
                                          i64, vp, vp, vp, sz, vp]
@@ -295,6 +298,20 @@ def modulation(cfg: synth.DitConfig, w: ModelWeights, sigma: Sequence[float],
     _check(lib().dit_modulation_forward(C.byref(c), C.byref(w.c), sig.ctypes.data, B,
                                         mod.data_ptr(), p, n, _stream()))
     return mod
+
+
+def modulation_noalloc(cfg: synth.DitConfig, w: ModelWeights, sigma: Sequence[float], out=None):
+    """mod fp32 [B, 17, D] through the entry point that takes no workspace
+    (its scratch is the library's fixed device array); out may be given."""
+    torch = _torch()
+    B = len(sigma)
+    if out is None:
+        out = torch.empty((B, MOD_ROWS, cfg.hidden), dtype=torch.float32, device="cuda")
+    sig = np.ascontiguousarray(sigma, dtype=np.float32)
+    c = config(cfg)
+    _check(lib().dit_modulation_forward_noalloc(C.byref(c), C.byref(w.c), sig.ctypes.data, B,
+                                                out.data_ptr(), _stream()))
+    return out
 
 
 def dual_block(cfg: synth.DitConfig, w: DualWeights, x, n_txt: int, mod, cos, sin,

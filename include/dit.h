@@ -184,6 +184,25 @@ int dit_modulation_forward(const dit_config* cfg, const dit_model_weights* w,
                            const float* sigma_host, int32_t B, float* mod_dev,
                            void* ws, size_t ws_bytes, dit_stream_t stream);
 
+/* dit_modulation_forward without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, serving loops
+ * and harnesses that forbid allocation). The intermediate vectors live in a
+ * fixed device array inside the library of DIT_NOALLOC_SCRATCH_BYTES (3 MiB
+ * and 768 bytes: DIT_MAX_BATCH rows at time_channels and hidden up to 4096),
+ * which each GPU the library runs on holds until the process ends; its
+ * address is looked up on the first call on each device (the current device
+ * is the one the stream belongs to). The call allocates nothing. Every call
+ * on one GPU shares that array and leaves its last contents there (every
+ * value is written before it is read, so nothing needs clearing): calls that
+ * overlap on one GPU (different streams, or threads) race and must be
+ * serialised by the caller. Returns DIT_E_UNSUPPORTED if B rows of this
+ * configuration need more scratch than the array holds; other arguments and
+ * results as for dit_modulation_forward. */
+enum { DIT_NOALLOC_SCRATCH_BYTES = 64 * (4096 + 2 * 4096) * 4 + 3 * 256 };
+int dit_modulation_forward_noalloc(const dit_config* cfg, const dit_model_weights* w,
+                                   const float* sigma_host, int32_t B, float* mod_dev,
+                                   dit_stream_t stream);
+
 /* One dual-stream block, in place on x ("tt_flux2_klein - Python reference",
  * Modules: the first 5 blocks). x: dev fp32 [B, S, D]. Text rows [0, n_txt)
  * use stream-0 weights and mod_txt; image+reference rows [n_txt, S) use

@@ -32,7 +32,7 @@ def header_functions():
 
 def test_exports_every_declared_function(L):
     names = header_functions()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     assert sorted(dit.EXPORTS) == names
     for n in names:
         assert hasattr(L, n), f"{n} not exported"
@@ -243,3 +243,27 @@ def test_block_validation_errors(L):
     assert r(C.byref(c), None, 10, FAKE, FAKE, None) == dit.DIT_E_NULL
     assert r(C.byref(c), FAKE, -1, FAKE, FAKE, None) == dit.DIT_E_SHAPE
     assert r(C.byref(c), FAKE, 0, FAKE, FAKE, None) == dit.DIT_OK  # nothing to do
+
+
+def test_modulation_noalloc_validation_errors(L):
+    # every rejection happens before the scratch lookup and the first launch
+    cfg = synth.FLUX2_KLEIN
+    c = dit.config(cfg)
+    m, _d, _s = _fake_model(cfg)
+    f = L.dit_modulation_forward_noalloc
+
+    def call(sig, B, mod=FAKE, model=m):
+        s = np.ascontiguousarray(sig, np.float32)
+        return f(C.byref(c), C.byref(model) if model is not None else None, s.ctypes.data, B,
+                 mod, None)
+
+    assert call([0.5], 0) == dit.DIT_E_SHAPE
+    assert call([0.5] * 65, 65) == dit.DIT_E_SHAPE
+    assert call([float("nan")], 1) == dit.DIT_E_VALUE
+    assert call([0.5], 1, mod=0) == dit.DIT_E_NULL
+    assert call([0.5], 1, mod=FAKE + 4) == dit.DIT_E_SHAPE
+    assert call([0.5], 1, model=None) == dit.DIT_E_NULL
+    m.t_in = 0
+    assert call([0.5], 1) == dit.DIT_E_NULL
+    assert "t_in" in dit.last_error()
+    assert f(C.byref(c), C.byref(m), None, 1, FAKE, None) == dit.DIT_E_NULL
