@@ -6,69 +6,86 @@
 // the final projection ("tt_flux2_klein - Python reference", Modules: the
 // DiT's 5 dual + 20 single blocks; the block maths is stated in dit.h).
 //
-// Design (one workgroup = 8 waves = 512 threads, one 256 x 256 output tile):
+// Design (one workgroup = 8 waves = 512 threads, one output tile of 256 or
+// 384 rows by 256 columns):
 //  * A [M, K] and W [N, K] are both K-contiguous, so one 64-wide K slice of
 //    each tile is a set of 128-byte row segments. Slices go from HBM/L2
 //    straight into LDS with buffer loads that write LDS (no register
 //    staging, no LDS store instructions), their 16-byte chunks XOR-swizzled
 //    by row so that MFMA fragment reads are free of bank conflicts. Two LDS
-//    stages (128 KiB of the CU's 160 KiB), one barrier per slice; fragments
-//    for the next 16-wide k-step are read while the current one's MFMAs run.
-//    A CU pulls about 36 bytes per clock from L2 into LDS this way, close to
-//    the 32 B/clk a 256 x 256 tile consumes at the full MFMA rate, so the
-//    loads must overlap the math: the tile runs 8 waves (two per SIMD) and
-//    only the upper four issue loads, while the lower four keep issuing
-//    MFMAs.
-//  * Each wave owns a 64 x 128 sub-tile (4 x 2 waves) as 2 x 4 blocks of
-//    v_mfma_f32_32x32x16_bf16 (fp32 accumulators, 128 per lane). The weight
-//    fragment is the MFMA's first operand and the activation fragment the
-//    second, so each lane ends up holding one output row and runs of four
-//    consecutive output columns: epilogue stores are 8-byte (bf16) or
-//    16-byte (fp32) vectors.
+//    stages, one barrier per slice; fragments for the next 16-wide k-step
+//    are read while the current one's MFMAs run.
+//  * What paces a slice is the stream of slice bytes from L2 into the CU
+//    (about 23 bytes per clock under full MFMA load), not the matrix cores:
+//    a 256 x 256 tile needs 32 B/clk to keep them busy. A 384-row tile does
+//    1.5x the MFMA work of a 256-row one for 1.25x the bytes (80 KiB per
+//    slice; the two stages fill the 160 KiB LDS), so launches use 384-row
+//    tiles wherever the rounds of tiles over the CUs allow it.
+//  * Loads overlap the math: the tile runs 8 waves (two per SIMD) and only
+//    the upper four issue loads, while the lower four keep issuing MFMAs
+//    (a wave that issues loads stalls while the CU's load queue is full).
+//  * Each wave owns a (32 FM) x 128 sub-tile (4 x 2 waves, FM = 2 or 3) as
+//    FM x 4 blocks of v_mfma_f32_32x32x16_bf16 (fp32 accumulators, 16 FM
+//    per lane per block column). The weight fragment is the MFMA's first
+//    operand and the activation fragment the second, so each lane ends up
+//    holding one output row and runs of four consecutive output columns.
 //  * Epilogues: bf16 store; SwiGLU (each wave's column half is gate rows and
 //    the other half the matching up rows, so SiLU(g) * u is lane-local);
 //    gated residual x += gate[b] * acc on the fp32 residual; fp32 store; and
 //    QK-RMSNorm + RoPE straight into the attention operands (a wave's 128
 //    columns are one head), so the fused projection never round-trips HBM.
-//    Output rows go through a (segment length, stride, offset) map, so
-//    stream-major operands scatter back into x[B, S, D] in place.
+//    Results are staged through LDS in passes of whole rows and leave 16
+//    bytes per lane. Output rows go through a (segment length, stride,
+//    offset) map, so stream-major operands scatter back into x[B, S, D].
 //  * Up to eight independent problems share one launch (text + image
 //    streams, the single block's QKV part + SwiGLU part, or the K chunks of
-//    a split contraction), so the small 512-row text problem fills gaps
-//    instead of taking its own launch.
-//  * Launches without the SwiGLU / QKV epilogues may use 256 x 224 tiles
+//    a split contraction); each problem has its own tile height.
+//  * Launches without the SwiGLU / QKV epilogues may use 224-wide tiles
 //    when that takes fewer rounds of tiles over the CUs (the N = 3072
 //    projections at 4608 rows: 252 tiles in one round instead of 216 full
 //    ones leaving 40 CUs idle).
-//  * Tile order: launch index -> XCD-contiguous logical index -> groups of
-//    7 row tiles walked column by column, so co-resident tiles on one XCD
-//    share A and W panels in its L2.
+//  * Tile order: every problem's tiles are dealt to the 8 XCDs in
+//    contiguous ranges (tile_map.hpp), so each XCD runs the same mix of
+//    tile sizes, larger first, and co-resident tiles on one XCD share A and
+//    W panels in its L2; inside a problem, groups of 7 row tiles are walked
+//    column by column.
 //  * The accumulation order of an output element depends only on K, never
-//    on M, the tile width or the tile position, so a batch row's results
+//    on M, the tile shape or the tile position (every tile runs the same
+//    MFMA over the same 16-wide k-steps in order), so a batch row's results
 //    are bitwise the same whatever else is in the batch.
+#include <algorithm>
+#include <cstdlib>
+#include <map>
+#include <mutex>
+#include <tuple>
+#include <vector>
+
 #include "common.hpp"
 #include "kernels.hpp"
+#include "tile_map.hpp"
 
 namespace dit {
 namespace {
 
-constexpr int BM = kGemmBM, BN = kGemmBN, BK = kGemmBK;
+constexpr int BN = kGemmBN, BK = kGemmBK;
 constexpr int NT = 512;                       // 8 waves, two per SIMD
-constexpr int WTM = 64, WTN = 128;            // wave tile: 4 x 2 waves
-constexpr int FM = WTM / 32, FN = WTN / 32;
+constexpr int WTN = 128, FN = WTN / 32;       // wave tile columns; 4 x 2 waves
 constexpr int ROW_U = BK / 8;                 // 16-byte units per LDS row
-constexpr int STAGE_U = (BM + BN) * ROW_U;    // 16-byte units per stage
+constexpr int MAX_BM = 384;
+constexpr int LDS_U = 2 * (MAX_BM + BN) * ROW_U;     // two stages of the tallest tile
+constexpr int RS_BYTE = LDS_U * 16 - 2 * MAX_BM * 4; // epilogue row scales, [2][BM]
 
-static_assert(NT == 512 && BM == 256 && BN == 256, "loader assumes 8 waves x 32 rows");
+static_assert(NT == 512 && BN == 256 && BK == 64, "loader assumes 8 waves x 32 rows");
+static_assert(LDS_U * 16 == 160 * 1024, "two 384-row stages fill the LDS");
 
 // Chunk swizzle by row: distinct for 8 consecutive rows and for the 8 rows of
 // either parity among 16 consecutive rows.
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
 // Tile order of a problem: groups of GROUP row tiles, row tile fastest, so the
-// 32 tiles an XCD runs at once span about 7 row tiles x 4-5 column tiles of
-// A and W panels in its L2. 7 measured best of 4..12 (0.5 % per step against
-// 8 on two boxes, 6 and 5 in between).
+// tiles an XCD runs at once span a few row tiles x a few column tiles of A and
+// W panels in its L2. 7 measured best of 4..12 (0.5 % per step against 8 on
+// two boxes, 6 and 5 in between).
 __device__ __forceinline__ void tile_coords(int local, int tiles_m, int tiles_n,
                                             int& tm, int& tn) {
   constexpr int GROUP = 7;
@@ -88,115 +105,126 @@ struct count_t {
   static constexpr int value = V;
 };
 
-// BNT: output columns per tile, 256 or 224 (BF16 / F32 / RESID epilogues
-// only). At 224 the N = 1 waves run three 32-column blocks instead of four
-// and W tile rows 224..255 are never loaded; per output element nothing
-// changes (same MFMA, same k order), so the width may be picked per launch.
-// EPI_QKV for one wave tile (64 rows x 128 columns = one head of q, k or v):
-// a row's 128 accumulators sit in lanes l and l ^ 32 (64 each), so the RMS
-// is lane-local plus one cross-half exchange; each lane's runs of 4 columns
-// hold two whole rotation pairs.
-template <int BNT>
-__global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const GemmBatch args) {
-  // two K-slice stages, then (EPI_QKV) 1 / rms of each tile row per wave column
-  __shared__ u32x4 lds[2 * STAGE_U + 2 * BM * 4 / 16];
-  float (*const row_scale)[BM] = reinterpret_cast<float (*)[BM]>(lds + 2 * STAGE_U);
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
+// One output tile of problem P (index pi of the launch): BM = 128 FM rows,
+// BNT columns (256, or 224 for the BF16 / F32 / RESID epilogues only: the
+// N = 1 waves then run three 32-column blocks instead of four and W tile
+// rows 224..255 are never loaded; per output element nothing changes).
+// EPI_QKV for one wave tile (32 FM rows x 128 columns = one head of q, k or
+// v): a row's 128 accumulators sit in lanes l and l ^ 32 (64 each), so the
+// RMS is lane-local plus one cross-half exchange; each lane's runs of 4
+// columns hold two whole rotation pairs.
+// FAM: the epilogue family of the launch, FAM_F32 (EPI_F32 / EPI_RESID) or
+// FAM_BF16 (EPI_BF16 / EPI_SWIGLU / EPI_QKV); one kernel per family keeps the
+// register allocation of each within the budget at 384 rows.
+enum { FAM_BF16 = 0, FAM_F32 = 1 };
+
+template <int BNT, int FM, int FAM>
+__device__ __forceinline__ void gemm_tile(const GemmBatch& args, const GemmProblem& P, int pi,
+                                          int local, u32x4* lds) {
+  constexpr int BM = 128 * FM, WTM = 32 * FM;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int L = xcd_remap(blockIdx.x, gridDim.x);
-  int pi = 0;
-#pragma unroll
-  for (int i = 1; i < kMaxGemmProblems; ++i)
-    if (i < args.count && L >= args.p[i].tile_begin) pi = i;
-  pi = __builtin_amdgcn_readfirstlane(pi);
-  // Constant-index copies keep every field in scalar registers.
-  GemmProblem P;
-  switch (pi) {
-    case 0: P = args.p[0]; break;
-    case 1: P = args.p[1]; break;
-    case 2: P = args.p[2]; break;
-    case 3: P = args.p[3]; break;
-    case 4: P = args.p[4]; break;
-    case 5: P = args.p[5]; break;
-    case 6: P = args.p[6]; break;
-    default: P = args.p[7]; break;
-  }
   const int M = P.M, N = P.N, K = P.K, epi = P.epi;
   int tm, tn;
-  tile_coords(L - P.tile_begin, P.tiles_m, P.tiles_n, tm, tn);
+  tile_coords(local, P.tiles_m, P.tiles_n, tm, tn);
   const int m0 = tm * BM;
 
   // ---- global -> LDS: buffer loads that write LDS directly (no register
-  // staging). Waves 4-7 issue every load of a slice: wave w fills tile rows
-  // 32 w' .. 32 w' + 31 of A and of W for w' = w and w' = w - 4, four
-  // instructions of 8 rows each per block of 32 rows. Waves 0-3 issue none,
-  // so their MFMAs never queue behind a load issue that waits for room in the
-  // CU's vector-memory queue, and each SIMD (one wave of either half) keeps
-  // its matrix core busy. A lane writes physical chunk lane % 8 of its row,
-  // so it fetches logical chunk (lane % 8) ^ swz(row). Rows past the end of
-  // A or W read as zero.
+  // staging). Waves 4-7 issue every load of a slice: loader lw = wave - 4
+  // fills the 32-row blocks lw + 4 h of A (h < FM) and of W (h < 2), four
+  // instructions of 8 rows each per block. Waves 0-3 issue none, so their
+  // MFMAs never queue behind a load issue that waits for room in the CU's
+  // vector-memory queue, and each SIMD (one wave of either half) keeps its
+  // matrix core busy. A lane writes physical chunk lane % 8 of its row, so
+  // it fetches logical chunk (lane % 8) ^ swz(row). Rows past the end of A
+  // or W read as zero.
   const int w_rows = epi == EPI_SWIGLU ? 2 * N : N;
   const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(P.A, clamp_u32((int64_t)M * P.lda * 2));
   const __amdgpu_buffer_rsrc_t w_rsrc = make_rsrc(P.W, clamp_u32((int64_t)w_rows * P.ldw * 2));
   const int lr = lane >> 3, lp = lane & 7;
   const bool loader = wave >= 4;
-  uint32_t a_off[2][2], w_off[2][2];  // [row block h: w' = wave - 4 h][row parity]
+  const int lw = wave - 4;
+  // lane part of a load's byte offset (row lr of an 8-row group, logical
+  // chunk (lane % 8) ^ swz(row) of the row, which depends on the row's
+  // parity); everything else is wave-uniform and goes to the scalar offset
+  uint32_t a_lane[2], w_lane[2];
 #pragma unroll
-  for (int h = 0; h < 2; ++h)
-#pragma unroll
-    for (int par = 0; par < 2; ++par) {
-      const int wb = wave - 4 * h;  // row block 32 wb .. 32 wb + 31
-      const int c = lp ^ (lr ^ par);
-      a_off[h][par] = (uint32_t)(((int64_t)(m0 + 32 * wb + lr) * P.lda + c * 8) * 2);
-      // SwiGLU: tile row j = 32 wb + r belongs to wave column group j / 128 =
-      // wb / 4; rows with (wb % 4) < 2 are gate rows, the others the matching
-      // up rows (N further down), so each wave's 128 output columns hold gate
-      // and up values of the same 64 activations
-      int64_t wrow;
-      if (epi == EPI_SWIGLU)
-        wrow = tn * (BN / 2) + (wb >> 2) * 64 + 32 * (wb & 1) + lr + (((wb & 3) >= 2) ? N : 0);
-      else
-        wrow = (int64_t)tn * BNT + 32 * wb + lr;
-      w_off[h][par] = (uint32_t)((wrow * P.ldw + c * 8) * 2);
-    }
-  const uint32_t a_istep = (uint32_t)(8 * P.lda * 2), w_istep = (uint32_t)(8 * P.ldw * 2);
+  for (int par = 0; par < 2; ++par) {
+    const int c = lp ^ (lr ^ par);
+    a_lane[par] = (uint32_t)((lr * P.lda + c * 8) * 2);
+    w_lane[par] = (uint32_t)((lr * P.ldw + c * 8) * 2);
+  }
+  // first row of W tile block wb (32 rows): SwiGLU tile row j = 32 wb + r
+  // belongs to wave column group j / 128 = wb / 4; rows with (wb % 4) < 2 are
+  // gate rows, the others the matching up rows (N further down), so each
+  // wave's 128 output columns hold gate and up values of the same 64
+  // activations
+  auto w_row0 = [&](int wb) -> int64_t {
+    if (epi == EPI_SWIGLU)
+      return (int64_t)tn * (BN / 2) + (wb >> 2) * 64 + 32 * (wb & 1) + (((wb & 3) >= 2) ? N : 0);
+    return (int64_t)tn * BNT + 32 * wb;
+  };
+  const uint32_t a_row_b = (uint32_t)(P.lda * 2), w_row_b = (uint32_t)(P.ldw * 2);
   auto dma = [&](int kt, int stage) {
     if (!loader) return;
     const uint32_t ko = (uint32_t)kt * (BK * 2);
+    u32x4* const sa = lds + stage * (BM * ROW_U);
+    u32x4* const sw = lds + 2 * BM * ROW_U + stage * (BN * ROW_U);
+    // The whole byte offset goes in the vector offset, which the buffer's
+    // range check covers (rows past the operand read as zero); its
+    // wave-uniform part is a running sum, 8 rows per instruction.
+#pragma unroll
+    for (int h = 0; h < FM; ++h) {
+      const int row = 32 * (lw + 4 * h);  // first tile row of the block
+      uint32_t so = __builtin_amdgcn_readfirstlane((uint32_t)(m0 + row) * a_row_b + ko);
+#pragma unroll
+      for (int i = 0; i < 4; ++i, so += 8 * a_row_b)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_ptr_t)(sa + (row + 8 * i) * ROW_U),
+                                                 16, a_lane[i & 1] + so, 0, 0, 0);
+    }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      u32x4* base = lds + stage * STAGE_U + (wave - 4 * h) * 32 * ROW_U;
+      const int wb = lw + 4 * h;
+      if (BNT == 224 && wb == 7) continue;  // W rows 224..255: not in the tile
+      uint32_t so = __builtin_amdgcn_readfirstlane((uint32_t)w_row0(wb) * w_row_b + ko);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_ptr_t)(base + i * 64), 16,
-                                                 a_off[h][i & 1] + i * a_istep + ko, 0, 0, 0);
-      if (BNT == 224 && wave - 4 * h == 7) continue;  // W rows 224..255: not in the tile
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rsrc, (lds_ptr_t)(base + BM * ROW_U + i * 64),
-                                                 16, w_off[h][i & 1] + i * w_istep + ko, 0, 0, 0);
+      for (int i = 0; i < 4; ++i, so += 8 * w_row_b)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rsrc,
+                                                 (lds_ptr_t)(sw + (32 * wb + 8 * i) * ROW_U), 16,
+                                                 w_lane[i & 1] + so, 0, 0, 0);
     }
   };
 
-  // ---- MFMA fragments, double-buffered across k-steps
+  // ---- MFMA fragments. 256-row tiles double-buffer both operands across
+  // k-steps; 384-row tiles (192 accumulators per lane) double-buffer A only
+  // and refetch each W fragment right after its last MFMA of the k-step.
+  constexpr int WB = FM == 2 ? 2 : 1;  // W fragment buffers
   const int fr = lane & 31, fg = lane >> 5;
   const int wm = wave & 3, wn = wave >> 2;
+  // LDS: A stage 0 | A stage 1 | W stage 0 | W stage 1 (rows of 8 units),
+  // so one base per operand and k-step reaches either stage and every row
+  // block through the read's immediate offset
   const int a_rd = (wm * WTM + fr) * ROW_U;
-  const int w_rd = BM * ROW_U + (wn * WTN + fr) * ROW_U;
+  const int w_rd = 2 * BM * ROW_U + (wn * WTN + fr) * ROW_U;
   const int sfr = swz(fr);
-  bf16x8 af[2][FM], wf[2][FN];
+  bf16x8 af[2][FM], wf[WB][FN];
   // FNA (a compile-time count): the wave's active 32-column blocks
   auto fload = [&](auto fna, int stage, int s, int buf) {
     constexpr int FNA = decltype(fna)::value;
-    const u32x4* st = lds + stage * STAGE_U;
+    const u32x4* sa = lds + stage * (BM * ROW_U);
+    const u32x4* sw = lds + stage * (BN * ROW_U);
     const int ch = (2 * s + fg) ^ sfr;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
-      af[buf][i] = __builtin_bit_cast(bf16x8, st[a_rd + i * 32 * ROW_U + ch]);
+      af[buf][i] = __builtin_bit_cast(bf16x8, sa[a_rd + i * 32 * ROW_U + ch]);
 #pragma unroll
     for (int j = 0; j < FNA; ++j)
-      wf[buf][j] = __builtin_bit_cast(bf16x8, st[w_rd + j * 32 * ROW_U + ch]);
+      wf[buf % WB][j] = __builtin_bit_cast(bf16x8, sw[w_rd + j * 32 * ROW_U + ch]);
   };
   f32x16 acc[FM][FN];
 #pragma unroll
@@ -209,8 +237,34 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const GemmBatch args) 
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FNA; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[buf][j], af[buf][i], acc[i][j],
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[buf % WB][j], af[buf][i],
+                                                            acc[i][j], 0, 0, 0);
+  };
+  // 384-row tiles: k-step with fragments A in af[buf], W in wf[0]; with
+  // `more`, the next k-step's fragments (k-step s of `stage`) are read
+  // meanwhile: A into af[buf ^ 1] first, then each W fragment right after
+  // the last MFMA that reads its register.
+  auto kstep_rolling = [&](auto fna, int buf, bool more, int stage, int s) {
+    constexpr int FNA = decltype(fna)::value;
+    const u32x4* sa = lds + stage * (BM * ROW_U);
+    const u32x4* sw = lds + stage * (BN * ROW_U);
+    const int ch = (2 * s + fg) ^ sfr;
+    if (more) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        af[buf ^ 1][i] = __builtin_bit_cast(bf16x8, sa[a_rd + i * 32 * ROW_U + ch]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < FNA; ++j) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[0][j], af[buf][i], acc[i][j],
                                                             0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (more) wf[0][j] = __builtin_bit_cast(bf16x8, sw[w_rd + j * 32 * ROW_U + ch]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
 
   // Two LDS stages. Slice kt + 2 is fetched while kt + 1 is in flight and kt
@@ -222,15 +276,28 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const GemmBatch args) 
   dma(0, 0);
   if (nk > 1) {
     dma(1, 1);
-    // a loader's loads of slice 1 may fly (16, or 12 for the wave that skips W rows 224..255)
-    if (BNT == 224 && wave == 7) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    // a loader's loads of slice 1 may fly: 4 FM + 8 instructions, 4 fewer for
+    // the wave that skips W rows 224..255
+    if (BNT == 224 && wave == 7) wait_vmcnt<4 * FM + 4>();
+    else wait_vmcnt<4 * FM + 8>();
   } else {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    wait_vmcnt<0>();
   }
   __syncthreads();
   auto main_loop = [&](auto fna) {
     fload(fna, 0, 0, 0);
+    if (FM == 3) {
+      for (int kt = 0; kt < nk; ++kt) {
+        const int cur = kt & 1;
+#pragma unroll
+        for (int s = 0; s < BK / 16 - 1; ++s) kstep_rolling(fna, s & 1, true, cur, s + 1);
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (kt + 2 < nk) dma(kt + 2, cur);
+        kstep_rolling(fna, (BK / 16 - 1) & 1, kt + 1 < nk, cur ^ 1, 0);
+      }
+      return;
+    }
     for (int kt = 0; kt < nk; ++kt) {
       const int cur = kt & 1;
 #pragma unroll
@@ -253,57 +320,56 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const GemmBatch args) 
   if (BNT == 224 && wn == 1) main_loop(count_t<FN - 1>{});
   else main_loop(count_t<FN>{});
 
-  // ---- epilogue. Lane holds row wm*64 + i*32 + fr of the tile, columns
-  // (block j) wn*128 + j*32 + 8*q + 4*fg + 0..3 for q = 0..3. Results are
-  // staged in LDS (free now: every fragment read of the loop happened before
-  // its last barrier) and leave in whole rows, 16 bytes per lane: stores
-  // straight from the MFMA layout would be 16-byte pieces of 32 rows per
-  // instruction. Every wave reaches every barrier below.
+  // ---- epilogue. Lane holds rows wm*WTM + i*32 + fr of the tile (i < FM),
+  // columns (block j) wn*128 + j*32 + 8*q + 4*fg + 0..3 for q = 0..3. Results
+  // are staged in LDS (free now: every fragment read of the loop happened
+  // before its last barrier) in passes of whole rows and leave 16 bytes per
+  // lane: stores straight from the MFMA layout would be 16-byte pieces of 32
+  // rows per instruction. Every wave reaches every barrier below.
   char* const T = reinterpret_cast<char*>(lds);
-  // bf16 stage [256][256]: 16-byte chunk c of row r at c ^ (r & 31)
-  auto stage_bf16 = [&](int r, int col, f32x4 v) {
-    *reinterpret_cast<u32x2*>(T + r * 512 + (((col >> 3) ^ (r & 31)) << 4) + ((col & 4) << 1)) =
-        pack_bf16x4(v);
-  };
+  // bf16 stage [rows][256]: 16-byte chunk c of row r at c ^ (r & 31)
   auto out_row_of = [&](int gr, int& b) -> int64_t {
     b = gr / P.seg_len;
     return (int64_t)b * P.seg_stride + P.seg_off + (gr - b * P.seg_len);
   };
 
-  if (epi == EPI_F32 || epi == EPI_RESID) {
-    // fp32 stage [128][256] per pass (rows 128 p ..), 16-byte chunk c of row r at c ^ (r & 31)
+  if (FAM == FAM_F32) {
+    // fp32 stage [128][256] per pass: pass p holds accumulator block i = p
+    // of every wave (stage row r is tile row (r / 32) WTM + 32 p + r % 32),
+    // so each pass frees its registers; 16-byte chunk c of row r at c ^ (r & 31)
 #pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
-      if ((wm >> 1) == pass) {
+    for (int pass = 0; pass < FM; ++pass) {
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
+      for (int j = 0; j < FN; ++j)
 #pragma unroll
-          for (int j = 0; j < FN; ++j)
+        for (int q = 0; q < 4; ++q) {
+          const int r = wm * 32 + fr;
+          const int c = (wn * WTN + j * 32 + 8 * q + 4 * fg) >> 2;
+          f32x4 v;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const int r = (wm & 1) * WTM + i * 32 + fr;
-              const int c = (wn * WTN + j * 32 + 8 * q + 4 * fg) >> 2;
-              f32x4 v;
-#pragma unroll
-              for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e];
-              *reinterpret_cast<f32x4*>(T + r * 1024 + ((c ^ (r & 31)) << 4)) = v;
-            }
-      }
+          for (int e = 0; e < 4; ++e) v[e] = acc[pass][j][4 * q + e];
+          *reinterpret_cast<f32x4*>(T + r * 1024 + ((c ^ (r & 31)) << 4)) = v;
+        }
       __syncthreads();
       // 16-byte unit u = it * NT + tid: row u / 64 = 8 it + wave, chunk
       // u % 64 = lane. The residual and gate reads of 8 rows are issued
       // together before any store (a store could alias a later read, so the
       // compiler would not move reads above it), one memory latency per 8 rows.
+      constexpr int RF = 8;  // rows in flight
+      // the rows' addresses are wave-uniform (scalar registers): computed here,
+      // per pass, instead of all passes' up front
+      int m0p = m0;
+      asm volatile("" : "+s"(m0p));
       const int c = lane, col = tn * BNT + c * 4;
       const bool col_ok = c * 4 < BNT && col < N;
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        float* dst[8];
-        f32x4 x[8], g[8];
+      for (int half = 0; half < 16 / RF; ++half) {
+        float* dst[RF];
+        f32x4 x[RF], g[RF];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const int r = 8 * (8 * half + k) + wave;
-          const int gr = m0 + pass * 128 + r;
+        for (int k = 0; k < RF; ++k) {
+          const int r = 8 * (RF * half + k) + wave;
+          const int gr = m0p + (r >> 5) * WTM + 32 * pass + (r & 31);
           dst[k] = nullptr;
           if (col_ok && gr < M) {
             int b;
@@ -315,8 +381,8 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const GemmBatch args) 
           }
         }
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const int r = 8 * (8 * half + k) + wave;
+        for (int k = 0; k < RF; ++k) {
+          const int r = 8 * (RF * half + k) + wave;
           if (dst[k] == nullptr) continue;
           const f32x4 v = *reinterpret_cast<const f32x4*>(T + r * 1024 + ((c ^ (r & 31)) << 4));
           *reinterpret_cast<f32x4*>(dst[k]) = epi == EPI_RESID ? x[k] + g[k] * v : v;
@@ -327,26 +393,21 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const GemmBatch args) 
     return;
   }
 
-  // bf16 results: phase A, values into the stage
-  if (epi == EPI_SWIGLU) {
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN / 2; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          f32x4 v;
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            v[e] = silu_f(acc[i][j][4 * q + e]) * acc[i][j + FN / 2][4 * q + e];
-          stage_bf16(wm * WTM + i * 32 + fr, wn * (WTN / 2) + j * 32 + 8 * q + 4 * fg, v);
-        }
-  } else if (epi == EPI_QKV && tn * BN + wn * WTN < N && (tn * BN + wn * WTN) / args.qkv.D < 2) {
+  // bf16 results in passes of up to two accumulator blocks of every wave
+  // (the whole tile at 256 rows; blocks {0, 1} then {2} at 384 rows: a
+  // 384 x 256 bf16 stage would not fit the LDS). In pass p with nb blocks,
+  // stage row r is tile row (r / (32 nb)) WTM + 32 (2 p + (r / 32) % nb) + r % 32.
+  constexpr int NPASS = (FM + 1) / 2;
+  const bool qk_head = epi == EPI_QKV && tn * BN + wn * WTN < N &&
+                       (tn * BN + wn * WTN) / args.qkv.D < 2;
+  float* const row_scale = reinterpret_cast<float*>(T + RS_BYTE);  // [2][BM]
+  if (qk_head) {
     // q or k head (the wave's 128 columns): the row's 1 / rms (times q_scale
-    // for q) from the fp32 accumulators, kept per row in LDS; a row's 128
-    // values sit in lanes l and l ^ 32, so the sum of squares needs one
-    // cross-half exchange. The values are staged raw; gain and rotation are
-    // applied on the way out, where 16 lanes share a token row.
+    // for q) from the fp32 accumulators, kept per row in LDS (outside every
+    // pass's stage); a row's 128 values sit in lanes l and l ^ 32, so the sum
+    // of squares needs one cross-half exchange. The values are staged raw;
+    // gain and rotation are applied on the way out, where 16 lanes share a
+    // token row.
     const QkvEpilogue& E = args.qkv;
     const float sc = (tn * BN + wn * WTN) / E.D == 0 ? E.q_scale : 1.f;
 #pragma unroll
@@ -357,125 +418,175 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const GemmBatch args) 
 #pragma unroll
         for (int e = 0; e < 16; ++e) ss += acc[i][j][e] * acc[i][j][e];
       ss = half_sum(ss);
-      if (fg == 0) row_scale[wn][wm * WTM + i * 32 + fr] = rsqrtf(ss * (1.f / 128.f) + E.eps) * sc;
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          f32x4 v;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e];
-          stage_bf16(wm * WTM + i * 32 + fr, wn * WTN + j * 32 + 8 * q + 4 * fg, v);
-        }
+      if (fg == 0) row_scale[wn * BM + wm * WTM + i * 32 + fr] = rsqrtf(ss * (1.f / 128.f) + E.eps) * sc;
     }
-  } else {
-    // plain bf16 (also the v heads of EPI_QKV)
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          f32x4 v;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e];
-          stage_bf16(wm * WTM + i * 32 + fr, wn * WTN + j * 32 + 8 * q + 4 * fg, v);
-        }
   }
-  __syncthreads();
-
-  // phase B: whole rows out, 16 bytes per lane
-  if (epi != EPI_QKV) {
-    const int ncol = epi == EPI_SWIGLU ? BN / 2 : BNT;  // output columns of the tile
-    const int upr = ncol / 8;                          // 16-byte units per row
-#pragma unroll 4
-    for (int it = 0; it < 256 * (BN / 8) / NT; ++it) {
-      const int u = it * NT + tid;
-      if (u >= 256 * upr) break;
-      const int r = u / upr, c = u - r * upr;
-      const int gr = m0 + r, col = tn * ncol + c * 8;
-      if (gr >= M || col >= N) continue;
-      int b;
-      *reinterpret_cast<u32x4*>(static_cast<bf16_t*>(P.C) + out_row_of(gr, b) * P.ldc + col) =
-          *reinterpret_cast<const u32x4*>(T + r * 512 + ((c ^ (r & 31)) << 4));
-    }
-    return;
-  }
-  // EPI_QKV: per 128-column head of the tile: q / k rows to [b, h, s, :]
-  // (16 lanes per token), v gathered 8 tokens per dim to v^T[b, h, d, s..s+7]
-  const QkvEpilogue& E = args.qkv;
+  // every result as bf16, packed 4 per register pair: half the registers of
+  // the accumulators, which the later passes would otherwise hold through
+  // the earlier passes' stores (SwiGLU: the gate and up halves combine
+  // first, so columns j < FN / 2 carry the products)
+  u32x2 pk[FM][FN][4];
 #pragma unroll
-  for (int hh = 0; hh < 2; ++hh) {
-    const int col0 = tn * BN + hh * 128;
-    if (col0 >= N) break;
-    const int part = col0 / E.D;
-    const int h = (col0 - part * E.D) >> 7;
-    if (part < 2) {
-      // 16 lanes per token row, 8 columns (4 rotation pairs) per lane
-      bf16_t* base = part == 0 ? E.q : E.k;
-      const float* gain = part == 0 ? E.q_gain[pi] : E.k_gain[pi];
-      const int cl = (tid & 15) * 8;  // column within the head
-      const f32x4 g0 = *reinterpret_cast<const f32x4*>(gain + cl);
-      const f32x4 g1 = *reinterpret_cast<const f32x4*>(gain + cl + 4);
-#pragma unroll 4
-      for (int it = 0; it < 256 * 16 / NT; ++it) {
-        const int u = it * NT + tid;
-        const int r = u >> 4, c = hh * 16 + (u & 15);
-        const int gr = m0 + r;
-        if (gr >= M) continue;
-        const int b = gr / P.seg_len;
-        const int s = P.seg_off + (gr - b * P.seg_len);
-        const u32x4 raw = *reinterpret_cast<const u32x4*>(T + r * 512 + ((c ^ (r & 31)) << 4));
-        const float rsc = row_scale[hh][r];
-        const f32x4 co = *reinterpret_cast<const f32x4*>(E.cos_t + (int64_t)s * 64 + (cl >> 1));
-        const f32x4 si = *reinterpret_cast<const f32x4*>(E.sin_t + (int64_t)s * 64 + (cl >> 1));
-        f32x8 y;
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int pr = 0; pr < 4; ++pr) {
-          const float gx0 = pr < 2 ? g0[2 * pr] : g1[2 * pr - 4];
-          const float gx1 = pr < 2 ? g0[2 * pr + 1] : g1[2 * pr - 3];
-          const float x0 = bf16_to_f32(raw[pr] & 0xFFFFu) * rsc * gx0;
-          const float x1 = bf16_to_f32(raw[pr] >> 16) * rsc * gx1;
-          y[2 * pr] = x0 * co[pr] - x1 * si[pr];
-          y[2 * pr + 1] = x0 * si[pr] + x1 * co[pr];
-        }
-        *reinterpret_cast<bf16x8*>(base + (((int64_t)b * E.H + h) * E.S_pad + s) * 128 + cl) =
-            pack_bf16x8(y);
-      }
-    } else {
-#pragma unroll 2
-      for (int it = 0; it < 128 * 32 / NT; ++it) {
-        const int u = it * NT + tid;
-        const int d = u & 127, tg = u >> 7;  // dim, group of 8 tokens
-        const int colb = ((hh * 128 + d) >> 3), wb = (d & 7) << 1;
-        uint16_t tok[8];
+    for (int j = 0; j < FN; ++j)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int r = tg * 8 + e;
-          tok[e] = *reinterpret_cast<const uint16_t*>(T + r * 512 + ((colb ^ (r & 31)) << 4) + wb);
-        }
-        const int r0 = m0 + tg * 8;
-        if (r0 >= M) continue;
-        const int b0 = r0 / P.seg_len;
-        const int s0 = P.seg_off + (r0 - b0 * P.seg_len);
-        if (r0 + 7 < M && (r0 + 7) / P.seg_len == b0 && (s0 & 7) == 0) {
-          u32x4 pk;
+      for (int q = 0; q < 4; ++q) {
+        f32x4 v;
+        if (epi == EPI_SWIGLU) {
+          if (j >= FN / 2) continue;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) pk[e] = (uint32_t)tok[2 * e] | ((uint32_t)tok[2 * e + 1] << 16);
-          *reinterpret_cast<u32x4*>(E.vt + (((int64_t)b0 * E.H + h) * 128 + d) * E.S_pad + s0) = pk;
+          for (int e = 0; e < 4; ++e)
+            v[e] = silu_f(acc[i][j][4 * q + e]) * acc[i][j + FN / 2][4 * q + e];
         } else {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int gr = r0 + e;
-            if (gr >= M) break;
+          for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e];
+        }
+        pk[i][j][q] = pack_bf16x4(v);
+      }
+#pragma unroll
+  for (int pass = 0; pass < NPASS; ++pass) {
+    constexpr int BPP = 2;
+    const int nb = min(FM - BPP * pass, BPP);  // blocks in this pass
+    const int prow = 32 * nb * 4;              // stage rows of this pass
+    // tile row of stage row r
+    auto tile_row = [&](int r) {
+      return (r / (32 * nb)) * WTM + 32 * (BPP * pass + (r >> 5) % nb) + (r & 31);
+    };
+    // phase A: this pass's blocks into the stage
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      if (i / BPP != pass) continue;
+      const int r = wm * 32 * nb + (i - BPP * pass) * 32 + fr;
+      // SwiGLU: 64 output columns per wave; plain bf16 and the raw q / k / v
+      // values of EPI_QKV: 128
+      const int nj = epi == EPI_SWIGLU ? FN / 2 : FN;
+      const int cw = epi == EPI_SWIGLU ? WTN / 2 : WTN;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        if (j >= nj) continue;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = wn * cw + j * 32 + 8 * q + 4 * fg;
+          *reinterpret_cast<u32x2*>(T + r * 512 + (((col >> 3) ^ (r & 31)) << 4) +
+                                    ((col & 4) << 1)) = pk[i][j][q];
+        }
+      }
+    }
+    __syncthreads();
+
+    // phase B: whole rows out, 16 bytes per lane
+    if (epi != EPI_QKV) {
+      const int ncol = epi == EPI_SWIGLU ? BN / 2 : BNT;  // output columns of the tile
+      const int upr = ncol / 8;                          // 16-byte units per row
+#pragma unroll 4
+      for (int it = 0; it < 256 * (BN / 8) / NT; ++it) {
+        const int u = it * NT + tid;
+        if (u >= prow * upr) break;
+        const int r = u / upr, c = u - r * upr;
+        const int gr = m0 + tile_row(r), col = tn * ncol + c * 8;
+        if (gr >= M || col >= N) continue;
+        int b;
+        *reinterpret_cast<u32x4*>(static_cast<bf16_t*>(P.C) + out_row_of(gr, b) * P.ldc + col) =
+            *reinterpret_cast<const u32x4*>(T + r * 512 + ((c ^ (r & 31)) << 4));
+      }
+    } else {
+      // EPI_QKV: per 128-column head of the tile: q / k rows to [b, h, s, :]
+      // (16 lanes per token), v gathered 8 tokens per dim to v^T[b, h, d, s..s+7]
+      const QkvEpilogue& E = args.qkv;
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int col0 = tn * BN + hh * 128;
+        if (col0 >= N) break;
+        const int part = col0 / E.D;
+        const int h = (col0 - part * E.D) >> 7;
+        if (part < 2) {
+          // 16 lanes per token row, 8 columns (4 rotation pairs) per lane
+          bf16_t* base = part == 0 ? E.q : E.k;
+          const float* gain = part == 0 ? E.q_gain[pi] : E.k_gain[pi];
+          const int cl = (tid & 15) * 8;  // column within the head
+          const f32x4 g0 = *reinterpret_cast<const f32x4*>(gain + cl);
+          const f32x4 g1 = *reinterpret_cast<const f32x4*>(gain + cl + 4);
+#pragma unroll 2
+          for (int it = 0; it < 256 * 16 / NT; ++it) {
+            const int u = it * NT + tid;
+            const int r = u >> 4, c = hh * 16 + (u & 15);
+            if (r >= prow) break;
+            const int tr = tile_row(r);
+            const int gr = m0 + tr;
+            if (gr >= M) continue;
             const int b = gr / P.seg_len;
             const int s = P.seg_off + (gr - b * P.seg_len);
-            E.vt[(((int64_t)b * E.H + h) * 128 + d) * E.S_pad + s] = tok[e];
+            const u32x4 raw = *reinterpret_cast<const u32x4*>(T + r * 512 + ((c ^ (r & 31)) << 4));
+            const float rsc = row_scale[hh * BM + tr];
+            const f32x4 co = *reinterpret_cast<const f32x4*>(E.cos_t + (int64_t)s * 64 + (cl >> 1));
+            const f32x4 si = *reinterpret_cast<const f32x4*>(E.sin_t + (int64_t)s * 64 + (cl >> 1));
+            f32x8 y;
+#pragma unroll
+            for (int pr = 0; pr < 4; ++pr) {
+              const float gx0 = pr < 2 ? g0[2 * pr] : g1[2 * pr - 4];
+              const float gx1 = pr < 2 ? g0[2 * pr + 1] : g1[2 * pr - 3];
+              const float x0 = bf16_to_f32(raw[pr] & 0xFFFFu) * rsc * gx0;
+              const float x1 = bf16_to_f32(raw[pr] >> 16) * rsc * gx1;
+              y[2 * pr] = x0 * co[pr] - x1 * si[pr];
+              y[2 * pr + 1] = x0 * si[pr] + x1 * co[pr];
+            }
+            *reinterpret_cast<bf16x8*>(base + (((int64_t)b * E.H + h) * E.S_pad + s) * 128 + cl) =
+                pack_bf16x8(y);
+          }
+        } else {
+#pragma unroll 2
+          for (int it = 0; it < 256 * 16 / NT; ++it) {
+            const int u = it * NT + tid;
+            const int d = u & 127, tg = u >> 7;  // dim, group of 8 tokens
+            if (tg * 8 >= prow) break;
+            const int colb = ((hh * 128 + d) >> 3), wb = (d & 7) << 1;
+            uint16_t tok[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int r = tg * 8 + e;
+              tok[e] = *reinterpret_cast<const uint16_t*>(T + r * 512 + ((colb ^ (r & 31)) << 4) + wb);
+            }
+            const int r0 = m0 + tile_row(tg * 8);  // 8 stage rows = 8 tile rows
+            if (r0 >= M) continue;
+            const int b0 = r0 / P.seg_len;
+            const int s0 = P.seg_off + (r0 - b0 * P.seg_len);
+            if (r0 + 7 < M && (r0 + 7) / P.seg_len == b0 && (s0 & 7) == 0) {
+              u32x4 pk;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) pk[e] = (uint32_t)tok[2 * e] | ((uint32_t)tok[2 * e + 1] << 16);
+              *reinterpret_cast<u32x4*>(E.vt + (((int64_t)b0 * E.H + h) * 128 + d) * E.S_pad + s0) = pk;
+            } else {
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                const int gr = r0 + e;
+                if (gr >= M) break;
+                const int b = gr / P.seg_len;
+                const int s = P.seg_off + (gr - b * P.seg_len);
+                E.vt[(((int64_t)b * E.H + h) * 128 + d) * E.S_pad + s] = tok[e];
+              }
+            }
           }
         }
       }
     }
+    if (pass + 1 < NPASS) __syncthreads();  // the next pass overwrites the stage
   }
+}
+
+template <int BNT, int FAM>
+__global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const GemmBatch args) {
+  __shared__ u32x4 lds[LDS_U];
+  int pi = 0, local = 0;
+  const auto tiles_of = [&](int i) { return args.p[i].tiles_m * args.p[i].tiles_n; };
+  if (!tile_of_block<kMaxGemmProblems>(tiles_of, args.count, (int)blockIdx.x, &pi, &local))
+    return;  // not reached: the grid has exactly one workgroup per tile
+  pi = __builtin_amdgcn_readfirstlane(pi);
+  local = __builtin_amdgcn_readfirstlane(local);
+  // fields are read from the kernel arguments (scalar loads) as needed
+  const GemmProblem& P = args.p[pi];
+  if (P.fm == 3) gemm_tile<BNT, 3, FAM>(args, P, pi, local, lds);
+  else gemm_tile<BNT, 2, FAM>(args, P, pi, local, lds);
 }
 
 // Compute units of the current device (cached per device).
@@ -493,48 +604,152 @@ int device_cus() {
   return cached[dev];
 }
 
-// Tile counts of every problem for tile width bnt; returns the total.
-int64_t assign_tiles(GemmBatch& batch, int bnt) {
-  int64_t total = 0;
-  for (int i = 0; i < batch.count; ++i) {
-    GemmProblem& p = batch.p[i];
+// ---- launch plan: tile width of the launch and tile height per problem.
+// A tile's time per K slice is modelled from what a loader wave does in it:
+// its load instructions (4 FM + 8) and its own MFMAs (FM x 4 k-steps x its
+// active column blocks), weighted 4 : 3. Fitted to kernel traces at 4608
+// rows (a 384-row tile takes 1.40x a 256-row one: 116 vs 83 us at K = 3072).
+// The launch time is modelled as one XCD's share of every problem (a
+// problem's tiles are dealt evenly to the 8 XCDs), in launch order, placed
+// greedily on that XCD's CUs, which reproduces the traced launch times of
+// the step within 3 %; plans are cached per launch shape.
+struct Plan {
+  int bnt;
+  int fm[kMaxGemmProblems];
+  int order[kMaxGemmProblems];
+};
+
+int64_t tile_cost(int fm, int bnt, int64_t K) {
+  const int loads = 4 * fm + 8, mfmas = fm * (bnt == 224 ? 3 : 4) * 4;
+  return (int64_t)(4 * loads + 3 * mfmas) * (K / BK);
+}
+
+int64_t model_time(const GemmBatch& b, const int* fm, const int* order, int bnt, int cus_per_xcd) {
+  std::vector<int64_t> cu((size_t)std::max(cus_per_xcd, 1), 0);
+  for (int oi = 0; oi < b.count; ++oi) {
+    const GemmProblem& p = b.p[order[oi]];
     const int cols = p.epi == EPI_SWIGLU ? BN / 2 : bnt;
-    p.tiles_m = (p.M + BM - 1) / BM;
-    p.tiles_n = (p.N + cols - 1) / cols;
-    p.tile_begin = (int32_t)total;
-    total += (int64_t)p.tiles_m * p.tiles_n;
+    const int64_t n = (int64_t)((p.M + 128 * fm[order[oi]] - 1) / (128 * fm[order[oi]])) *
+                      ((p.N + cols - 1) / cols);
+    const int64_t share = (n + 7) / 8;
+    const int64_t c = tile_cost(fm[order[oi]], bnt, p.K);
+    for (int64_t t = 0; t < share; ++t) {
+      auto it = std::min_element(cu.begin(), cu.end());
+      *it += c;
+    }
   }
-  return total;
+  return *std::max_element(cu.begin(), cu.end());
+}
+
+// DIT_GEMM_TILE_ROWS=256 or 384 forces one tile height on every problem
+// (tests compare the two bit for bit; timing runs compare them with the
+// model's choice). Any other value, or none, leaves the choice to the model.
+int forced_rows() {
+  const char* e = std::getenv("DIT_GEMM_TILE_ROWS");
+  if (!e) return 0;
+  const int v = std::atoi(e);
+  return v == 256 || v == 384 ? v : 0;
+}
+
+Plan make_plan(const GemmBatch& b, int cus, int forced) {
+  bool narrow_ok = true;
+  for (int i = 0; i < b.count; ++i)
+    if (b.p[i].epi == EPI_SWIGLU || b.p[i].epi == EPI_QKV) narrow_ok = false;
+  // candidates: 384-row tiles for any subset of the (at most three) largest
+  // problems with at least 384 rows; everything else 256 rows
+  int big[3], nbig = 0;
+  if (!forced) {
+    std::vector<std::pair<int64_t, int>> sz;
+    for (int i = 0; i < b.count; ++i)
+      if (b.p[i].M >= 384) sz.push_back({-(int64_t)b.p[i].M * b.p[i].N * b.p[i].K, i});
+    std::sort(sz.begin(), sz.end());
+    for (size_t j = 0; j < sz.size() && nbig < 3; ++j) big[nbig++] = sz[j].second;
+  }
+  Plan best{};
+  int64_t best_t = -1;
+  const int cpx = std::max(1, cus / 8);
+  for (int bnt : {256, 224}) {
+    if (bnt == 224 && !narrow_ok) continue;
+    for (int mask = 0; mask < (1 << nbig); ++mask) {
+      Plan pl{};
+      pl.bnt = bnt;
+      for (int i = 0; i < kMaxGemmProblems; ++i) pl.fm[i] = forced == 384 ? 3 : 2;
+      for (int j = 0; j < nbig; ++j)
+        if (mask >> j & 1) pl.fm[big[j]] = 3;
+      // taller tiles first (stable), so each XCD ends on its short tiles
+      for (int i = 0; i < b.count; ++i) pl.order[i] = i;
+      std::stable_sort(pl.order, pl.order + b.count,
+                       [&](int x, int y) { return pl.fm[x] > pl.fm[y]; });
+      const int64_t t = model_time(b, pl.fm, pl.order, bnt, cpx);
+      if (best_t < 0 || t < best_t) {
+        best_t = t;
+        best = pl;
+      }
+    }
+  }
+  return best;
+}
+
+using PlanKey = std::tuple<int, int, int, std::vector<int64_t>>;
+
+Plan cached_plan(const GemmBatch& b, int cus) {
+  const int forced = forced_rows();
+  static std::mutex mu;
+  static std::map<PlanKey, Plan> cache;
+  std::vector<int64_t> shape;
+  for (int i = 0; i < b.count; ++i) {
+    const GemmProblem& p = b.p[i];
+    shape.insert(shape.end(), {(int64_t)p.M, (int64_t)p.N, (int64_t)p.K, (int64_t)p.epi});
+  }
+  PlanKey key{cus, forced, b.count, shape};
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  const Plan pl = make_plan(b, cus, forced);
+  if (cache.size() < 4096) cache.emplace(key, pl);
+  return pl;
 }
 
 }  // namespace
 
 hipError_t gemm_launch(GemmBatch& batch, hipStream_t stream) {
   for (int i = batch.count; i < kMaxGemmProblems; ++i) batch.p[i] = GemmProblem{};
-  // Tile width: 224 instead of 256 when every epilogue allows it and the
-  // launch then takes fewer rounds x per-tile time. A 224-wide tile does 7/8
-  // of the MFMA work but loads 15/16 of the bytes, and the loads bound it,
-  // so its time counts as 15/16. E.g. N = 3072 at M = 4608: 216 tiles of 256
-  // leave 40 of 256 CUs idle for the whole launch, 252 tiles of 224 finish
-  // in one shorter round; N = 27648 keeps 256 (8 rounds against 9 x 15/16).
-  bool narrow_ok = true;
-  for (int i = 0; i < batch.count; ++i)
-    if (batch.p[i].epi == EPI_SWIGLU || batch.p[i].epi == EPI_QKV) narrow_ok = false;
-  int bnt = BN;
-  if (narrow_ok) {
-    const int64_t cus = device_cus();
-    const int64_t r256 = (assign_tiles(batch, 256) + cus - 1) / cus;
-    const int64_t r224 = (assign_tiles(batch, 224) + cus - 1) / cus;
-    if (r224 * 15 < r256 * 16) bnt = 224;
+  if (batch.count < 1 || batch.count > kMaxGemmProblems) return hipErrorInvalidValue;
+  // one epilogue family per launch
+  auto is_f32 = [](int epi) { return epi == EPI_F32 || epi == EPI_RESID; };
+  const bool f32 = is_f32(batch.p[0].epi);
+  for (int i = 1; i < batch.count; ++i)
+    if (is_f32(batch.p[i].epi) != f32) return hipErrorInvalidValue;
+  const Plan pl = cached_plan(batch, device_cus());
+  // reorder the problems (and the per-problem QK gains) into launch order
+  GemmBatch b = batch;
+  for (int i = 0; i < batch.count; ++i) {
+    b.p[i] = batch.p[pl.order[i]];
+    b.qkv.q_gain[i] = batch.qkv.q_gain[pl.order[i]];
+    b.qkv.k_gain[i] = batch.qkv.k_gain[pl.order[i]];
   }
-  const int64_t total = assign_tiles(batch, bnt);
+  int64_t total = 0;
+  for (int i = 0; i < b.count; ++i) {
+    GemmProblem& p = b.p[i];
+    p.fm = pl.fm[pl.order[i]];
+    const int cols = p.epi == EPI_SWIGLU ? BN / 2 : pl.bnt;
+    p.tiles_m = (p.M + 128 * p.fm - 1) / (128 * p.fm);
+    p.tiles_n = (p.N + cols - 1) / cols;
+    p.tile_begin = (int32_t)total;
+    total += (int64_t)p.tiles_m * p.tiles_n;
+  }
   if (total > INT32_MAX) return hipErrorInvalidValue;
-  batch.total_tiles = (int32_t)total;
+  b.total_tiles = (int32_t)total;
+  batch.total_tiles = b.total_tiles;
   if (total == 0) return hipSuccess;
-  if (bnt == 224)
-    hipLaunchKernelGGL(gemm_bf16_kernel<224>, dim3((unsigned)total), dim3(NT), 0, stream, batch);
+  const dim3 grid((unsigned)total);
+  if (f32)
+    hipLaunchKernelGGL((pl.bnt == 224 ? gemm_bf16_kernel<224, FAM_F32> : gemm_bf16_kernel<256, FAM_F32>),
+                       grid, dim3(NT), 0, stream, b);
+  else if (pl.bnt == 224)
+    hipLaunchKernelGGL((gemm_bf16_kernel<224, FAM_BF16>), grid, dim3(NT), 0, stream, b);
   else
-    hipLaunchKernelGGL(gemm_bf16_kernel<256>, dim3((unsigned)total), dim3(NT), 0, stream, batch);
+    hipLaunchKernelGGL((gemm_bf16_kernel<256, FAM_BF16>), grid, dim3(NT), 0, stream, b);
   return hipGetLastError();
 }
 

@@ -39,7 +39,9 @@ struct GemmProblem {
   int64_t lda, ldw, ldc, gate_bstride, seg_stride;
   int32_t M, N, K, epi;
   int32_t seg_len, seg_off;
-  int32_t tiles_m, tiles_n, tile_begin, pad_;
+  // set by gemm_launch: tile height 128 fm rows (fm = 2 or 3), tile counts,
+  // and the problem's first tile in launch order
+  int32_t tiles_m, tiles_n, tile_begin, fm;
 };
 
 constexpr int kMaxGemmProblems = 8;
@@ -69,9 +71,14 @@ struct GemmBatch {
 // Requirements checked by the caller: K % 64 == 0, N % 32 == 0 (EPI_QKV: N = 3D,
 // D % 128 == 0),
 // lda/ldw % 8 == 0, 16-byte aligned A and W; ldc % 4 == 0.
-constexpr int kGemmBM = 256, kGemmBN = 256, kGemmBK = 64;
+constexpr int kGemmBN = 256, kGemmBK = 64;
 
-// Fills tiles_m/tiles_n/tile_begin/total_tiles and launches.
+// The problems of one launch are all of the fp32 family (EPI_F32 /
+// EPI_RESID) or all of the bf16 family (the others).
+// Picks the tile shapes (rows per problem, width per launch), fills
+// fm/tiles_m/tiles_n/tile_begin/total_tiles and launches. May reorder the
+// problems of its copy of the batch (with their QK gains); the caller's
+// batch keeps its order.
 hipError_t gemm_launch(GemmBatch& batch, hipStream_t stream);
 
 // ------------------------------------------------------------------ norms

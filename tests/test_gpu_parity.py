@@ -7,6 +7,7 @@ the block's increment x_out - x_in (rel-L2 <= 3e-2), which the residual would
 otherwise hide. Full-size steps compare against stored oracle outputs
 (tests/golden/*.npz, written by tests/golden/make_golden.py from oracle/ only).
 """
+import contextlib
 import os
 
 import numpy as np
@@ -250,6 +251,75 @@ def test_batch_rows_bitwise_independent():
         dit.dual_block(cfg, wd, x1, 40, m1, cos_d, sin_d)
         dit.single_block(cfg, ws, x1, m1, cos_d, sin_d)
         assert np.array_equal(to_np(x1)[0], both[b]), f"row {b}"
+
+
+# ---------------------------------------------------------------- GEMM tile heights
+
+@contextlib.contextmanager
+def gemm_tile_rows(rows):
+    """Force one GEMM tile height (256 or 384 rows) on every launch."""
+    old = os.environ.get("DIT_GEMM_TILE_ROWS")
+    os.environ["DIT_GEMM_TILE_ROWS"] = str(rows)
+    try:
+        yield
+    finally:
+        if old is None:
+            del os.environ["DIT_GEMM_TILE_ROWS"]
+        else:
+            os.environ["DIT_GEMM_TILE_ROWS"] = old
+
+
+TILE_CASES = [
+    # (name, cfg kwargs, n_txt, grid, refs, B): ragged row counts, a batch,
+    # and the 1024x1024 shape, where the launch plan mixes both heights
+    ("d256_refs_b3", {}, 17, (6, 6), ((3, 5), (2, 2)), 3),
+    ("d3072_s600", {"hidden": 3072, "heads": 24, "mlp_hidden": 9216}, 88, (16, 32), (), 1),
+    ("d3072_s1300_b2", {"hidden": 3072, "heads": 24, "mlp_hidden": 9216}, 40, (30, 42), (), 2),
+    ("d3072_1024px", {"hidden": 3072, "heads": 24, "mlp_hidden": 9216}, 512, (64, 64), (), 1),
+]
+
+
+@pytest.mark.parametrize("case", TILE_CASES, ids=[c[0] for c in TILE_CASES])
+def test_gemm_tile_heights_bitwise(case):
+    """Every output element runs the same MFMA over the same k-steps whatever
+    the tile height, so blocks computed with 256-row tiles, 384-row tiles and
+    the launch plan's mix agree bit for bit (dual and single blocks: the QKV,
+    SwiGLU and gated-residual epilogues)."""
+    name, kw, n_txt, grid, refs, B = case
+    cfg = small_cfg(**kw)
+    pos, S, xs, mod_d, cos_d, sin_d, *_ = setup_block(cfg, n_txt, grid, refs, B,
+                                                      [0.75, 0.5, 0.25][:B])
+    wd = dit.DualWeights(synth.dual_weights(cfg, 0, 0))
+    wsn = dit.SingleWeights(synth.single_weights(cfg, 0, 0))
+    outs = {}
+    for rows in (256, 384, None):
+        ctx = gemm_tile_rows(rows) if rows else contextlib.nullcontext()
+        with ctx:
+            x = torch.from_numpy(xs).cuda()
+            dit.dual_block(cfg, wd, x, n_txt, mod_d, cos_d, sin_d)
+            dit.single_block(cfg, wsn, x, mod_d, cos_d, sin_d)
+            torch.cuda.synchronize()
+        outs[rows] = to_np(x)
+        log(f"tiles {name}: {rows or 'plan'} rows done")
+    assert np.array_equal(outs[256], outs[384]), "256- and 384-row tiles differ"
+    assert np.array_equal(outs[256], outs[None]), "the launch plan's tiles differ"
+
+
+def test_gemm_tile_heights_bitwise_step():
+    """A small step (embeddings with a K-split, final projection, fp32
+    epilogues) with 256-row and 384-row tiles: bitwise equal."""
+    cfg = small_cfg(hidden=1024, heads=8, mlp_hidden=3072, txt_channels=4096)
+    mw = synth.ModelWeights(cfg, 0, cache=True)
+    dw = dit.ModelWeights(mw)
+    wl = synth.Workload("s", 2, 48, (20, 21), ((6, 5),), 0.6)
+    pos = dit.position_ids(wl.n_txt, wl.img_grid, wl.ref_grids)
+    cos_d, sin_d = dit.rope_tables(cfg, pos)
+    got = {}
+    for rows in (256, 384):
+        with gemm_tile_rows(rows):
+            v, _ = run_step(cfg, dw, wl, cos_d, sin_d)
+        got[rows] = to_np(v)
+    assert np.array_equal(got[256], got[384])
 
 
 # ---------------------------------------------------------------- steps
