@@ -388,15 +388,11 @@ void set_rows(dit::GemmProblem& p, int seg_len, int64_t seg_stride, int seg_off)
   p.seg_off = seg_off;
 }
 
+void gemm_work(const dit::GemmBatch& g, double& flops, double& bytes);
+
 int run_gemm(dit::GemmBatch& g, hipStream_t st) {
-  double flops = 0, bytes = 0;
-  for (int i = 0; i < g.count; ++i) {
-    const dit::GemmProblem& p = g.p[i];
-    const double n_w = p.epi == dit::EPI_SWIGLU ? 2.0 * p.N : (double)p.N;
-    flops += 2.0 * p.M * n_w * p.K;
-    const double out = p.epi == dit::EPI_RESID ? 8.0 : (p.epi == dit::EPI_F32 ? 4.0 : 2.0);
-    bytes += 2.0 * p.M * p.K + 2.0 * n_w * p.K + out * p.M * p.N;
-  }
+  double flops, bytes;
+  gemm_work(g, flops, bytes);
   DIT_TRY(timed(DIT_K_GEMM, flops, bytes, st, [&] { return dit::gemm_launch(g, st); }));
   return DIT_OK;
 }
@@ -516,10 +512,39 @@ int run_qkv(const dit_config& c, const BlockLayout& L, void* ws, dit::GemmBatch&
   return run_qkv_pad(pa, st);
 }
 
+double attention_flops(const dit::AttnArgs& aa) {
+  return 4.0 * aa.B * aa.H * (double)aa.S * aa.S * 128.0;
+}
+double attention_bytes(const dit::AttnArgs& aa) {
+  return (double)aa.B * aa.H * aa.S * 128.0 * 2.0 * 4.0;
+}
+
 int run_attention(const dit::AttnArgs& aa, hipStream_t st) {
-  const double bh = (double)aa.B * aa.H, S = (double)aa.S;
-  DIT_TRY(timed(DIT_K_ATTENTION, 4.0 * bh * S * S * 128.0, bh * S * 128.0 * 2.0 * 4.0, st,
+  DIT_TRY(timed(DIT_K_ATTENTION, attention_flops(aa), attention_bytes(aa), st,
                 [&] { return dit::attention_launch(aa, st); }));
+  return DIT_OK;
+}
+
+// GEMM problems' algorithmic FLOPs and bytes (each operand read once, each
+// result written once; a gated residual is read and written).
+void gemm_work(const dit::GemmBatch& g, double& flops, double& bytes) {
+  flops = bytes = 0;
+  for (int i = 0; i < g.count; ++i) {
+    const dit::GemmProblem& p = g.p[i];
+    const double n_w = p.epi == dit::EPI_SWIGLU ? 2.0 * p.N : (double)p.N;
+    flops += 2.0 * p.M * n_w * p.K;
+    const double out = p.epi == dit::EPI_RESID ? 8.0 : (p.epi == dit::EPI_F32 ? 4.0 : 2.0);
+    bytes += 2.0 * p.M * p.K + 2.0 * n_w * p.K + out * p.M * p.N;
+  }
+}
+
+// Attention fused with the GEMM batch g (bf16 family, independent of it).
+int run_attention_gemm(const dit::AttnArgs& aa, dit::GemmBatch& g, hipStream_t st) {
+  if (g.count == 0) return run_attention(aa, st);
+  double flops, bytes;
+  gemm_work(g, flops, bytes);
+  DIT_TRY(timed(DIT_K_ATTN_GEMM, flops + attention_flops(aa), bytes + attention_bytes(aa), st,
+                [&] { return dit::attn_gemm_launch(aa, g, st); }));
   return DIT_OK;
 }
 
@@ -709,17 +734,16 @@ int launch_single(const dit_config& c, const dit_single_weights& w, float* x, in
   na.seg[0].seg_len = (int)S;
   DIT_CHECK(run_norm(na, st));
 
-  {
-    dit::GemmBatch g{};
-    g.count = 2;
-    g.p[0] = problem(h, D, w.w_in, D, (int)R, (int)(3 * D), (int)D, dit::EPI_QKV, nullptr, 0);
-    set_rows(g.p[0], (int)S, 0, 0);
-    g.p[1] = problem(h, D, bf(w.w_in) + 3 * D * D, D, (int)R, (int)F, (int)D, dit::EPI_SWIGLU,
-                     d6 + D, ld6);
-    const float* qg[2] = {w.q_gain, nullptr};
-    const float* kg[2] = {w.k_gain, nullptr};
-    DIT_CHECK(run_qkv(c, L, ws, g, qg, kg, cos_t, sin_t, B, S, st));
-  }
+  // The input projection's QKV part feeds the attention; its SwiGLU part
+  // does not, so its rows are split between the QKV launch and a launch
+  // fused with the attention (rows [0, m1) and [m1, R)), where its tiles fill
+  // the CUs the attention's last round leaves idle. The split depends on the
+  // shapes only; every element's arithmetic is the same either way.
+  dit::GemmProblem qkv = problem(h, D, w.w_in, D, (int)R, (int)(3 * D), (int)D, dit::EPI_QKV,
+                                 nullptr, 0);
+  set_rows(qkv, (int)S, 0, 0);
+  const dit::GemmProblem glu = problem(h, D, bf(w.w_in) + 3 * D * D, D, (int)R, (int)F, (int)D,
+                                       dit::EPI_SWIGLU, d6 + D, ld6);
   dit::AttnArgs aa{};
   aa.q = bf(at(ws, L.q));
   aa.k = bf(at(ws, L.k));
@@ -732,7 +756,29 @@ int launch_single(const dit_config& c, const dit_single_weights& w, float* x, in
   aa.B = B;
   aa.H = c.heads;
   aa.stream_major = 0;
-  DIT_CHECK(run_attention(aa, st));
+  const int64_t m1 = dit::fused_split_rows(qkv, glu, 128, aa);
+  {
+    dit::GemmBatch g{};
+    g.p[g.count++] = qkv;
+    if (m1 > 0) {
+      g.p[g.count] = glu;
+      g.p[g.count++].M = (int)m1;
+    }
+    const float* qg[2] = {w.q_gain, nullptr};
+    const float* kg[2] = {w.k_gain, nullptr};
+    DIT_CHECK(run_qkv(c, L, ws, g, qg, kg, cos_t, sin_t, B, S, st));
+  }
+  {
+    dit::GemmBatch g{};
+    if (m1 < R) {
+      dit::GemmProblem p = glu;
+      p.A = glu.A + m1 * D;
+      p.C = d6 + D + m1 * ld6;
+      p.M = (int)(R - m1);
+      g.p[g.count++] = p;
+    }
+    DIT_CHECK(run_attention_gemm(aa, g, st));
+  }
   {
     dit::GemmBatch g{};
     g.count = 1;

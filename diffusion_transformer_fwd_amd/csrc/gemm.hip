@@ -63,6 +63,7 @@
 #include "common.hpp"
 #include "kernels.hpp"
 #include "tile_map.hpp"
+#include "attention_unit.hpp"
 
 namespace dit {
 namespace {
@@ -574,12 +575,12 @@ __device__ __forceinline__ void gemm_tile(const GemmBatch& args, const GemmProbl
   }
 }
 
+// GEMM tile of launch index `block` of batch args.
 template <int BNT, int FAM>
-__global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const GemmBatch args) {
-  __shared__ u32x4 lds[LDS_U];
+__device__ __forceinline__ void gemm_block(const GemmBatch& args, int block, u32x4* lds) {
   int pi = 0, local = 0;
   const auto tiles_of = [&](int i) { return args.p[i].tiles_m * args.p[i].tiles_n; };
-  if (!tile_of_block<kMaxGemmProblems>(tiles_of, args.count, (int)blockIdx.x, &pi, &local))
+  if (!tile_of_block<kMaxGemmProblems>(tiles_of, args.count, block, &pi, &local))
     return;  // not reached: the grid has exactly one workgroup per tile
   pi = __builtin_amdgcn_readfirstlane(pi);
   local = __builtin_amdgcn_readfirstlane(local);
@@ -587,6 +588,35 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const GemmBatch args) 
   const GemmProblem& P = args.p[pi];
   if (P.fm == 3) gemm_tile<BNT, 3, FAM>(args, P, pi, local, lds);
   else gemm_tile<BNT, 2, FAM>(args, P, pi, local, lds);
+}
+
+template <int BNT, int FAM>
+__global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const GemmBatch args) {
+  __shared__ u32x4 lds[LDS_U];
+  gemm_block<BNT, FAM>(args, (int)blockIdx.x, lds);
+}
+
+// Fused launch: the attention units (blocks [0, n_attn), dealt to the XCDs
+// like the attention kernel's) and then the tiles of a bf16-family GEMM batch
+// that does not depend on them. The hardware hands out workgroups in launch
+// order, so the GEMM tiles start as attention units finish and fill the CUs
+// that the attention's last round would leave idle. Both parts run 8 waves
+// with two per SIMD; the attention uses the first 128 KiB of the LDS.
+struct AttnGemmArgs {
+  AttnArgs attn;
+  GemmBatch gemm;
+  int32_t n_attn;
+};
+
+__global__ __launch_bounds__(NT, 1) void attn_gemm_kernel(const AttnGemmArgs args) {
+  __shared__ u32x4 lds[LDS_U];
+  static_assert(att::NT == NT && att::LDS_BYTES <= LDS_U * 16, "one workgroup shape");
+  const int blk = (int)blockIdx.x;
+  if (blk < args.n_attn) {
+    att::attention_unit(args.attn, xcd_remap(blk, args.n_attn), reinterpret_cast<char*>(lds));
+    return;
+  }
+  gemm_block<BN, FAM_BF16>(args.gemm, blk - args.n_attn, lds);
 }
 
 // Compute units of the current device (cached per device).
@@ -624,19 +654,33 @@ int64_t tile_cost(int fm, int bnt, int64_t K) {
   return (int64_t)(4 * loads + 3 * mfmas) * (K / BK);
 }
 
-int64_t model_time(const GemmBatch& b, const int* fm, const int* order, int bnt, int cus_per_xcd) {
+// Model time of an attention unit over S keys, in tile_cost units: a unit
+// takes about 1.55 us per 64-key tile at S = 4608 next to 83 us for a
+// 256-row GEMM tile at K = 3072 (7680 units).
+int64_t attn_unit_cost(int64_t S) { return 143 * ((S + 63) / 64); }
+
+// Work ahead of the GEMM tiles in a fused launch (none for a plain one).
+struct Prefix {
+  int64_t units = 0;  // attention units of the launch
+  int64_t cost = 0;   // model cost of one
+};
+
+int64_t model_time(const GemmBatch& b, const int* fm, const int* order, int bnt, int cus_per_xcd,
+                   const Prefix& pre) {
   std::vector<int64_t> cu((size_t)std::max(cus_per_xcd, 1), 0);
+  auto place = [&](int64_t n, int64_t c) {
+    for (int64_t t = 0; t < n; ++t) {
+      auto it = std::min_element(cu.begin(), cu.end());
+      *it += c;
+    }
+  };
+  place((pre.units + 7) / 8, pre.cost);
   for (int oi = 0; oi < b.count; ++oi) {
     const GemmProblem& p = b.p[order[oi]];
     const int cols = p.epi == EPI_SWIGLU ? BN / 2 : bnt;
     const int64_t n = (int64_t)((p.M + 128 * fm[order[oi]] - 1) / (128 * fm[order[oi]])) *
                       ((p.N + cols - 1) / cols);
-    const int64_t share = (n + 7) / 8;
-    const int64_t c = tile_cost(fm[order[oi]], bnt, p.K);
-    for (int64_t t = 0; t < share; ++t) {
-      auto it = std::min_element(cu.begin(), cu.end());
-      *it += c;
-    }
+    place((n + 7) / 8, tile_cost(fm[order[oi]], bnt, p.K));
   }
   return *std::max_element(cu.begin(), cu.end());
 }
@@ -651,7 +695,7 @@ int forced_rows() {
   return v == 256 || v == 384 ? v : 0;
 }
 
-Plan make_plan(const GemmBatch& b, int cus, int forced) {
+Plan make_plan(const GemmBatch& b, int cus, int forced, const Prefix& pre, int64_t* time) {
   bool narrow_ok = true;
   for (int i = 0; i < b.count; ++i)
     if (b.p[i].epi == EPI_SWIGLU || b.p[i].epi == EPI_QKV) narrow_ok = false;
@@ -680,19 +724,20 @@ Plan make_plan(const GemmBatch& b, int cus, int forced) {
       for (int i = 0; i < b.count; ++i) pl.order[i] = i;
       std::stable_sort(pl.order, pl.order + b.count,
                        [&](int x, int y) { return pl.fm[x] > pl.fm[y]; });
-      const int64_t t = model_time(b, pl.fm, pl.order, bnt, cpx);
+      const int64_t t = model_time(b, pl.fm, pl.order, bnt, cpx, pre);
       if (best_t < 0 || t < best_t) {
         best_t = t;
         best = pl;
       }
     }
   }
+  if (time) *time = best_t;
   return best;
 }
 
-using PlanKey = std::tuple<int, int, int, std::vector<int64_t>>;
+using PlanKey = std::tuple<int, int, int64_t, int, std::vector<int64_t>>;
 
-Plan cached_plan(const GemmBatch& b, int cus) {
+Plan cached_plan(const GemmBatch& b, int cus, const Prefix& pre = Prefix{}) {
   const int forced = forced_rows();
   static std::mutex mu;
   static std::map<PlanKey, Plan> cache;
@@ -701,28 +746,26 @@ Plan cached_plan(const GemmBatch& b, int cus) {
     const GemmProblem& p = b.p[i];
     shape.insert(shape.end(), {(int64_t)p.M, (int64_t)p.N, (int64_t)p.K, (int64_t)p.epi});
   }
-  PlanKey key{cus, forced, b.count, shape};
+  shape.insert(shape.end(), {pre.units, pre.cost});
+  PlanKey key{cus, forced, 0, b.count, shape};
   std::lock_guard<std::mutex> lock(mu);
   auto it = cache.find(key);
   if (it != cache.end()) return it->second;
-  const Plan pl = make_plan(b, cus, forced);
+  const Plan pl = make_plan(b, cus, forced, pre, nullptr);
   if (cache.size() < 4096) cache.emplace(key, pl);
   return pl;
 }
 
 }  // namespace
 
-hipError_t gemm_launch(GemmBatch& batch, hipStream_t stream) {
-  for (int i = batch.count; i < kMaxGemmProblems; ++i) batch.p[i] = GemmProblem{};
-  if (batch.count < 1 || batch.count > kMaxGemmProblems) return hipErrorInvalidValue;
-  // one epilogue family per launch
-  auto is_f32 = [](int epi) { return epi == EPI_F32 || epi == EPI_RESID; };
-  const bool f32 = is_f32(batch.p[0].epi);
-  for (int i = 1; i < batch.count; ++i)
-    if (is_f32(batch.p[i].epi) != f32) return hipErrorInvalidValue;
-  const Plan pl = cached_plan(batch, device_cus());
-  // reorder the problems (and the per-problem QK gains) into launch order
-  GemmBatch b = batch;
+namespace {
+
+bool is_f32_epi(int epi) { return epi == EPI_F32 || epi == EPI_RESID; }
+
+// Applies plan pl to a copy of batch: launch order, tile heights and counts.
+// Returns the tile count (< 0 if it does not fit the grid).
+int64_t prepare(const GemmBatch& batch, const Plan& pl, GemmBatch& b) {
+  b = batch;
   for (int i = 0; i < batch.count; ++i) {
     b.p[i] = batch.p[pl.order[i]];
     b.qkv.q_gain[i] = batch.qkv.q_gain[pl.order[i]];
@@ -735,11 +778,32 @@ hipError_t gemm_launch(GemmBatch& batch, hipStream_t stream) {
     const int cols = p.epi == EPI_SWIGLU ? BN / 2 : pl.bnt;
     p.tiles_m = (p.M + 128 * p.fm - 1) / (128 * p.fm);
     p.tiles_n = (p.N + cols - 1) / cols;
-    p.tile_begin = (int32_t)total;
+    p.tile_begin = (int32_t)std::min<int64_t>(total, INT32_MAX);
     total += (int64_t)p.tiles_m * p.tiles_n;
   }
-  if (total > INT32_MAX) return hipErrorInvalidValue;
+  if (total > INT32_MAX) return -1;
   b.total_tiles = (int32_t)total;
+  return total;
+}
+
+bool valid_batch(GemmBatch& batch) {
+  for (int i = batch.count; i < kMaxGemmProblems; ++i) batch.p[i] = GemmProblem{};
+  if (batch.count < 1 || batch.count > kMaxGemmProblems) return false;
+  // one epilogue family per launch
+  for (int i = 1; i < batch.count; ++i)
+    if (is_f32_epi(batch.p[i].epi) != is_f32_epi(batch.p[0].epi)) return false;
+  return true;
+}
+
+}  // namespace
+
+hipError_t gemm_launch(GemmBatch& batch, hipStream_t stream) {
+  if (!valid_batch(batch)) return hipErrorInvalidValue;
+  const bool f32 = is_f32_epi(batch.p[0].epi);
+  const Plan pl = cached_plan(batch, device_cus());
+  GemmBatch b;
+  const int64_t total = prepare(batch, pl, b);
+  if (total < 0) return hipErrorInvalidValue;
   batch.total_tiles = b.total_tiles;
   if (total == 0) return hipSuccess;
   const dim3 grid((unsigned)total);
@@ -751,6 +815,75 @@ hipError_t gemm_launch(GemmBatch& batch, hipStream_t stream) {
   else
     hipLaunchKernelGGL((gemm_bf16_kernel<256, FAM_BF16>), grid, dim3(NT), 0, stream, b);
   return hipGetLastError();
+}
+
+hipError_t attn_gemm_launch(const AttnArgs& a, GemmBatch& batch, hipStream_t stream) {
+  if (batch.count == 0) return attention_launch(a, stream);
+  if (!valid_batch(batch) || is_f32_epi(batch.p[0].epi)) return hipErrorInvalidValue;
+  Prefix pre;
+  pre.units = att::attention_units(a);
+  pre.cost = attn_unit_cost(a.S);
+  const Plan pl0 = cached_plan(batch, device_cus(), pre);
+  Plan pl = pl0;
+  pl.bnt = BN;  // the fused kernel runs full-width tiles only
+  AttnGemmArgs args{};
+  args.attn = a;
+  args.n_attn = (int32_t)pre.units;
+  const int64_t total = prepare(batch, pl, args.gemm);
+  if (total < 0 || pre.units + total > INT32_MAX) return hipErrorInvalidValue;
+  batch.total_tiles = args.gemm.total_tiles;
+  hipLaunchKernelGGL(attn_gemm_kernel, dim3((unsigned)(pre.units + total)), dim3(NT), 0, stream,
+                     args);
+  return hipGetLastError();
+}
+
+int64_t fused_split_rows(const GemmProblem& first, const GemmProblem& rest, int64_t row_step,
+                         const AttnArgs& a) {
+  // DIT_FUSED_SPLIT_ROWS=m forces the split at min(m, rows) (tests compare
+  // splits bit for bit; timing runs compare them with the model's choice)
+  if (const char* e = std::getenv("DIT_FUSED_SPLIT_ROWS")) {
+    const long long v = std::atoll(e);
+    if (v >= 0) return std::min<int64_t>((int64_t)v, rest.M);
+  }
+  static std::mutex mu;
+  static std::map<std::vector<int64_t>, int64_t> cache;
+  const int cus = device_cus(), forced = forced_rows();
+  const std::vector<int64_t> key{cus, forced, row_step, first.M, first.N, first.K, first.epi,
+                                 rest.M, rest.N, rest.K, rest.epi, a.S, a.B, a.H};
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = cache.find(key);
+    if (it != cache.end()) return it->second;
+  }
+  Prefix pre;
+  pre.units = att::attention_units(a);
+  pre.cost = attn_unit_cost(a.S);
+  const int64_t R = rest.M;
+  int64_t best_rows = 0, best_t = -1;
+  for (int64_t m1 = 0; m1 <= R; m1 = (m1 + row_step > R && m1 < R) ? R : m1 + row_step) {
+    GemmBatch b1{}, b2{};
+    b1.p[b1.count++] = first;
+    if (m1 > 0) {
+      b1.p[b1.count] = rest;
+      b1.p[b1.count++].M = (int32_t)m1;
+    }
+    if (m1 < R) {
+      b2.p[b2.count] = rest;
+      b2.p[b2.count++].M = (int32_t)(R - m1);
+    }
+    int64_t t1 = 0, t2 = 0;
+    make_plan(b1, cus, forced, Prefix{}, &t1);
+    if (b2.count) make_plan(b2, cus, forced, pre, &t2);
+    else t2 = model_time(b2, nullptr, nullptr, BN, std::max(1, cus / 8), pre);
+    if (best_t < 0 || t1 + t2 < best_t) {
+      best_t = t1 + t2;
+      best_rows = m1;
+    }
+    if (m1 == R) break;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (cache.size() < 4096) cache.emplace(key, best_rows);
+  return best_rows;
 }
 
 }  // namespace dit

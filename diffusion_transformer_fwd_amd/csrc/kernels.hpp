@@ -143,6 +143,18 @@ struct AttnArgs {
 };
 hipError_t attention_launch(const AttnArgs& a, hipStream_t stream);
 
+// Attention fused with a bf16-family GEMM batch that does not depend on it
+// (one launch: the attention's work-groups first, then the GEMM tiles, which
+// fill the CUs of the attention's last round). An empty batch is a plain
+// attention launch.
+hipError_t attn_gemm_launch(const AttnArgs& a, GemmBatch& batch, hipStream_t stream);
+
+// For a GEMM launch of {first, rows [0, m) of rest} followed by a fused
+// launch of {attention a, rows [m, rest.M) of rest}: the m (a multiple of
+// row_step, or rest.M) that minimises the modelled time of the two launches.
+int64_t fused_split_rows(const GemmProblem& first, const GemmProblem& rest, int64_t row_step,
+                         const AttnArgs& a);
+
 // ------------------------------------------------------------------ small ops
 // RoPE tables from int32 positions [S, 4]: omega[a][j] given in double.
 struct RopeArgs {

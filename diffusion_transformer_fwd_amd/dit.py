@@ -28,9 +28,9 @@ EXPORTS = ("dit_position_ids", "dit_workspace_bytes", "dit_status_string", "dit_
            "dit_denoise_forward", "dit_profile_begin", "dit_profile_end",
            "dit_modulation_forward_noalloc")
 (K_GEMM, K_ATTENTION, K_MODNORM, K_QKV_PAD, K_GEMV, K_ROPE_TABLES, K_TIME, K_SPLIT_SUM, K_LATENT,
- K_COUNT) = range(10)
+ K_ATTN_GEMM, K_COUNT) = range(11)
 KERNEL_NAMES = ("gemm", "attention", "modnorm", "qkv_pad", "gemv", "rope_tables", "time_features",
-                "split_sum", "latent")
+                "split_sum", "latent", "attn_gemm")
 MAX_STEPS = 64
 
 

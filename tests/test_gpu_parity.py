@@ -305,6 +305,56 @@ def test_gemm_tile_heights_bitwise(case):
     assert np.array_equal(outs[256], outs[None]), "the launch plan's tiles differ"
 
 
+@contextlib.contextmanager
+def fused_split_rows(rows):
+    """Force the split of the single block's SwiGLU rows between the QKV
+    launch and the launch fused with the attention."""
+    old = os.environ.get("DIT_FUSED_SPLIT_ROWS")
+    os.environ["DIT_FUSED_SPLIT_ROWS"] = str(rows)
+    try:
+        yield
+    finally:
+        if old is None:
+            del os.environ["DIT_FUSED_SPLIT_ROWS"]
+        else:
+            os.environ["DIT_FUSED_SPLIT_ROWS"] = old
+
+
+FUSED_CASES = [
+    ("d256_refs_b3", {}, 17, (6, 6), ((3, 5), (2, 2)), 3),
+    ("d3072_s1300_b2", {"hidden": 3072, "heads": 24, "mlp_hidden": 9216}, 40, (30, 42), (), 2),
+    ("d3072_1024px", {"hidden": 3072, "heads": 24, "mlp_hidden": 9216}, 512, (64, 64), (), 1),
+]
+
+
+@pytest.mark.parametrize("case", FUSED_CASES, ids=[c[0] for c in FUSED_CASES])
+def test_single_block_fused_split_bitwise(case):
+    """The single block's SwiGLU rows go partly with the QKV projection and
+    partly into the launch fused with the attention; every split (none fused,
+    all fused, a ragged one, the model's) gives the same block bit for bit,
+    and it matches the oracle."""
+    name, kw, n_txt, grid, refs, B = case
+    cfg = small_cfg(**kw)
+    sig = [0.75, 0.4, 0.6][:B]
+    pos, S, xs, mod_d, cos_d, sin_d, mod_o, cos_o, sin_o = setup_block(cfg, n_txt, grid, refs, B, sig)
+    w = synth.single_weights(cfg, 0, 0)
+    ws = dit.SingleWeights(w)
+    R = B * S
+    outs = {}
+    for rows in (R, 0, 200, None):
+        ctx = fused_split_rows(rows) if rows is not None else contextlib.nullcontext()
+        with ctx:
+            x = torch.from_numpy(xs).cuda()
+            dit.single_block(cfg, ws, x, mod_d, cos_d, sin_d)
+            torch.cuda.synchronize()
+        outs[rows] = to_np(x)
+        log(f"fused split {name}: {rows if rows is not None else 'plan'} rows done")
+    for rows in (0, 200, None):
+        assert np.array_equal(outs[R], outs[rows]), f"split {rows} differs from no fusion"
+    want = O.single_block(xs, w, mod_o["single"], cos_o, sin_o, cfg.heads, cfg.eps, cfg.prenorm)
+    check_block(xs, outs[None], want, f"single fused {name}")
+
+
 def test_gemm_tile_heights_bitwise_step():
     """A small step (embeddings with a K-split, final projection, fp32
     epilogues) with 256-row and 384-row tiles: bitwise equal."""
