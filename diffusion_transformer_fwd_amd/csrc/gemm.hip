@@ -119,12 +119,15 @@ __device__ __forceinline__ void wait_vmcnt() {
 // v): a row's 128 accumulators sit in lanes l and l ^ 32 (64 each), so the
 // RMS is lane-local plus one cross-half exchange; each lane's runs of 4
 // columns hold two whole rotation pairs.
-// FAM: the epilogue family of the launch, FAM_F32 (EPI_F32 / EPI_RESID) or
-// FAM_BF16 (EPI_BF16 / EPI_SWIGLU / EPI_QKV); one kernel per family keeps the
-// register allocation of each within the budget at 384 rows.
+// FAM: the epilogue family of a launch, FAM_F32 (EPI_F32 / EPI_RESID) or
+// FAM_BF16 (EPI_BF16 / EPI_SWIGLU / EPI_QKV): one kernel per family. EK: the
+// epilogue code a tile instantiation carries (EK_F32, EK_QKV, or EK_BF16 for
+// EPI_BF16 / EPI_SWIGLU); each has its own copy of the main loop, which keeps
+// every instantiation's registers within the budget at 384 rows.
 enum { FAM_BF16 = 0, FAM_F32 = 1 };
+enum { EK_BF16 = 0, EK_QKV = 1, EK_F32 = 2 };
 
-template <int BNT, int FM, int FAM>
+template <int BNT, int FM, int EK>
 __device__ __forceinline__ void gemm_tile(const GemmBatch& args, const GemmProblem& P, int pi,
                                           int local, u32x4* lds) {
   constexpr int BM = 128 * FM, WTM = 32 * FM;
@@ -334,7 +337,7 @@ __device__ __forceinline__ void gemm_tile(const GemmBatch& args, const GemmProbl
     return (int64_t)b * P.seg_stride + P.seg_off + (gr - b * P.seg_len);
   };
 
-  if (FAM == FAM_F32) {
+  if (EK == EK_F32) {
     // fp32 stage [128][256] per pass: pass p holds accumulator block i = p
     // of every wave (stage row r is tile row (r / 32) WTM + 32 p + r % 32),
     // so each pass frees its registers; 16-byte chunk c of row r at c ^ (r & 31)
@@ -394,34 +397,135 @@ __device__ __forceinline__ void gemm_tile(const GemmBatch& args, const GemmProbl
     return;
   }
 
-  // bf16 results in passes of up to two accumulator blocks of every wave
-  // (the whole tile at 256 rows; blocks {0, 1} then {2} at 384 rows: a
-  // 384 x 256 bf16 stage would not fit the LDS). In pass p with nb blocks,
-  // stage row r is tile row (r / (32 nb)) WTM + 32 (2 p + (r / 32) % nb) + r % 32.
-  constexpr int NPASS = (FM + 1) / 2;
-  const bool qk_head = epi == EPI_QKV && tn * BN + wn * WTN < N &&
-                       (tn * BN + wn * WTN) / args.qkv.D < 2;
-  float* const row_scale = reinterpret_cast<float*>(T + RS_BYTE);  // [2][BM]
-  if (qk_head) {
-    // q or k head (the wave's 128 columns): the row's 1 / rms (times q_scale
-    // for q) from the fp32 accumulators, kept per row in LDS (outside every
-    // pass's stage); a row's 128 values sit in lanes l and l ^ 32, so the sum
-    // of squares needs one cross-half exchange. The values are staged raw;
-    // gain and rotation are applied on the way out, where 16 lanes share a
-    // token row.
+  if (EK == EK_QKV) {
+    // fp32 stage [128][256] per pass, laid out like the fp32 family's: pass p
+    // holds accumulator block i = p of every wave, so q and k are rounded to
+    // bf16 once, after the norm, gain and rotation. A row's 1 / rms (times
+    // q_scale for q) comes from the fp32 accumulators first and is kept per
+    // row in LDS (outside every pass's stage); a row's 128 values of a head
+    // sit in lanes l and l ^ 32, so the sum of squares needs one cross-half
+    // exchange.
     const QkvEpilogue& E = args.qkv;
-    const float sc = (tn * BN + wn * WTN) / E.D == 0 ? E.q_scale : 1.f;
+    float* const row_scale = reinterpret_cast<float*>(T + RS_BYTE);  // [2][BM]
+    const int wcol0 = tn * BN + wn * WTN;  // first projection column of the wave
+    if (wcol0 < N && wcol0 / E.D < 2) {
+      const float sc = wcol0 / E.D == 0 ? E.q_scale : 1.f;
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      float ss = 0.f;
+      for (int i = 0; i < FM; ++i) {
+        float ss = 0.f;
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) ss += acc[i][j][e] * acc[i][j][e];
+        ss = half_sum(ss);
+        if (fg == 0)
+          row_scale[wn * BM + wm * WTM + i * 32 + fr] = rsqrtf(ss * (1.f / 128.f) + E.eps) * sc;
+      }
+    }
+#pragma unroll
+    for (int pass = 0; pass < FM; ++pass) {
 #pragma unroll
       for (int j = 0; j < FN; ++j)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) ss += acc[i][j][e] * acc[i][j][e];
-      ss = half_sum(ss);
-      if (fg == 0) row_scale[wn * BM + wm * WTM + i * 32 + fr] = rsqrtf(ss * (1.f / 128.f) + E.eps) * sc;
+        for (int q = 0; q < 4; ++q) {
+          const int r = wm * 32 + fr;
+          const int c = (wn * WTN + j * 32 + 8 * q + 4 * fg) >> 2;
+          f32x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = acc[pass][j][4 * q + e];
+          *reinterpret_cast<f32x4*>(T + r * 1024 + ((c ^ (r & 31)) << 4)) = v;
+        }
+      __syncthreads();
+      // stage row r is tile row (r / 32) WTM + 32 pass + r % 32
+      auto tile_row = [&](int r) { return (r >> 5) * WTM + 32 * pass + (r & 31); };
+      auto stage_f32 = [&](int r, int col) -> const float* {  // tile column col of stage row r
+        return reinterpret_cast<const float*>(T + r * 1024 + ((((col >> 2) ^ (r & 31))) << 4)) +
+               (col & 3);
+      };
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int col0 = tn * BN + hh * 128;
+        if (col0 >= N) break;
+        const int part = col0 / E.D;
+        const int h = (col0 - part * E.D) >> 7;
+        if (part < 2) {
+          // q / k rows to [b, h, s, :]: 16 lanes per token row, 8 columns (4
+          // rotation pairs) per lane
+          bf16_t* base = part == 0 ? E.q : E.k;
+          const float* gain = part == 0 ? E.q_gain[pi] : E.k_gain[pi];
+          const int cl = (tid & 15) * 8;  // column within the head
+          const f32x4 g0 = *reinterpret_cast<const f32x4*>(gain + cl);
+          const f32x4 g1 = *reinterpret_cast<const f32x4*>(gain + cl + 4);
+#pragma unroll 2
+          for (int it = 0; it < 128 * 16 / NT; ++it) {
+            const int r = (it * NT + tid) >> 4;
+            const int tr = tile_row(r);
+            const int gr = m0 + tr;
+            if (gr >= M) continue;
+            const int b = gr / P.seg_len;
+            const int s = P.seg_off + (gr - b * P.seg_len);
+            const f32x4 v0 = *reinterpret_cast<const f32x4*>(stage_f32(r, hh * 128 + cl));
+            const f32x4 v1 = *reinterpret_cast<const f32x4*>(stage_f32(r, hh * 128 + cl + 4));
+            const float rsc = row_scale[hh * BM + tr];
+            const f32x4 co = *reinterpret_cast<const f32x4*>(E.cos_t + (int64_t)s * 64 + (cl >> 1));
+            const f32x4 si = *reinterpret_cast<const f32x4*>(E.sin_t + (int64_t)s * 64 + (cl >> 1));
+            f32x8 y;
+#pragma unroll
+            for (int pr = 0; pr < 4; ++pr) {
+              const float gx0 = pr < 2 ? g0[2 * pr] : g1[2 * pr - 4];
+              const float gx1 = pr < 2 ? g0[2 * pr + 1] : g1[2 * pr - 3];
+              const float a0 = pr < 2 ? v0[2 * pr] : v1[2 * pr - 4];
+              const float a1 = pr < 2 ? v0[2 * pr + 1] : v1[2 * pr - 3];
+              const float x0 = a0 * rsc * gx0;
+              const float x1 = a1 * rsc * gx1;
+              y[2 * pr] = x0 * co[pr] - x1 * si[pr];
+              y[2 * pr + 1] = x0 * si[pr] + x1 * co[pr];
+            }
+            *reinterpret_cast<bf16x8*>(base + (((int64_t)b * E.H + h) * E.S_pad + s) * 128 + cl) =
+                pack_bf16x8(y);
+          }
+        } else {
+          // v to v^T[b, h, d, s..s+7]: 8 tokens per dim and lane
+#pragma unroll 2
+          for (int it = 0; it < 128 * 16 / NT; ++it) {
+            const int u = it * NT + tid;
+            const int d = u & 127, tg = u >> 7;  // dim, group of 8 stage rows
+            f32x8 tv;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) tv[e] = *stage_f32(tg * 8 + e, hh * 128 + d);
+            const bf16x8 tb = pack_bf16x8(tv);
+            const int r0 = m0 + tile_row(tg * 8);  // 8 stage rows = 8 tile rows
+            if (r0 >= M) continue;
+            const int b0 = r0 / P.seg_len;
+            const int s0 = P.seg_off + (r0 - b0 * P.seg_len);
+            if (r0 + 7 < M && (r0 + 7) / P.seg_len == b0 && (s0 & 7) == 0) {
+              *reinterpret_cast<bf16x8*>(E.vt + (((int64_t)b0 * E.H + h) * 128 + d) * E.S_pad + s0) = tb;
+            } else {
+              const u32x4 tw = __builtin_bit_cast(u32x4, tb);
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                const int gr = r0 + e;
+                if (gr >= M) break;
+                const int b = gr / P.seg_len;
+                const int s = P.seg_off + (gr - b * P.seg_len);
+                E.vt[(((int64_t)b * E.H + h) * 128 + d) * E.S_pad + s] =
+                    (bf16_t)((tw[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+              }
+            }
+          }
+        }
+      }
+      if (pass + 1 < FM) __syncthreads();  // the next pass overwrites the stage
     }
+    return;
   }
+
+  // bf16 results (SwiGLU, plain bf16) in passes of up to two accumulator
+  // blocks of every wave (the whole tile at 256 rows; blocks {0, 1} then {2}
+  // at 384 rows: a 384 x 256 bf16 stage would not fit the LDS). In pass p
+  // with nb blocks, stage row r is tile row
+  // (r / (32 nb)) WTM + 32 (2 p + (r / 32) % nb) + r % 32.
+  constexpr int NPASS = (FM + 1) / 2;
   // every result as bf16, packed 4 per register pair: half the registers of
   // the accumulators, which the later passes would otherwise hold through
   // the earlier passes' stores (SwiGLU: the gate and up halves combine
@@ -459,8 +563,7 @@ __device__ __forceinline__ void gemm_tile(const GemmBatch& args, const GemmProbl
     for (int i = 0; i < FM; ++i) {
       if (i / BPP != pass) continue;
       const int r = wm * 32 * nb + (i - BPP * pass) * 32 + fr;
-      // SwiGLU: 64 output columns per wave; plain bf16 and the raw q / k / v
-      // values of EPI_QKV: 128
+      // SwiGLU: 64 output columns per wave; plain bf16: 128
       const int nj = epi == EPI_SWIGLU ? FN / 2 : FN;
       const int cw = epi == EPI_SWIGLU ? WTN / 2 : WTN;
 #pragma unroll
@@ -477,99 +580,18 @@ __device__ __forceinline__ void gemm_tile(const GemmBatch& args, const GemmProbl
     __syncthreads();
 
     // phase B: whole rows out, 16 bytes per lane
-    if (epi != EPI_QKV) {
-      const int ncol = epi == EPI_SWIGLU ? BN / 2 : BNT;  // output columns of the tile
-      const int upr = ncol / 8;                          // 16-byte units per row
+    const int ncol = epi == EPI_SWIGLU ? BN / 2 : BNT;  // output columns of the tile
+    const int upr = ncol / 8;                          // 16-byte units per row
 #pragma unroll 4
-      for (int it = 0; it < 256 * (BN / 8) / NT; ++it) {
-        const int u = it * NT + tid;
-        if (u >= prow * upr) break;
-        const int r = u / upr, c = u - r * upr;
-        const int gr = m0 + tile_row(r), col = tn * ncol + c * 8;
-        if (gr >= M || col >= N) continue;
-        int b;
-        *reinterpret_cast<u32x4*>(static_cast<bf16_t*>(P.C) + out_row_of(gr, b) * P.ldc + col) =
-            *reinterpret_cast<const u32x4*>(T + r * 512 + ((c ^ (r & 31)) << 4));
-      }
-    } else {
-      // EPI_QKV: per 128-column head of the tile: q / k rows to [b, h, s, :]
-      // (16 lanes per token), v gathered 8 tokens per dim to v^T[b, h, d, s..s+7]
-      const QkvEpilogue& E = args.qkv;
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int col0 = tn * BN + hh * 128;
-        if (col0 >= N) break;
-        const int part = col0 / E.D;
-        const int h = (col0 - part * E.D) >> 7;
-        if (part < 2) {
-          // 16 lanes per token row, 8 columns (4 rotation pairs) per lane
-          bf16_t* base = part == 0 ? E.q : E.k;
-          const float* gain = part == 0 ? E.q_gain[pi] : E.k_gain[pi];
-          const int cl = (tid & 15) * 8;  // column within the head
-          const f32x4 g0 = *reinterpret_cast<const f32x4*>(gain + cl);
-          const f32x4 g1 = *reinterpret_cast<const f32x4*>(gain + cl + 4);
-#pragma unroll 2
-          for (int it = 0; it < 256 * 16 / NT; ++it) {
-            const int u = it * NT + tid;
-            const int r = u >> 4, c = hh * 16 + (u & 15);
-            if (r >= prow) break;
-            const int tr = tile_row(r);
-            const int gr = m0 + tr;
-            if (gr >= M) continue;
-            const int b = gr / P.seg_len;
-            const int s = P.seg_off + (gr - b * P.seg_len);
-            const u32x4 raw = *reinterpret_cast<const u32x4*>(T + r * 512 + ((c ^ (r & 31)) << 4));
-            const float rsc = row_scale[hh * BM + tr];
-            const f32x4 co = *reinterpret_cast<const f32x4*>(E.cos_t + (int64_t)s * 64 + (cl >> 1));
-            const f32x4 si = *reinterpret_cast<const f32x4*>(E.sin_t + (int64_t)s * 64 + (cl >> 1));
-            f32x8 y;
-#pragma unroll
-            for (int pr = 0; pr < 4; ++pr) {
-              const float gx0 = pr < 2 ? g0[2 * pr] : g1[2 * pr - 4];
-              const float gx1 = pr < 2 ? g0[2 * pr + 1] : g1[2 * pr - 3];
-              const float x0 = bf16_to_f32(raw[pr] & 0xFFFFu) * rsc * gx0;
-              const float x1 = bf16_to_f32(raw[pr] >> 16) * rsc * gx1;
-              y[2 * pr] = x0 * co[pr] - x1 * si[pr];
-              y[2 * pr + 1] = x0 * si[pr] + x1 * co[pr];
-            }
-            *reinterpret_cast<bf16x8*>(base + (((int64_t)b * E.H + h) * E.S_pad + s) * 128 + cl) =
-                pack_bf16x8(y);
-          }
-        } else {
-#pragma unroll 2
-          for (int it = 0; it < 256 * 16 / NT; ++it) {
-            const int u = it * NT + tid;
-            const int d = u & 127, tg = u >> 7;  // dim, group of 8 tokens
-            if (tg * 8 >= prow) break;
-            const int colb = ((hh * 128 + d) >> 3), wb = (d & 7) << 1;
-            uint16_t tok[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const int r = tg * 8 + e;
-              tok[e] = *reinterpret_cast<const uint16_t*>(T + r * 512 + ((colb ^ (r & 31)) << 4) + wb);
-            }
-            const int r0 = m0 + tile_row(tg * 8);  // 8 stage rows = 8 tile rows
-            if (r0 >= M) continue;
-            const int b0 = r0 / P.seg_len;
-            const int s0 = P.seg_off + (r0 - b0 * P.seg_len);
-            if (r0 + 7 < M && (r0 + 7) / P.seg_len == b0 && (s0 & 7) == 0) {
-              u32x4 pk;
-#pragma unroll
-              for (int e = 0; e < 4; ++e) pk[e] = (uint32_t)tok[2 * e] | ((uint32_t)tok[2 * e + 1] << 16);
-              *reinterpret_cast<u32x4*>(E.vt + (((int64_t)b0 * E.H + h) * 128 + d) * E.S_pad + s0) = pk;
-            } else {
-#pragma unroll
-              for (int e = 0; e < 8; ++e) {
-                const int gr = r0 + e;
-                if (gr >= M) break;
-                const int b = gr / P.seg_len;
-                const int s = P.seg_off + (gr - b * P.seg_len);
-                E.vt[(((int64_t)b * E.H + h) * 128 + d) * E.S_pad + s] = tok[e];
-              }
-            }
-          }
-        }
-      }
+    for (int it = 0; it < 256 * (BN / 8) / NT; ++it) {
+      const int u = it * NT + tid;
+      if (u >= prow * upr) break;
+      const int r = u / upr, c = u - r * upr;
+      const int gr = m0 + tile_row(r), col = tn * ncol + c * 8;
+      if (gr >= M || col >= N) continue;
+      int b;
+      *reinterpret_cast<u32x4*>(static_cast<bf16_t*>(P.C) + out_row_of(gr, b) * P.ldc + col) =
+          *reinterpret_cast<const u32x4*>(T + r * 512 + ((c ^ (r & 31)) << 4));
     }
     if (pass + 1 < NPASS) __syncthreads();  // the next pass overwrites the stage
   }
@@ -586,8 +608,16 @@ __device__ __forceinline__ void gemm_block(const GemmBatch& args, int block, u32
   local = __builtin_amdgcn_readfirstlane(local);
   // fields are read from the kernel arguments (scalar loads) as needed
   const GemmProblem& P = args.p[pi];
-  if (P.fm == 3) gemm_tile<BNT, 3, FAM>(args, P, pi, local, lds);
-  else gemm_tile<BNT, 2, FAM>(args, P, pi, local, lds);
+  if (FAM == FAM_F32) {
+    if (P.fm == 3) gemm_tile<BNT, 3, EK_F32>(args, P, pi, local, lds);
+    else gemm_tile<BNT, 2, EK_F32>(args, P, pi, local, lds);
+  } else if (P.epi == EPI_QKV) {
+    if (P.fm == 3) gemm_tile<BNT, 3, EK_QKV>(args, P, pi, local, lds);
+    else gemm_tile<BNT, 2, EK_QKV>(args, P, pi, local, lds);
+  } else {
+    if (P.fm == 3) gemm_tile<BNT, 3, EK_BF16>(args, P, pi, local, lds);
+    else gemm_tile<BNT, 2, EK_BF16>(args, P, pi, local, lds);
+  }
 }
 
 template <int BNT, int FAM>
