@@ -1,0 +1,114 @@
+// Host-side planning and argument checks of libdit.so: workspace layouts,
+// validation of every entry point's arguments (all of it runs before the
+// first launch, so an error leaves device memory untouched), the thread-local
+// error message, and the host-only entry points (position ids, workspace
+// sizes, status strings). Plain C++ with no HIP dependency, so it also builds
+// with a host compiler and its sanitizers.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/dit.h"
+
+#define DIT_CHECK(status)                                                         \
+  do {                                                                            \
+    const int s_ = (status);                                                      \
+    if (s_ != DIT_OK) return s_;                                                  \
+  } while (0)
+
+namespace dit {
+namespace host {
+
+constexpr size_t kAlign = 256;
+constexpr uint64_t kMaxBufferBytes = 0xFFFFFFFFull;  // 32-bit buffer offsets
+
+// Records a printf-style message as the thread's last error; returns status.
+int fail(int status, const char* fmt, ...);
+// The calling thread's last message.
+const char* last_error_message();
+
+size_t align_up(size_t v);
+int64_t round_up(int64_t v, int64_t m);
+bool aligned(const void* p, size_t a);
+
+// Workspace regions (byte offsets, each 256-byte aligned) of one block call,
+// kind 0 = dual, 1 = single.
+struct BlockLayout {
+  int64_t R = 0, S_pad = 0;
+  int64_t u_cols = 0;
+  size_t h = 0, u = 0, d6 = 0, o = 0, q = 0, k = 0, vt = 0, total = 0;
+};
+BlockLayout block_layout(const dit_config& c, int kind, int64_t B, int64_t S);
+
+// The modulation's intermediate vectors.
+struct ModLayout {
+  size_t e = 0, t1 = 0, m = 0, total = 0;
+};
+ModLayout mod_layout(const dit_config& c, int64_t B);
+
+// One step: residual, modulation result, the modulation's and a block's
+// workspace.
+struct StepLayout {
+  size_t x = 0, mod = 0, modws = 0, block = 0, total = 0;
+};
+StepLayout step_layout(const dit_config& c, int64_t B, int64_t S);
+
+// Steps whose modulation vectors one pass over the modulation weights
+// computes in the sampling loop.
+constexpr int kModSteps = 4;
+
+// The sampling loop: a step's workspace, the latent operand and velocity, the
+// modulation of kModSteps steps and the embedded text rows.
+struct DenoiseLayout {
+  size_t step = 0, lat = 0, v = 0, mods = 0, modws = 0, txt = 0, total = 0;
+};
+DenoiseLayout denoise_layout(const dit_config& c, int64_t B, int64_t S);
+
+// K chunks of a GEMM that runs K-split (depends on N and K only).
+int split_k_chunks(int64_t N, int64_t K);
+
+// Checks shared by the entry points.
+int check_config(const dit_config* c);
+int check_batch_seq(int32_t B, int64_t S);
+int check_ws(const void* ws, size_t have, size_t need);
+int check_ptr(const void* p, const char* what, size_t align = 16);
+int check_operand_sizes(const dit_config& c, int64_t rows);
+int check_dual_weights(const dit_dual_weights* w);
+int check_single_weights(const dit_single_weights* w);
+int check_model_weights(const dit_config& c, const dit_model_weights* w, bool blocks);
+int check_sigmas(const float* sigma, int32_t B);
+int check_block_common(const dit_config* cfg, float* x, int32_t B, int64_t S,
+                       int64_t mod_batch_stride, const float* cos_t, const float* sin_t);
+int check_step_args(const dit_config* cfg, const dit_model_weights* w, const void* txt,
+                    int32_t B, int64_t n_txt, int64_t n_img, int64_t n_ref,
+                    const float* cos_dev, const float* sin_dev);
+
+// All argument checks of each device entry point, in the order the entry
+// point runs them; DIT_OK means the call may launch. ws_bytes / ws of the
+// no-allocation modulation are ignored there (noalloc = true checks the
+// fixed scratch capacity instead).
+int validate_rope(const dit_config* cfg, const int32_t* pos_dev, int64_t S, const float* cos_dev,
+                  const float* sin_dev);
+int validate_modulation(const dit_config* cfg, const dit_model_weights* w,
+                        const float* sigma_host, int32_t B, const float* mod_dev, const void* ws,
+                        size_t ws_bytes, bool noalloc);
+int validate_dual(const dit_config* cfg, const dit_dual_weights* w, float* x, int32_t B,
+                  int64_t S, int64_t n_txt, const float* mod_txt, const float* mod_img,
+                  int64_t mod_batch_stride, const float* cos_dev, const float* sin_dev,
+                  const void* ws, size_t ws_bytes);
+int validate_single(const dit_config* cfg, const dit_single_weights* w, float* x, int32_t B,
+                    int64_t S, const float* mod, int64_t mod_batch_stride, const float* cos_dev,
+                    const float* sin_dev, const void* ws, size_t ws_bytes);
+int validate_step(const dit_config* cfg, const dit_model_weights* w, const void* txt,
+                  const void* latents, const float* sigma_host, int32_t B, int64_t n_txt,
+                  int64_t n_img, int64_t n_ref, const float* cos_dev, const float* sin_dev,
+                  const float* v_out, const void* ws, size_t ws_bytes);
+int validate_denoise(const dit_config* cfg, const dit_model_weights* w, const void* txt,
+                     const float* z, const void* ref, const float* sigmas_host, int32_t n_steps,
+                     int32_t B, int64_t n_txt, int64_t n_img, int64_t n_ref,
+                     const float* cos_dev, const float* sin_dev, const void* ws,
+                     size_t ws_bytes);
+
+}  // namespace host
+}  // namespace dit

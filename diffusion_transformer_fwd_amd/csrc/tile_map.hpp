@@ -34,7 +34,9 @@ DIT_HD inline bool tile_of_block(const TilesOf& tiles_of, int count, int block, 
   const int x = block & 7;
   int k = block >> 3;
   int start = 0;  // first XCD of the current problem's window
+#if defined(__HIPCC__)
 #pragma unroll
+#endif
   for (int i = 0; i < MAXP; ++i) {
     if (i >= count) break;
     const int n = tiles_of(i), q = n >> 3, r = n & 7;
