@@ -205,15 +205,20 @@ __global__ __launch_bounds__(256) void time_features_kernel(const TimeArgs a) {
 constexpr int kGemvMaxB = 4;
 constexpr int kGemvMaxK = 4096;
 __global__ __launch_bounds__(256) void gemv_kernel(const GemvArgs a) {
-  extern __shared__ float xs_dyn[];  // [B][K]
+  // x as [B][2][K / 8][4]: element k = 8 c + e of row b at ((2 b + e / 4) K/8 + c) 4 + e % 4,
+  // so the lanes of a wave, which take consecutive chunks c, read consecutive
+  // 16-byte words (a plain [B][K] layout has them 32 bytes apart, which
+  // conflicts on the LDS banks)
+  extern __shared__ float xs_dyn[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int K8 = a.K >> 3;
   for (int i = tid; i < a.B * a.K; i += 256) {
     const int b = i / a.K, k = i - b * a.K;
-    float v = a.x[(int64_t)b * a.K + k];
-    xs_dyn[i] = a.act_in == ACT_SILU ? silu_f(v) : v;
+    const float v = a.x[(int64_t)b * a.K + k];
+    const int c = k >> 3, e = k & 7;
+    xs_dyn[((2 * b + (e >> 2)) * K8 + c) * 4 + (e & 3)] = a.act_in == ACT_SILU ? silu_f(v) : v;
   }
   __syncthreads();
-  const int K8 = a.K >> 3;
   for (int row = blockIdx.x * 4 + wave; row < a.total_rows; row += gridDim.x * 4) {
     int si = 0;
 #pragma unroll
@@ -243,9 +248,12 @@ __global__ __launch_bounds__(256) void gemv_kernel(const GemvArgs a) {
 #pragma unroll
       for (int b = 0; b < kGemvMaxB; ++b) {
         if (b < a.B) {
-          const float* xb = &xs_dyn[b * a.K + c * 8];
+          const f32x4 x0 = *reinterpret_cast<const f32x4*>(&xs_dyn[((2 * b) * K8 + c) * 4]);
+          const f32x4 x1 = *reinterpret_cast<const f32x4*>(&xs_dyn[((2 * b + 1) * K8 + c) * 4]);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[b] += wv[e] * xb[e];
+          for (int e = 0; e < 4; ++e) acc[b] += wv[e] * x0[e];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[b] += wv[4 + e] * x1[e];
         }
       }
     }
