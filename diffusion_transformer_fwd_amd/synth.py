@@ -266,3 +266,114 @@ def step_inputs(cfg: DitConfig, wl: Workload, batch_row: int = 0,
         "txt": text_embedding(cfg, s, wl.n_txt),
         "latents": np.concatenate(lat, axis=0),
     }
+
+
+# ---------------------------------------------------------------- VAE decoder
+
+@dataclasses.dataclass(frozen=True)
+class VaeConfig:
+    """Shape of the latent decoder (a reading; the pages give none: they say
+    only that the decoder runs on the card, has GroupNorm layers and takes
+    non-square images, "flux2-klein-p100a", What this port adds).
+
+    block_channels lists the encoder-order widths; the decoder's up levels
+    run them in reverse (512, 512, 256, 128 for the default), each with
+    `layers` ResNet blocks and, except the last, a 2x upsample.
+    """
+    z_channels: int = 32
+    block_channels: Tuple[int, ...] = (128, 256, 512, 512)
+    layers: int = 3
+    groups: int = 32
+    eps: float = 1e-6
+    out_channels: int = 3
+
+    @property
+    def top(self) -> int:
+        return self.block_channels[-1]
+
+    @property
+    def level_channels(self) -> Tuple[int, ...]:
+        return tuple(reversed(self.block_channels))
+
+    def resnet_channels(self):
+        """[(name, c_in, c_out)] of every ResNet block in execution order."""
+        out = [("mid.res0.", self.top, self.top), ("mid.res1.", self.top, self.top)]
+        c = self.top
+        for lv, co in enumerate(self.level_channels):
+            for r in range(self.layers):
+                out.append((f"up{lv}.res{r}.", c, co))
+                c = co
+        return out
+
+
+VAE_KLEIN = VaeConfig()
+# Small decoder for element-wise tests: both identity and 1x1 shortcuts,
+# 1, 2 and 4 channels per group.
+VAE_TINY = VaeConfig(block_channels=(32, 64, 64, 128), layers=2)
+
+
+def _conv_w(seed: int, name: str, c_out: int, k: int, c_in: int) -> np.ndarray:
+    """[c_out, k, k, c_in] conv weight, N(0, 1 / (k k c_in))."""
+    return normal(seed, name, (c_out, k, k, c_in), std=1.0 / np.sqrt(k * k * c_in))
+
+
+def _bias(seed: int, name: str, n: int) -> np.ndarray:
+    return normal(seed, name, (n,), std=0.02)
+
+
+def vae_weights(vcfg: VaeConfig, seed: int = 0) -> Dict[str, np.ndarray]:
+    """Decoder weights by dotted name (float32 storage of bf16 values).
+
+    Conv weights are [C_out, kh, kw, C_in]; GroupNorm gains are
+    1 + 0.1 N(0, 1), GroupNorm shifts 0.1 N(0, 1), biases N(0, 0.02^2); the
+    latent affine acts on the 4 z_channels token channels.
+    """
+    z, top = vcfg.z_channels, vcfg.top
+    w: Dict[str, np.ndarray] = {
+        "lat_scale": normal(seed, "vae.lat_scale", (4 * z,), std=0.1, mean=1.0),
+        "lat_shift": normal(seed, "vae.lat_shift", (4 * z,), std=0.1),
+        "conv_in.w": _conv_w(seed, "vae.conv_in.w", top, 3, z),
+        "conv_in.b": _bias(seed, "vae.conv_in.b", top),
+    }
+
+    def gn(p: str, c: int):
+        w[p + "g"] = normal(seed, "vae." + p + "g", (c,), std=0.1, mean=1.0)
+        w[p + "b"] = normal(seed, "vae." + p + "b", (c,), std=0.1)
+
+    def conv(p: str, co: int, k: int, ci: int):
+        w[p + "w"] = _conv_w(seed, "vae." + p + "w", co, k, ci)
+        w[p + "b"] = _bias(seed, "vae." + p + "b", co)
+
+    for p, ci, co in vcfg.resnet_channels():
+        gn(p + "gn1.", ci)
+        conv(p + "conv1.", co, 3, ci)
+        gn(p + "gn2.", co)
+        conv(p + "conv2.", co, 3, co)
+        if ci != co:
+            conv(p + "short.", co, 1, ci)
+    gn("mid.attn.gn.", top)
+    for t in "qkvo":
+        conv(f"mid.attn.{t}.", top, 1, top)
+    for lv, co in enumerate(vcfg.level_channels[:-1]):
+        conv(f"up{lv}.upconv.", co, 3, co)
+    c0 = vcfg.level_channels[-1]
+    gn("norm_out.", c0)
+    conv("conv_out.", vcfg.out_channels, 3, c0)
+    return w
+
+
+def vae_latents(vcfg: VaeConfig, seed: int, hp: int, wp: int) -> np.ndarray:
+    """Image tokens [hp * wp, 4 z] as the sampler leaves them, N(0, 1)."""
+    return normal(seed, "vae.input.z", (hp * wp, 4 * vcfg.z_channels))
+
+
+@dataclasses.dataclass(frozen=True)
+class VaeWorkload:
+    """One decode: batch and token grid (hp, wp); the image is 16 hp x 16 wp."""
+    name: str
+    batch: int
+    grid: Tuple[int, int]
+
+
+V_DECODE_1024 = VaeWorkload("vae_decode_1024px", 1, (64, 64))
+V_DECODE_1920x1088_B4 = VaeWorkload("vae_decode_1920x1088_b4", 4, (68, 120))

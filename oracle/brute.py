@@ -231,3 +231,110 @@ def step(cfg, weights, txt, lat, sigma: float, n_img: int, pos) -> List[List[flo
     fm = mod["final"]
     wo = _l(gw["proj_out"])
     return [matvec(wo, adaln(x[t], fm[0], fm[1], eps, layer)) for t in range(n_txt, n_txt + n_img)]
+
+
+# ------------------------------------------------------------ latent decoder
+# Loop versions of the decoder's primitives for one sample, images as nested
+# [H][W][C] lists, conv weights as [O][k][k][C] (the readings of the
+# decoder's header in vae_oracle: cross-correlation with zero padding,
+# GroupNorm over consecutive channel runs, nearest 2x upsampling, 2x2
+# patches with token channel 4k + 2i + j).
+
+def conv_image(x, w, b=None):
+    x, w = _l(x), _l(w)
+    H, W, C = len(x), len(x[0]), len(x[0][0])
+    O, k = len(w), len(w[0])
+    p = k // 2
+    out = [[[0.0] * O for _ in range(W)] for _ in range(H)]
+    for y in range(H):
+        for xx in range(W):
+            for o in range(O):
+                s = 0.0 if b is None else float(_l(b)[o])
+                for ky in range(k):
+                    yy = y + ky - p
+                    if yy < 0 or yy >= H:
+                        continue
+                    for kx in range(k):
+                        xs = xx + kx - p
+                        if xs < 0 or xs >= W:
+                            continue
+                        px, wk = x[yy][xs], w[o][ky][kx]
+                        for c in range(C):
+                            s += px[c] * wk[c]
+                out[y][xx][o] = s
+    return out
+
+
+def group_norm_image(x, gamma, beta, groups: int, eps: float):
+    x, gamma, beta = _l(x), _l(gamma), _l(beta)
+    H, W, C = len(x), len(x[0]), len(x[0][0])
+    cg = C // groups
+    out = [[[0.0] * C for _ in range(W)] for _ in range(H)]
+    for g in range(groups):
+        vals = [x[y][xx][c] for y in range(H) for xx in range(W)
+                for c in range(g * cg, (g + 1) * cg)]
+        n = len(vals)
+        mu = sum(vals) / n
+        var = sum((v - mu) * (v - mu) for v in vals) / n
+        r = 1.0 / math.sqrt(var + eps)
+        for y in range(H):
+            for xx in range(W):
+                for c in range(g * cg, (g + 1) * cg):
+                    out[y][xx][c] = (x[y][xx][c] - mu) * r * gamma[c] + beta[c]
+    return out
+
+
+def map_image(f, x):
+    return [[[f(v) for v in px] for px in row] for row in _l(x)]
+
+
+def add_images(a, b):
+    return [[[u + v for u, v in zip(pa, pb)] for pa, pb in zip(ra, rb)]
+            for ra, rb in zip(_l(a), _l(b))]
+
+
+def upsample_image(x):
+    x = _l(x)
+    H, W = len(x), len(x[0])
+    return [[list(x[y // 2][xx // 2]) for xx in range(2 * W)] for y in range(2 * H)]
+
+
+def patchify_image(img):
+    """[2hp][2wp][Z] -> tokens [hp * wp][4 Z], token (r, c) row-major,
+    channel 4k + 2i + j = pixel (2r + i, 2c + j) channel k."""
+    img = _l(img)
+    hp, wp, Z = len(img) // 2, len(img[0]) // 2, len(img[0][0])
+    toks = []
+    for r in range(hp):
+        for c in range(wp):
+            t = [0.0] * (4 * Z)
+            for k in range(Z):
+                for i in range(2):
+                    for j in range(2):
+                        t[4 * k + 2 * i + j] = img[2 * r + i][2 * c + j][k]
+            toks.append(t)
+    return toks
+
+
+def resnet_image(x, w, p: str, groups: int, eps: float):
+    h = conv_image(map_image(silu, group_norm_image(x, w[p + "gn1.g"], w[p + "gn1.b"],
+                                                    groups, eps)),
+                   w[p + "conv1.w"], w[p + "conv1.b"])
+    h = conv_image(map_image(silu, group_norm_image(h, w[p + "gn2.g"], w[p + "gn2.b"],
+                                                    groups, eps)),
+                   w[p + "conv2.w"], w[p + "conv2.b"])
+    s = x if (p + "short.w") not in w else conv_image(x, w[p + "short.w"], w[p + "short.b"])
+    return add_images(s, h)
+
+
+def attention_block_image(x, w, p: str, groups: int, eps: float):
+    x = _l(x)
+    H, W = len(x), len(x[0])
+    t = group_norm_image(x, w[p + "gn.g"], w[p + "gn.b"], groups, eps)
+    flat = lambda im: [px for row in im for px in row]
+    q = flat(conv_image(t, w[p + "q.w"], w[p + "q.b"]))
+    k = flat(conv_image(t, w[p + "k.w"], w[p + "k.b"]))
+    v = flat(conv_image(t, w[p + "v.w"], w[p + "v.b"]))
+    o = attention_rows(q, k, v)
+    o_img = [[o[y * W + xx] for xx in range(W)] for y in range(H)]
+    return add_images(x, conv_image(o_img, w[p + "o.w"], w[p + "o.b"]))
