@@ -19,7 +19,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdit.so")
-SOURCES = ["gemm.hip", "attention.hip", "norm.hip", "abi.cpp", "plan.cpp"]
+SOURCES = ["gemm.hip", "attention.hip", "norm.hip", "abi.cpp", "plan.cpp", "vae.hip", "vae_abi.cpp"]
 ARCH = "gfx950"
 
 CFLAGS = [

@@ -17,6 +17,16 @@
 #include "../../include/dit.h"
 #include "kernels.hpp"
 #include "plan.hpp"
+#include "profile.hpp"
+
+namespace dit {
+namespace prof {
+Profiler& state() {
+  static Profiler p;
+  return p;
+}
+}  // namespace prof
+}  // namespace dit
 
 namespace {
 
@@ -30,47 +40,7 @@ using namespace dit::host;
   } while (0)
 
 // ---------------------------------------------------------------- profiling
-// Optional event pairs around every launch (dit_profile_begin/end).
-struct ProfRecord {
-  int kind;
-  double flops, bytes;
-  hipEvent_t start, stop;
-};
-struct Profiler {
-  std::mutex mu;
-  bool on = false;
-  std::vector<ProfRecord> recs;
-  std::vector<hipEvent_t> pool;
-};
-Profiler g_prof;
-
-hipEvent_t prof_event() {
-  if (!g_prof.pool.empty()) {
-    hipEvent_t e = g_prof.pool.back();
-    g_prof.pool.pop_back();
-    return e;
-  }
-  hipEvent_t e = nullptr;
-  if (hipEventCreate(&e) != hipSuccess) return nullptr;
-  return e;
-}
-
-// Runs `launch` (returning hipError_t); when profiling, brackets it with events.
-template <class F>
-hipError_t timed(int kind, double flops, double bytes, hipStream_t st, F&& launch) {
-  if (!g_prof.on) return launch();
-  std::lock_guard<std::mutex> lock(g_prof.mu);
-  ProfRecord r{kind, flops, bytes, prof_event(), prof_event()};
-  if (!r.start || !r.stop) return hipErrorOutOfMemory;
-  hipError_t e = hipEventRecord(r.start, st);
-  if (e != hipSuccess) return e;
-  e = launch();
-  if (e != hipSuccess) return e;
-  e = hipEventRecord(r.stop, st);
-  if (e != hipSuccess) return e;
-  g_prof.recs.push_back(r);
-  return hipSuccess;
-}
+using dit::prof::timed;
 
 // ---------------------------------------------------------------- layouts
 
@@ -759,6 +729,7 @@ int dit_denoise_forward(const dit_config* cfg, const dit_model_weights* w, const
 }
 
 int dit_profile_begin(void) {
+  dit::prof::Profiler& g_prof = dit::prof::state();
   std::lock_guard<std::mutex> lock(g_prof.mu);
   g_prof.recs.clear();
   g_prof.on = true;
@@ -767,12 +738,13 @@ int dit_profile_begin(void) {
 
 int dit_profile_end(dit_kernel_stats* out) {
   if (!out) return fail(DIT_E_NULL, "out is NULL");
+  dit::prof::Profiler& g_prof = dit::prof::state();
   std::lock_guard<std::mutex> lock(g_prof.mu);
   if (!g_prof.on) return fail(DIT_E_VALUE, "dit_profile_end without dit_profile_begin");
   g_prof.on = false;
   for (int k = 0; k < DIT_K_COUNT; ++k) out[k] = dit_kernel_stats{k, 0, 0.0, 0.0, 0.0};
   int status = DIT_OK;
-  for (ProfRecord& r : g_prof.recs) {
+  for (dit::prof::Record& r : g_prof.recs) {
     float ms = 0.f;
     hipError_t e = hipEventSynchronize(r.stop);
     if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.start, r.stop);

@@ -223,4 +223,80 @@ struct RowsCopyArgs {
 hipError_t rows_copy_launch(const RowsCopyArgs& a, hipStream_t stream);
 hipError_t euler_launch(const LatentArgs& a, hipStream_t stream);
 
+// ------------------------------------------------------------------ latent decoder
+// Implicit-GEMM convolution, channels last: out[b, m, n] for output pixel m
+// of an H x W grid (row-major) and channel n,
+//   sum over sources s, K index k < taps_s C_s (k = tap C_s + c) of
+//   A_s[b, pixel(m, tap), c] W_s[b][n, k]
+// plus bias, a second bias and a bf16 residual, stored bf16 or fp32. A 3x3
+// tap (dy, dx) = (tap / 3 - 1, tap % 3 - 1) reads pixel (y + dy, x + dx),
+// zero outside the grid; with `up` the source grid is (H / 2, W / 2) and
+// the pixel read is ((y + dy) / 2, (x + dx) / 2) (nearest 2x upsampling
+// before the conv). A plain GEMM is the 1 x M grid with taps = 1.
+struct ConvSource {
+  const bf16_t* x;      // [B][pixels][lda] (sample stride x_bs elements)
+  const bf16_t* w;      // [N][ldw] (sample stride w_bs; 0 = shared weights)
+  int64_t x_bs, w_bs;
+  uint32_t x_bytes, w_bytes;  // bytes of one sample's A / of W (< 2^31)
+  int32_t lda, ldw, C, taps, up;
+  int32_t slices;       // ceil(taps C / 64), set by conv_launch
+  float inv_c;          // 1 / C, set by conv_launch
+};
+struct ConvArgs {
+  ConvSource src[2];
+  void* out;            // [B][M][ldo], bf16 or fp32
+  const float* bias;    // [N] (or [M] with bias_rows), may be null
+  const float* bias2;   // [N], may be null
+  const bf16_t* resid;  // [B][M][ldr] bf16, may be null; may alias out
+  int64_t out_bs, resid_bs;
+  int32_t nsrc, B, H, W, N, ldo, ldr, out_f32, bias_rows;
+  int32_t vec;          // 16-byte epilogue stores allowed (set by conv_launch)
+  int32_t tiles_m, tiles_n, cfg;  // set by conv_launch
+};
+// Checks the shapes the kernel assumes (returns hipErrorInvalidValue on a
+// violation), picks the tile shape and launches.
+hipError_t conv_launch(ConvArgs& a, hipStream_t stream);
+
+// GroupNorm (+ optional SiLU), channels last, per sample over H * W pixels:
+// statistics from per-block partial sums around a per-group shift (the
+// group's first value), combined in double in a fixed order; then
+// y = act(x * a_c + s_c) with a_c = gamma_c rstd, s_c = beta_c - mean a_c.
+struct GroupNormArgs {
+  const bf16_t* x;
+  bf16_t* y;
+  float* part;          // [B][nblk][G][2] partial sums (workspace)
+  float* ab;            // [B][C][2] per-channel scale / shift (workspace)
+  const float* gamma;
+  const float* beta;
+  int64_t x_bs, y_bs;   // sample strides (elements)
+  int32_t B, HW, C, G, ppb, nblk, silu;
+  float eps;
+};
+// ppb / nblk: pixels per statistics block (a multiple of 256 / (C / 8)) and
+// the block count per sample, ppb nblk >= HW.
+hipError_t group_norm_launch(const GroupNormArgs& a, hipStream_t stream);
+
+// Row softmax: p[r, j] = bf16(exp(c s[r, j] - max) / sum), c = scale,
+// j < n (n % 4 == 0), rows of s fp32 (stride lds), p bf16 (stride ldp).
+struct SoftmaxArgs {
+  const float* s;
+  bf16_t* p;
+  int64_t lds, ldp;
+  int32_t rows, n;
+  float scale;
+};
+hipError_t softmax_rows_launch(const SoftmaxArgs& a, hipStream_t stream);
+
+// Latent tokens z fp32 [B][hp * wp][4 Z] -> image x bf16 [B][2hp][2wp][Z]:
+// u = z * scale[c] + shift[c] per token channel c = 4k + 2i + j, written to
+// pixel (2r + i, 2c + j) channel k of token (r, c).
+struct LatentImageArgs {
+  const float* z;
+  const float* scale;
+  const float* shift;
+  bf16_t* x;
+  int32_t B, hp, wp, Z;
+};
+hipError_t latent_image_launch(const LatentImageArgs& a, hipStream_t stream);
+
 }  // namespace dit

@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 
@@ -369,6 +370,221 @@ int validate_denoise(const dit_config* cfg, const dit_model_weights* w, const vo
   return check_ws(ws, ws_bytes, denoise_layout(*cfg, B, n_txt + n_img + n_ref).total);
 }
 
+
+// ---------------------------------------------------------------- decoder
+
+namespace {
+bool pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+constexpr int64_t kMaxSampleBytes = 0x7FFFFFFFll;  // conv offsets and the zero-read marker
+constexpr int64_t kScoreChunkBytes = 1ll << 30;    // fp32 attention scores per chunk
+}  // namespace
+
+void gn_blocks(int64_t HW, int C, int* ppb, int* nblk) {
+  const int64_t ppi = 256 / (C / 8);
+  int64_t p = 65536 / C;  // about 128 KiB of bf16 per block
+  if (p < ppi) p = ppi;
+  p = p / ppi * ppi;
+  *ppb = (int)p;
+  *nblk = (int)((HW + p - 1) / p);
+}
+
+int check_vae_config(const dit_vae_config* c) {
+  if (!c) return fail(DIT_E_NULL, "decoder config is NULL");
+  if (c->z_channels < 8 || c->z_channels > 256 || c->z_channels % 8)
+    return fail(DIT_E_UNSUPPORTED, "z_channels %d: a multiple of 8 in [8, 256]", c->z_channels);
+  if (c->groups < 1 || c->groups > 1024)
+    return fail(DIT_E_UNSUPPORTED, "groups %d out of [1, 1024]", c->groups);
+  for (int i = 0; i < 4; ++i) {
+    const int w = c->block_channels[i];
+    if (!pow2(w) || w < 32 || w > 2048 || w % c->groups)
+      return fail(DIT_E_UNSUPPORTED,
+                  "block_channels[%d] = %d: a power of two in [32, 2048] divisible by groups %d",
+                  i, w, c->groups);
+  }
+  if (c->layers < 1 || c->layers > DIT_VAE_MAX_LAYERS)
+    return fail(DIT_E_UNSUPPORTED, "layers %d out of [1, %d]", c->layers, DIT_VAE_MAX_LAYERS);
+  if (!(c->eps > 0.f) || !std::isfinite(c->eps))
+    return fail(DIT_E_VALUE, "eps must be positive and finite");
+  return DIT_OK;
+}
+
+int vae_level_channels(const dit_vae_config& c, int l) { return c.block_channels[3 - l]; }
+
+int vae_resnet_in(const dit_vae_config& c, int l, int r) {
+  if (r > 0) return vae_level_channels(c, l);
+  return l == 0 ? c.block_channels[3] : vae_level_channels(c, l - 1);
+}
+
+VaeLayout vae_layout(const dit_vae_config& c, int64_t B, int64_t hp, int64_t wp) {
+  VaeLayout L;
+  const int64_t H0 = 2 * hp, W0 = 2 * wp, top = c.block_channels[3];
+  L.n0 = H0 * W0;
+  auto gn = [&](int64_t pix, int C) {
+    int ppb, nblk;
+    gn_blocks(pix, C, &ppb, &nblk);
+    L.gn_nblk = std::max<int64_t>(L.gn_nblk, nblk);
+  };
+  L.act = L.n0 * top;
+  L.act_h = L.n0 * top;
+  gn(L.n0, (int)top);
+  int cmax = (int)top;
+  for (int l = 0; l < 4; ++l) {
+    const int64_t pix = (H0 << l) * (W0 << l);
+    const int co = vae_level_channels(c, l);
+    cmax = std::max(cmax, co);
+    for (int r = 0; r < c.layers; ++r) {
+      const int ci = vae_resnet_in(c, l, r);
+      L.act = std::max<int64_t>(L.act, pix * std::max(ci, co));
+      L.act_h = std::max<int64_t>(L.act_h, pix * co);
+      gn(pix, ci);
+      gn(pix, co);
+    }
+  }
+  L.ld = round_up(L.n0, 8);
+  L.mq = L.n0;
+  if (L.n0 * L.ld * 4 > kScoreChunkBytes)
+    L.mq = std::max<int64_t>(256, kScoreChunkBytes / (L.ld * 4) / 256 * 256);
+  // DIT_VAE_ATTN_ROWS (tests): a smaller positive multiple of 256 query rows
+  // per chunk, so that small images exercise the chunked path
+  if (const char* e = std::getenv("DIT_VAE_ATTN_ROWS")) {
+    const long long v = std::atoll(e);
+    if (v > 0 && v % 256 == 0 && v < L.mq) L.mq = v;
+  }
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  L.p = take((size_t)(B * L.act * 2));
+  L.q = take((size_t)(B * L.act * 2));
+  L.t = take((size_t)(B * L.act * 2));
+  L.h = take((size_t)(B * L.act_h * 2));
+  L.lat = take((size_t)(B * L.n0 * c.z_channels * 2));
+  L.part = take((size_t)(B * L.gn_nblk * c.groups * 2 * 4));
+  L.ab = take((size_t)(B * cmax * 2 * 4));
+  L.s = take((size_t)(L.mq * L.ld * 4));
+  L.pm = take((size_t)(L.mq * L.ld * 2));
+  L.vt = take((size_t)(B * top * L.ld * 2));
+  L.total = off;
+  return L;
+}
+
+namespace {
+int check_resnet(const dit_vae_resnet& r, int ci, int co, const char* where) {
+  const void* need[] = {r.gn1_gamma, r.gn1_beta, r.conv1_w, r.conv1_b,
+                        r.gn2_gamma, r.gn2_beta, r.conv2_w, r.conv2_b};
+  for (const void* p : need) DIT_CHECK(check_ptr(p, where));
+  if (ci != co) {
+    DIT_CHECK(check_ptr(r.short_w, where));
+    DIT_CHECK(check_ptr(r.short_b, where));
+  } else if (r.short_w || r.short_b) {
+    return fail(DIT_E_NULL, "%s: a shortcut is given but the block keeps %d channels", where, ci);
+  }
+  return DIT_OK;
+}
+}  // namespace
+
+int validate_vae_decode(const dit_vae_config* cfg, const dit_vae_weights* w, const float* z,
+                        int32_t B, int32_t hp, int32_t wp, const float* image, const void* ws,
+                        size_t ws_bytes) {
+  DIT_CHECK(check_vae_config(cfg));
+  if (!w) return fail(DIT_E_NULL, "decoder weights are NULL");
+  const void* need[] = {w->lat_scale, w->lat_shift, w->conv_in_w, w->conv_in_b,
+                        w->attn_gn_gamma, w->attn_gn_beta, w->norm_out_gamma,
+                        w->norm_out_beta, w->conv_out_w, w->conv_out_b};
+  for (const void* p : need) DIT_CHECK(check_ptr(p, "decoder weight"));
+  for (int i = 0; i < 4; ++i) {
+    DIT_CHECK(check_ptr(w->attn_w[i], "attention weight"));
+    DIT_CHECK(check_ptr(w->attn_b[i], "attention bias"));
+  }
+  const int top = cfg->block_channels[3];
+  DIT_CHECK(check_resnet(w->mid[0], top, top, "mid ResNet 0"));
+  DIT_CHECK(check_resnet(w->mid[1], top, top, "mid ResNet 1"));
+  char where[64];
+  for (int l = 0; l < 4; ++l) {
+    for (int r = 0; r < cfg->layers; ++r) {
+      snprintf(where, sizeof where, "level %d ResNet %d", l, r);
+      DIT_CHECK(check_resnet(w->up[l][r], vae_resnet_in(*cfg, l, r), vae_level_channels(*cfg, l),
+                             where));
+    }
+    if (l < 3) {
+      DIT_CHECK(check_ptr(w->upconv_w[l], "upsample conv weight"));
+      DIT_CHECK(check_ptr(w->upconv_b[l], "upsample conv bias"));
+    }
+  }
+  DIT_CHECK(check_ptr(z, "z"));
+  DIT_CHECK(check_ptr(image, "image"));
+  if (B < 1 || B > DIT_MAX_BATCH)
+    return fail(DIT_E_SHAPE, "B %d out of [1, %d]", B, DIT_MAX_BATCH);
+  if (hp < 1 || wp < 1 || 16ll * hp > 32766 || 16ll * wp > 32767)
+    return fail(DIT_E_SHAPE, "token grid %d x %d out of range", hp, wp);
+  const VaeLayout L = vae_layout(*cfg, B, hp, wp);
+  if (L.act * 2 > kMaxSampleBytes || L.mq * L.ld * 2 > kMaxSampleBytes ||
+      (int64_t)top * L.ld * 2 > kMaxSampleBytes)
+    return fail(DIT_E_UNSUPPORTED, "a %d x %d token grid needs activations over 2 GiB per sample",
+                hp, wp);
+  return check_ws(ws, ws_bytes, L.total);
+}
+
+int validate_vae_conv(const void* xin, int32_t c_in, int32_t ksize, int32_t up, const void* w,
+                      const float* bias, const void* xs, int32_t c_short, const void* short_w,
+                      const float* short_b, const void* resid, int32_t B, int32_t H, int32_t W,
+                      int32_t c_out, const void* out) {
+  DIT_CHECK(check_ptr(xin, "xin"));
+  DIT_CHECK(check_ptr(w, "w"));
+  DIT_CHECK(check_ptr(out, "out"));
+  if (bias) DIT_CHECK(check_ptr(bias, "bias"));
+  if (resid) DIT_CHECK(check_ptr(resid, "resid"));
+  if ((xs != nullptr) != (short_w != nullptr))
+    return fail(DIT_E_NULL, "xs and short_w go together");
+  if (xs) {
+    DIT_CHECK(check_ptr(xs, "xs"));
+    DIT_CHECK(check_ptr(short_w, "short_w"));
+    if (short_b) DIT_CHECK(check_ptr(short_b, "short_b"));
+    if (c_short < 8 || c_short % 8) return fail(DIT_E_SHAPE, "c_short %d: a multiple of 8", c_short);
+  }
+  if (c_in < 8 || c_in % 8) return fail(DIT_E_SHAPE, "c_in %d: a multiple of 8", c_in);
+  if (ksize != 1 && ksize != 3) return fail(DIT_E_SHAPE, "ksize %d: 1 or 3", ksize);
+  if (up != 0 && up != 1) return fail(DIT_E_VALUE, "up must be 0 or 1");
+  if (B < 1 || B > DIT_MAX_BATCH) return fail(DIT_E_SHAPE, "B %d out of [1, %d]", B, DIT_MAX_BATCH);
+  if (H < 2 || W < 1 || H > 32766 || W > 32767 || c_out < 1 || c_out > 4096)
+    return fail(DIT_E_SHAPE, "grid %d x %d, c_out %d out of range", H, W, c_out);
+  if (up && (H % 2 || W % 2)) return fail(DIT_E_SHAPE, "an upsampled conv needs an even grid");
+  const int64_t pix = (int64_t)H * W;
+  const int64_t taps = (int64_t)ksize * ksize;
+  if ((up ? pix / 4 : pix) * c_in * 2 > kMaxSampleBytes || pix * c_out * 4 > kMaxSampleBytes ||
+      pix * c_short * 2 > kMaxSampleBytes ||
+      ((int64_t)c_out + 256) * taps * c_in * 2 > kMaxSampleBytes ||
+      ((int64_t)c_out + 256) * c_short * 2 > kMaxSampleBytes)
+    return fail(DIT_E_UNSUPPORTED, "a sample or a weight exceeds 2 GiB");
+  return DIT_OK;
+}
+
+size_t vae_group_norm_ws(int64_t B, int64_t HW, int C, int groups) {
+  int ppb, nblk;
+  gn_blocks(HW, C, &ppb, &nblk);
+  return align_up((size_t)(B * nblk * groups * 2 * 4)) + align_up((size_t)(B * C * 2 * 4));
+}
+
+int validate_vae_group_norm(const void* x, const void* y, const float* gamma, const float* beta,
+                            int32_t B, int64_t HW, int32_t C, int32_t groups, float eps,
+                            const void* ws, size_t ws_bytes) {
+  DIT_CHECK(check_ptr(x, "x"));
+  DIT_CHECK(check_ptr(y, "y"));
+  DIT_CHECK(check_ptr(gamma, "gamma"));
+  DIT_CHECK(check_ptr(beta, "beta"));
+  if (x == y) return fail(DIT_E_VALUE, "x and y may not alias");
+  if (B < 1 || B > DIT_MAX_BATCH) return fail(DIT_E_SHAPE, "B %d out of [1, %d]", B, DIT_MAX_BATCH);
+  if (HW < 1 || HW > (1ll << 30)) return fail(DIT_E_SHAPE, "HW %lld out of range", (long long)HW);
+  if (!pow2(C) || C < 8 || C > 2048)
+    return fail(DIT_E_UNSUPPORTED, "C %d: a power of two in [8, 2048]", C);
+  if (groups < 1 || groups > 1024 || C % groups)
+    return fail(DIT_E_UNSUPPORTED, "groups %d must divide C %d (at most 1024)", groups, C);
+  if (!(eps > 0.f) || !std::isfinite(eps)) return fail(DIT_E_VALUE, "eps must be positive and finite");
+  return check_ws(ws, ws_bytes, vae_group_norm_ws(B, HW, C, groups));
+}
+
 }  // namespace host
 }  // namespace dit
 
@@ -446,6 +662,38 @@ size_t dit_workspace_bytes(const dit_config* cfg, int32_t kind, int32_t B, int64
     case DIT_WS_DENOISE: return denoise_layout(*cfg, B, S).total;
     default: fail(DIT_E_VALUE, "unknown workspace kind %d", kind); return 0;
   }
+}
+
+
+int dit_vae_config_check(const dit_vae_config* cfg) { return check_vae_config(cfg); }
+
+void dit_vae_config_default(dit_vae_config* cfg) {
+  if (!cfg) return;
+  cfg->z_channels = 32;
+  cfg->block_channels[0] = 128;
+  cfg->block_channels[1] = 256;
+  cfg->block_channels[2] = 512;
+  cfg->block_channels[3] = 512;
+  cfg->layers = 3;
+  cfg->groups = 32;
+  cfg->eps = 1e-6f;
+}
+
+size_t dit_vae_workspace_bytes(const dit_vae_config* cfg, int32_t B, int32_t hp, int32_t wp) {
+  if (check_vae_config(cfg) != DIT_OK) return 0;
+  if (B < 1 || B > DIT_MAX_BATCH || hp < 1 || wp < 1 || 16ll * hp > 32766 || 16ll * wp > 32767) {
+    fail(DIT_E_SHAPE, "B %d, token grid %d x %d out of range", B, hp, wp);
+    return 0;
+  }
+  return vae_layout(*cfg, B, hp, wp).total;
+}
+
+size_t dit_vae_group_norm_ws_bytes(int32_t B, int64_t HW, int32_t C, int32_t groups) {
+  if (B < 1 || HW < 1 || C < 8 || C % 8 || C > 2048 || groups < 1 || C % groups) {
+    fail(DIT_E_SHAPE, "B %d, HW %lld, C %d, groups %d out of range", B, (long long)HW, C, groups);
+    return 0;
+  }
+  return vae_group_norm_ws(B, HW, C, groups);
 }
 
 }  // extern "C"

@@ -10,6 +10,7 @@
 #include <stdint.h>
 
 #include "../../include/dit.h"
+#include "../../include/dit_vae.h"
 
 #define DIT_CHECK(status)                                                         \
   do {                                                                            \
@@ -109,6 +110,40 @@ int validate_denoise(const dit_config* cfg, const dit_model_weights* w, const vo
                      int32_t B, int64_t n_txt, int64_t n_img, int64_t n_ref,
                      const float* cos_dev, const float* sin_dev, const void* ws,
                      size_t ws_bytes);
+
+// ---------------------------------------------------------------- decoder
+// GroupNorm statistics blocks: pixels per block (a multiple of the pixels
+// one pass of 256 threads covers, 256 / (C / 8)) and block count.
+void gn_blocks(int64_t HW, int C, int* ppb, int* nblk);
+
+// Decoder workspace: activation buffers p, q (stream), t (normalized), h
+// (first conv of a ResNet), the unpatchified latent, GroupNorm partials and
+// per-channel scale / shift, and the attention's scores (fp32) and
+// probabilities (bf16) for mq query rows at a time, and v^T (bf16 [B][C][ld]).
+struct VaeLayout {
+  int64_t n0 = 0, ld = 0, mq = 0;     // attention: pixels, padded row, query rows per chunk
+  int64_t act = 0, act_h = 0;        // elements per sample of p / q / t and of h
+  int64_t gn_nblk = 0;               // largest GroupNorm block count
+  size_t p = 0, q = 0, t = 0, h = 0, lat = 0, part = 0, ab = 0, s = 0, pm = 0, vt = 0,
+         total = 0;
+};
+VaeLayout vae_layout(const dit_vae_config& c, int64_t B, int64_t hp, int64_t wp);
+int check_vae_config(const dit_vae_config* c);
+// channel width of decoder level l (0 = deepest) and the input width of
+// ResNet r of level l
+int vae_level_channels(const dit_vae_config& c, int l);
+int vae_resnet_in(const dit_vae_config& c, int l, int r);
+int validate_vae_decode(const dit_vae_config* cfg, const dit_vae_weights* w, const float* z,
+                        int32_t B, int32_t hp, int32_t wp, const float* image, const void* ws,
+                        size_t ws_bytes);
+int validate_vae_conv(const void* xin, int32_t c_in, int32_t ksize, int32_t up, const void* w,
+                      const float* bias, const void* xs, int32_t c_short, const void* short_w,
+                      const float* short_b, const void* resid, int32_t B, int32_t H, int32_t W,
+                      int32_t c_out, const void* out);
+size_t vae_group_norm_ws(int64_t B, int64_t HW, int C, int groups);
+int validate_vae_group_norm(const void* x, const void* y, const float* gamma, const float* beta,
+                            int32_t B, int64_t HW, int32_t C, int32_t groups, float eps,
+                            const void* ws, size_t ws_bytes);
 
 }  // namespace host
 }  // namespace dit

@@ -1,0 +1,670 @@
+// Latent decoder kernels on gfx950 (the decoder that runs on the card after
+// the last step, "tt_flux2_klein - Python reference", Lower-level entry
+// points: decode; it has GroupNorm layers and takes non-square images,
+// "flux2-klein-p100a", What this port adds). The layer list is a reading,
+// stated in dit_vae.h.
+//
+// Convolution as an implicit GEMM on MFMA (one workgroup = 8 waves, one
+// output tile of BM pixels by BN channels):
+//  * Activations are channels-last bf16, so for a fixed kernel tap a pixel's
+//    64-channel K slice is one 128-byte run. Slices go from L2 straight into
+//    LDS with buffer loads that write LDS (as in the DiT GEMM): every loader
+//    lane computes, per slice, the source pixel of each of its rows for its
+//    16-byte chunk's tap, and a pixel outside the grid (zero padding), a K
+//    index past the end, or a row past the tile's last pixel reads through
+//    an offset beyond the buffer's range, which returns zeros. The upsample
+//    before a conv is the same address map at half resolution, so the
+//    upsampled tensor never exists.
+//  * A ResNet's 1x1 shortcut is a second K range of the same tile (its own
+//    source and weights), so the block output is one launch.
+//  * Only waves 4-7 issue loads; all eight run MFMAs (v_mfma_f32_32x32x16_bf16,
+//    wave tile 64 x 32 FN), two LDS stages, one barrier per slice.
+//  * Epilogue: fp32 accumulators staged through LDS in two passes; bias(es)
+//    and the residual are added in fp32, then one rounding to bf16 (or an
+//    fp32 store), 16 bytes per lane where the row allows.
+//  * Tiles are walked channel-tile fastest and dealt to the XCDs in
+//    contiguous ranges, so an XCD's L2 holds a band of image rows and their
+//    halo.
+// The k order of every output element depends only on the layer (its taps
+// and channels), not on the tile shape or position, so batch rows are
+// bitwise independent.
+#include <algorithm>
+#include <cmath>
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace dit {
+namespace {
+
+constexpr int CBK = 64;            // K slice
+constexpr int CNT = 512;           // 8 waves
+constexpr int ROW_U = CBK / 8;     // 16-byte units per LDS row
+constexpr uint32_t OOB = 0x80000000u;  // beyond every buffer's range (< 2^31 bytes)
+
+__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// WM waves along the pixels (4 or 8), 8 / WM along the channels; wave tile
+// 64 x 32 FN.
+template <int WM, int FN>
+__global__ __launch_bounds__(CNT, 1) void conv_kernel(const ConvArgs a) {
+  constexpr int WN = 8 / WM;
+  constexpr int FM = 2;
+  constexpr int BM = 64 * WM, BN = 32 * FN * WN;
+  constexpr int A_PER = BM / 128;           // 32-row A blocks per loader wave
+  constexpr int W_BLK = BN / 32;            // 32-row W blocks in the tile
+  constexpr int W_PER = (W_BLK + 3) / 4;    // W blocks per loader wave (at most)
+  constexpr int STAGE_U = (BM + BN) * ROW_U;
+  __shared__ u32x4 lds[2 * STAGE_U];
+  static_assert(WM * 32 * BN * 4 <= 2 * STAGE_U * 16, "epilogue stage fits");
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int per_b = a.tiles_m * a.tiles_n;
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  const int b = L / per_b;
+  const int rem = L - b * per_b;
+  const int tm = rem / a.tiles_n, tn = rem - tm * a.tiles_n;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int H = a.H, W = a.W, M = H * W;
+
+  // ---- loaders: waves 4-7. Lane (lr, lp) of an 8-row group writes physical
+  // chunk lp of row lr, i.e. logical chunk lp ^ swz(row) = lp ^ lr ^ (i & 1)
+  // for the group's index i within its 32-row block.
+  const int lr = (lane >> 3), lp = lane & 7;
+  const bool loader = wave >= 4;
+  const int lw = wave - 4;
+  // Each A row of this lane: on an image grid the pixel (y, x) packed as
+  // y << 16 | x (y = 0x7FFF past the last pixel, which fails every bounds
+  // check); on a 1 x M grid (a plain GEMM, gemm_rows) the row index itself
+  // (0xFFFFFFFF past the end).
+  const bool gemm_rows = H == 1;
+  uint32_t yx[A_PER * 4];
+#pragma unroll
+  for (int h = 0; h < A_PER; ++h)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = m0 + 32 * (lw + 4 * h) + 8 * i + lr;
+      uint32_t v;
+      if (gemm_rows) {
+        v = m < M ? (uint32_t)m : 0xFFFFFFFFu;
+      } else {
+        v = 0x7FFFu << 16;
+        if (m < M) {
+          const int y = m / W;
+          v = ((uint32_t)y << 16) | (uint32_t)(m - y * W);
+        }
+      }
+      yx[h * 4 + i] = v;
+    }
+  __amdgpu_buffer_rsrc_t ar[2], wr[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const ConvSource& S = a.src[s < a.nsrc ? s : 0];
+    ar[s] = make_rsrc(S.x + (int64_t)b * S.x_bs, S.x_bytes);
+    wr[s] = make_rsrc(S.w + (int64_t)b * S.w_bs, S.w_bytes);
+  }
+  const int slices0 = a.src[0].slices;
+  const int nk = slices0 + (a.nsrc > 1 ? a.src[1].slices : 0);
+
+  auto dma = [&](int kt, int stage) {
+    if (!loader) return;
+    const int s = kt >= slices0 ? 1 : 0;
+    const ConvSource& S = a.src[s];
+    const int j = kt - (s ? slices0 : 0);
+    const int C = S.C, lda = S.lda, taps = S.taps, up = S.up;
+    const int kend = taps * C;
+    // per chunk parity: tap offsets, channel, and whether k is in range
+    int dy[2], dx[2], ci[2];
+    bool kok[2];
+    int kk[2];
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+      const int cl = lp ^ lr ^ par;
+      const int k = j * CBK + cl * 8;
+      kk[par] = k;
+      kok[par] = k < kend;
+      int tap = 0;
+      if (taps != 1) tap = (int)(((float)k + 0.5f) * S.inv_c);
+      ci[par] = k - tap * C;
+      const int ty = (tap * 11) >> 5;  // tap / 3 for tap < 9
+      dy[par] = taps == 1 ? 0 : ty - 1;
+      dx[par] = taps == 1 ? 0 : tap - 3 * ty - 1;
+    }
+    u32x4* const sa = lds + stage * STAGE_U;
+    u32x4* const sw = lds + stage * STAGE_U + BM * ROW_U;
+    const __amdgpu_buffer_rsrc_t A = s ? ar[1] : ar[0];
+    const __amdgpu_buffer_rsrc_t Wr = s ? wr[1] : wr[0];
+    const int Wi = up ? (W >> 1) : W;
+#pragma unroll
+    for (int h = 0; h < A_PER; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int par = i & 1;
+        const uint32_t v = yx[h * 4 + i];
+        uint32_t off;
+        if (gemm_rows) {
+          off = (kok[par] && v < (uint32_t)M) ? (v * (uint32_t)lda + (uint32_t)ci[par]) * 2u : OOB;
+        } else {
+          const int y = (int)(v >> 16), x = (int)(v & 0xFFFFu);
+          const int yy = y + dy[par], xx = x + dx[par];
+          const bool ok = kok[par] && (unsigned)yy < (unsigned)H && (unsigned)xx < (unsigned)W;
+          const int py = up ? (yy >> 1) : yy, px = up ? (xx >> 1) : xx;
+          off = ok ? (uint32_t)((py * Wi + px) * lda + ci[par]) * 2u : OOB;
+        }
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            A, (lds_ptr_t)(sa + (32 * (lw + 4 * h) + 8 * i) * ROW_U), 16, off, 0, 0, 0);
+      }
+#pragma unroll
+    for (int h = 0; h < W_PER; ++h) {
+      const int wb = lw + 4 * h;
+      if (wb >= W_BLK) break;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int par = i & 1;
+        const int n = n0 + 32 * wb + 8 * i + lr;
+        const uint32_t off =
+            kok[par] ? (uint32_t)(n * S.ldw + kk[par]) * 2u : OOB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            Wr, (lds_ptr_t)(sw + (32 * wb + 8 * i) * ROW_U), 16, off, 0, 0, 0);
+      }
+    }
+  };
+
+  // ---- MFMA fragments (both operands double-buffered across k-steps)
+  const int fr = lane & 31, fg = lane >> 5;
+  const int wm = WM == 8 ? wave : (wave & 3), wn = WM == 8 ? 0 : (wave >> 2);
+  const int a_rd = (wm * 64 + fr) * ROW_U;
+  const int w_rd = BM * ROW_U + (wn * 32 * FN + fr) * ROW_U;
+  const int sfr = swz(fr);
+  bf16x8 af[2][FM], wf[2][FN];
+  auto fload = [&](int stage, int s, int buf) {
+    const u32x4* st = lds + stage * STAGE_U;
+    const int ch = (2 * s + fg) ^ sfr;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+      af[buf][i] = __builtin_bit_cast(bf16x8, st[a_rd + i * 32 * ROW_U + ch]);
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      wf[buf][j] = __builtin_bit_cast(bf16x8, st[w_rd + j * 32 * ROW_U + ch]);
+  };
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
+  auto mfmas = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] =
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[buf][j], af[buf][i], acc[i][j], 0, 0, 0);
+  };
+
+  dma(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (nk > 1) dma(1, 1);
+  fload(0, 0, 0);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+#pragma unroll
+    for (int s = 0; s < CBK / 16 - 1; ++s) {
+      fload(cur, s + 1, (s + 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas(s & 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // every wave is done with stage cur and slice kt + 1 has landed
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (kt + 2 < nk) dma(kt + 2, cur);
+    if (kt + 1 < nk) fload(cur ^ 1, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas((CBK / 16 - 1) & 1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // ---- epilogue. Lane holds pixel rows wm*64 + i*32 + fr (i < 2) and
+  // channels wn*32FN + j*32 + 8q + 4fg + 0..3. Pass p stages block i = p of
+  // every wave as fp32 [WM*32][BN] (16-byte chunk c of row r at
+  // c ^ (r & SWM)); the LDS is free (the loop's last fragment reads came
+  // before its last barrier).
+  char* const T = reinterpret_cast<char*>(lds);
+  constexpr int SROW = BN * 4;
+  constexpr int SWM = (BN / 4 < 32 ? BN / 4 : 32) - 1;
+  constexpr int UPR = BN / 8;  // 8-channel units per stage row
+#pragma unroll
+  for (int pass = 0; pass < FM; ++pass) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = wm * 32 + fr;
+        const int c = (wn * 32 * FN + j * 32 + 8 * q + 4 * fg) >> 2;
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = acc[pass][j][4 * q + e];
+        *reinterpret_cast<f32x4*>(T + r * SROW + ((c ^ (r & SWM)) << 4)) = v;
+      }
+    __syncthreads();
+    for (int u = tid; u < WM * 32 * UPR; u += CNT) {
+      const int r = u / UPR, cu = u - r * UPR;
+      const int m = m0 + (r >> 5) * 64 + 32 * pass + (r & 31);
+      const int col = n0 + 8 * cu;
+      if (m >= M || col >= a.N) continue;
+      const f32x4 v0 = *reinterpret_cast<const f32x4*>(T + r * SROW + (((2 * cu) ^ (r & SWM)) << 4));
+      const f32x4 v1 =
+          *reinterpret_cast<const f32x4*>(T + r * SROW + (((2 * cu + 1) ^ (r & SWM)) << 4));
+      float o[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+      const int nv = a.N - col < 8 ? a.N - col : 8;
+      const bool full = nv == 8 && a.vec;
+      if (a.bias) {
+        if (a.bias_rows) {
+          const float bb = a.bias[m];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[e] += bb;
+        } else if (full) {
+          const f32x4 b0 = *reinterpret_cast<const f32x4*>(a.bias + col);
+          const f32x4 b1 = *reinterpret_cast<const f32x4*>(a.bias + col + 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            o[e] += b0[e];
+            o[4 + e] += b1[e];
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (e < nv) o[e] += a.bias[col + e];
+        }
+      }
+      if (a.bias2) {
+        if (full) {
+          const f32x4 b0 = *reinterpret_cast<const f32x4*>(a.bias2 + col);
+          const f32x4 b1 = *reinterpret_cast<const f32x4*>(a.bias2 + col + 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            o[e] += b0[e];
+            o[4 + e] += b1[e];
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (e < nv) o[e] += a.bias2[col + e];
+        }
+      }
+      if (a.resid) {
+        const bf16_t* rp = a.resid + (int64_t)b * a.resid_bs + (int64_t)m * a.ldr + col;
+        if (full) {
+          const u32x4 rv = *reinterpret_cast<const u32x4*>(rp);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[e] += bf16_to_f32((rv[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (e < nv) o[e] += bf16_to_f32(rp[e]);
+        }
+      }
+      if (a.out_f32) {
+        float* op = static_cast<float*>(a.out) + (int64_t)b * a.out_bs + (int64_t)m * a.ldo + col;
+        if (full) {
+          *reinterpret_cast<f32x4*>(op) = f32x4{o[0], o[1], o[2], o[3]};
+          *reinterpret_cast<f32x4*>(op + 4) = f32x4{o[4], o[5], o[6], o[7]};
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (e < nv) op[e] = o[e];
+        }
+      } else {
+        bf16_t* op = static_cast<bf16_t*>(a.out) + (int64_t)b * a.out_bs + (int64_t)m * a.ldo + col;
+        const f32x8 ov = {o[0], o[1], o[2], o[3], o[4], o[5], o[6], o[7]};
+        const bf16x8 pv = pack_bf16x8(ov);
+        if (full) {
+          *reinterpret_cast<bf16x8*>(op) = pv;
+        } else {
+          const u32x4 pw = __builtin_bit_cast(u32x4, pv);
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (e < nv) op[e] = (bf16_t)((pw[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+        }
+      }
+    }
+    __syncthreads();  // the next pass overwrites the stage
+  }
+}
+
+// ------------------------------------------------------------------ GroupNorm
+constexpr int GN_NT = 256;
+
+// Partial sums of d = x - shift_g and d^2 per (sample, block, group); block
+// blockIdx.x covers pixels [blk ppb, blk ppb + ppb) of sample blockIdx.y.
+// Thread: 8 consecutive channels (chunk tid % (C / 8)) of every
+// (256 / (C / 8))-th pixel; sums per channel, then over the block's pixel
+// lanes and over the group's channels in a fixed order.
+__global__ __launch_bounds__(GN_NT) void gn_stats_kernel(const GroupNormArgs g) {
+  __shared__ float red[GN_NT * 8 * 2];
+  const int tid = threadIdx.x;
+  const int b = blockIdx.y, blk = blockIdx.x;
+  const int C = g.C, cpt = C >> 3, ppi = GN_NT / cpt;
+  const int cu = tid % cpt, pl = tid / cpt;
+  const int cg = C / g.G;
+  const bf16_t* x = g.x + (int64_t)b * g.x_bs;
+  float sh[8], s1[8], s2[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int c = 8 * cu + e;
+    sh[e] = bf16_to_f32(x[(c / cg) * cg]);
+    s1[e] = 0.f;
+    s2[e] = 0.f;
+  }
+  const int p0 = blk * g.ppb;
+  const int p1 = min(p0 + g.ppb, g.HW);
+  for (int p = p0 + pl; p < p1; p += ppi) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(x + (int64_t)p * C + 8 * cu);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float d = bf16_to_f32((v[e >> 1] >> (16 * (e & 1))) & 0xFFFFu) - sh[e];
+      s1[e] += d;
+      s2[e] += d * d;
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    red[(pl * C + 8 * cu + e) * 2] = s1[e];
+    red[(pl * C + 8 * cu + e) * 2 + 1] = s2[e];
+  }
+  __syncthreads();
+  // per channel, over the pixel lanes in order (C <= 2048: up to 8 channels
+  // per thread); results kept in registers, then written over red[0 .. 2C)
+  float c1[8], c2[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const int c = tid + t * GN_NT;
+    c1[t] = 0.f;
+    c2[t] = 0.f;
+    if (c < C) {
+      for (int q = 0; q < ppi; ++q) {
+        c1[t] += red[(q * C + c) * 2];
+        c2[t] += red[(q * C + c) * 2 + 1];
+      }
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const int c = tid + t * GN_NT;
+    if (c < C) {
+      red[2 * c] = c1[t];
+      red[2 * c + 1] = c2[t];
+    }
+  }
+  __syncthreads();
+  for (int gg = tid; gg < g.G; gg += GN_NT) {
+    float a1 = 0.f, a2 = 0.f;
+    for (int c = gg * cg; c < (gg + 1) * cg; ++c) {
+      a1 += red[2 * c];
+      a2 += red[2 * c + 1];
+    }
+    float* out = g.part + (((int64_t)b * g.nblk + blk) * g.G + gg) * 2;
+    out[0] = a1;
+    out[1] = a2;
+  }
+}
+
+// Per sample: each wave reduces whole groups (lane l takes blocks l, l + 64,
+// ... in order, then a fixed shuffle tree), in double; then the per-channel
+// scale and shift.
+__global__ __launch_bounds__(GN_NT) void gn_finalize_kernel(const GroupNormArgs g) {
+  __shared__ double mr[2 * 1024];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int b = blockIdx.x;
+  const int cg = g.C / g.G;
+  const bf16_t* x = g.x + (int64_t)b * g.x_bs;
+  for (int gg = wave; gg < g.G; gg += GN_NT / 64) {
+    double a1 = 0.0, a2 = 0.0;
+    for (int k = lane; k < g.nblk; k += 64) {
+      const float* p = g.part + (((int64_t)b * g.nblk + k) * g.G + gg) * 2;
+      a1 += (double)p[0];
+      a2 += (double)p[1];
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      a1 += __shfl_xor(a1, o, 64);
+      a2 += __shfl_xor(a2, o, 64);
+    }
+    if (lane == 0) {
+      const double n = (double)g.HW * (double)cg;
+      const double md = a1 / n;
+      double var = a2 / n - md * md;
+      if (var < 0.0) var = 0.0;
+      mr[2 * gg] = (double)bf16_to_f32(x[gg * cg]) + md;
+      mr[2 * gg + 1] = 1.0 / sqrt(var + (double)g.eps);
+    }
+  }
+  __syncthreads();
+  for (int c = tid; c < g.C; c += GN_NT) {
+    const int gg = c / cg;
+    const double sc = (double)g.gamma[c] * mr[2 * gg + 1];
+    g.ab[((int64_t)b * g.C + c) * 2] = (float)sc;
+    g.ab[((int64_t)b * g.C + c) * 2 + 1] = (float)((double)g.beta[c] - mr[2 * gg] * sc);
+  }
+}
+
+// y = act(x a_c + s_c), 8 channels per thread and step.
+__global__ __launch_bounds__(GN_NT) void gn_apply_kernel(const GroupNormArgs g) {
+  const int64_t units_b = (int64_t)g.HW * (g.C >> 3);
+  const int64_t total = units_b * g.B;
+  const int cpt = g.C >> 3;
+  for (int64_t u = (int64_t)blockIdx.x * GN_NT + threadIdx.x; u < total;
+       u += (int64_t)gridDim.x * GN_NT) {
+    const int b = (int)(u / units_b);
+    const int64_t r = u - (int64_t)b * units_b;
+    const int64_t p = r / cpt;
+    const int cu = (int)(r - p * cpt);
+    const u32x4 v =
+        *reinterpret_cast<const u32x4*>(g.x + (int64_t)b * g.x_bs + p * g.C + 8 * cu);
+    const float* ab = g.ab + ((int64_t)b * g.C + 8 * cu) * 2;
+    const f32x4 q0 = *reinterpret_cast<const f32x4*>(ab);
+    const f32x4 q1 = *reinterpret_cast<const f32x4*>(ab + 4);
+    const f32x4 q2 = *reinterpret_cast<const f32x4*>(ab + 8);
+    const f32x4 q3 = *reinterpret_cast<const f32x4*>(ab + 12);
+    const float sc[8] = {q0[0], q0[2], q1[0], q1[2], q2[0], q2[2], q3[0], q3[2]};
+    const float sf[8] = {q0[1], q0[3], q1[1], q1[3], q2[1], q2[3], q3[1], q3[3]};
+    f32x8 y;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float t = fmaf(bf16_to_f32((v[e >> 1] >> (16 * (e & 1))) & 0xFFFFu), sc[e], sf[e]);
+      y[e] = g.silu ? silu_f(t) : t;
+    }
+    *reinterpret_cast<bf16x8*>(g.y + (int64_t)b * g.y_bs + p * g.C + 8 * cu) = pack_bf16x8(y);
+  }
+}
+
+// ------------------------------------------------------------------ softmax
+__global__ __launch_bounds__(256) void softmax_rows_kernel(const SoftmaxArgs a) {
+  __shared__ float wm_[4], wl_[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t row = blockIdx.x;
+  const float* s = a.s + row * a.lds;
+  const float c = a.scale * 1.4426950408889634f;  // log2(e)
+  float m = -INFINITY, l = 0.f;
+  for (int i = 4 * tid; i < a.n; i += 1024) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(s + i);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float t = v[e] * c;
+      if (t > m) {
+        l = l * exp2f(m - t) + 1.f;
+        m = t;
+      } else {
+        l += exp2f(t - m);
+      }
+    }
+  }
+  // combine (m, l) over the block
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float m2 = __shfl_xor(m, o, 64), l2 = __shfl_xor(l, o, 64);
+    const float mm = fmaxf(m, m2);
+    l = (m == -INFINITY ? 0.f : l * exp2f(m - mm)) + (m2 == -INFINITY ? 0.f : l2 * exp2f(m2 - mm));
+    m = mm;
+  }
+  if (lane == 0) {
+    wm_[wave] = m;
+    wl_[wave] = l;
+  }
+  __syncthreads();
+  float M = wm_[0];
+#pragma unroll
+  for (int w = 1; w < 4; ++w) M = fmaxf(M, wm_[w]);
+  float Lsum = 0.f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) Lsum += wl_[w] * exp2f(wm_[w] - M);
+  const float inv = 1.f / Lsum;
+  bf16_t* p = a.p + row * a.ldp;
+  for (int i = 4 * tid; i < a.n; i += 1024) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(s + i);
+    f32x4 y;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) y[e] = exp2f(v[e] * c - M) * inv;
+    *reinterpret_cast<u32x2*>(p + i) = pack_bf16x4(y);
+  }
+  // padding columns [n, ldp) read as exact zeros by a product over ldp keys
+  for (int64_t i = a.n + tid; i < a.ldp; i += 256) p[i] = 0;
+}
+
+// ------------------------------------------------------------------ latent image
+__global__ __launch_bounds__(256) void latent_image_kernel(const LatentImageArgs a) {
+  const int H = 2 * a.hp, W = 2 * a.wp, Z = a.Z;
+  const int64_t total = (int64_t)a.B * H * W * Z;
+  for (int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x; t < total;
+       t += (int64_t)gridDim.x * 256) {
+    const int k = (int)(t % Z);
+    const int64_t px = t / Z;
+    const int X = (int)(px % W);
+    const int64_t by = px / W;
+    const int Y = (int)(by % H);
+    const int b = (int)(by / H);
+    const int64_t tok = (int64_t)b * a.hp * a.wp + (int64_t)(Y >> 1) * a.wp + (X >> 1);
+    const int ch = 4 * k + 2 * (Y & 1) + (X & 1);
+    const float u = fmaf(a.z[tok * 4 * Z + ch], a.scale[ch], a.shift[ch]);
+    const f32x4 uv = {u, 0.f, 0.f, 0.f};
+    a.x[t] = (bf16_t)(pack_bf16x4(uv)[0] & 0xFFFFu);
+  }
+}
+
+// ------------------------------------------------------------------ host side
+struct TileCfg {
+  int wm, fn, bm, bn;
+};
+constexpr TileCfg kCfgs[] = {{4, 4, 256, 256}, {8, 4, 512, 128}, {4, 2, 256, 128}, {8, 1, 512, 32}};
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Tile shape: the modelled time is rounds of tiles over 256 CUs times a
+// tile's MFMA work divided by the shape's relative efficiency.
+int pick_cfg(const ConvArgs& a) {
+  const int64_t M = (int64_t)a.H * a.W;
+  static const double eff[] = {1.0, 0.95, 0.8, 0.5};
+  int best = 0;
+  double best_t = 1e300;
+  for (int c = 0; c < 4; ++c) {
+    const TileCfg& t = kCfgs[c];
+    const int64_t tiles = (int64_t)a.B * ceil_div(M, t.bm) * ceil_div(a.N, t.bn);
+    const double rounds = (double)ceil_div(tiles, 256);
+    const double time = rounds * t.bm * t.bn / eff[c];
+    if (time < best_t * 0.999) {
+      best_t = time;
+      best = c;
+    }
+  }
+  return best;
+}
+
+}  // namespace
+
+hipError_t conv_launch(ConvArgs& a, hipStream_t stream) {
+  const int64_t M = (int64_t)a.H * a.W;
+  if (a.B <= 0 || M <= 0 || a.N <= 0) return hipSuccess;
+  // image grids: y and x fit the packed 16-bit fields; 1 x M grids: plain rows
+  if (a.nsrc < 1 || a.nsrc > 2 || M > (1 << 30) || (a.H > 1 && (a.H > 32766 || a.W > 32767)))
+    return hipErrorInvalidValue;
+  for (int s = 0; s < a.nsrc; ++s) {
+    ConvSource& S = a.src[s];
+    if (!S.x || !S.w || S.C <= 0 || S.C % 8 || S.lda % 8 || S.ldw % 8 ||
+        (S.taps != 1 && S.taps != 9) || (S.up && (a.H % 2 || a.W % 2)) ||
+        (a.H == 1 && (S.taps != 1 || S.up)) ||
+        S.x_bytes >= OOB || S.w_bytes >= OOB || S.lda < S.C || S.ldw < S.taps * S.C)
+      return hipErrorInvalidValue;
+    // offsets of every row (pixel or weight row) stay below 2^31
+    const int64_t pix = S.up ? M / 4 : M;
+    if ((int64_t)pix * S.lda * 2 > (int64_t)S.x_bytes ||
+        ((int64_t)a.N + 256) * S.ldw * 2 >= (int64_t)OOB)
+      return hipErrorInvalidValue;
+    S.slices = (int)ceil_div((int64_t)S.taps * S.C, CBK);
+    S.inv_c = 1.0f / (float)S.C;
+  }
+  if (!a.out || (a.resid && a.ldr < a.N) || a.ldo < a.N) return hipErrorInvalidValue;
+  if (a.nsrc < 2) a.src[1] = a.src[0];
+  a.vec = (a.ldo % 8 == 0) && (reinterpret_cast<uintptr_t>(a.out) % 16 == 0) &&
+          (a.out_bs % 8 == 0) &&
+          (!a.resid || (a.ldr % 8 == 0 && reinterpret_cast<uintptr_t>(a.resid) % 16 == 0 &&
+                        a.resid_bs % 8 == 0)) &&
+          (!a.bias || a.bias_rows || reinterpret_cast<uintptr_t>(a.bias) % 16 == 0) &&
+          (!a.bias2 || reinterpret_cast<uintptr_t>(a.bias2) % 16 == 0);
+  const int c = pick_cfg(a);
+  const TileCfg& t = kCfgs[c];
+  a.cfg = c;
+  a.tiles_m = (int)ceil_div(M, t.bm);
+  a.tiles_n = (int)ceil_div(a.N, t.bn);
+  const int64_t n_wg = (int64_t)a.B * a.tiles_m * a.tiles_n;
+  if (n_wg > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)n_wg);
+  switch (c) {
+    case 0: hipLaunchKernelGGL((conv_kernel<4, 4>), grid, dim3(CNT), 0, stream, a); break;
+    case 1: hipLaunchKernelGGL((conv_kernel<8, 4>), grid, dim3(CNT), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((conv_kernel<4, 2>), grid, dim3(CNT), 0, stream, a); break;
+    default: hipLaunchKernelGGL((conv_kernel<8, 1>), grid, dim3(CNT), 0, stream, a); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t group_norm_launch(const GroupNormArgs& g, hipStream_t stream) {
+  if (g.B <= 0 || g.HW <= 0) return hipSuccess;
+  const int cpt = g.C / 8;
+  if (g.C % 8 || g.C > 2048 || GN_NT % cpt || g.G <= 0 || g.C % g.G || g.G > 1024 ||
+      g.ppb % (GN_NT / cpt) || (int64_t)g.nblk * g.ppb < g.HW)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(gn_stats_kernel, dim3((unsigned)g.nblk, (unsigned)g.B), dim3(GN_NT), 0,
+                     stream, g);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(gn_finalize_kernel, dim3((unsigned)g.B), dim3(GN_NT), 0, stream, g);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t units = (int64_t)g.B * g.HW * cpt;
+  const int64_t blocks = std::min<int64_t>(ceil_div(units, GN_NT), 256 * 16);
+  hipLaunchKernelGGL(gn_apply_kernel, dim3((unsigned)blocks), dim3(GN_NT), 0, stream, g);
+  return hipGetLastError();
+}
+
+hipError_t softmax_rows_launch(const SoftmaxArgs& a, hipStream_t stream) {
+  if (a.rows <= 0 || a.n <= 0) return hipSuccess;
+  if (a.n % 4 || a.lds % 4 || a.ldp % 4 || a.lds < a.n || a.ldp < a.n)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(softmax_rows_kernel, dim3((unsigned)a.rows), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t latent_image_launch(const LatentImageArgs& a, hipStream_t stream) {
+  const int64_t total = (int64_t)a.B * 4 * a.hp * a.wp * a.Z;
+  if (total <= 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>(ceil_div(total, 256), 4096);
+  hipLaunchKernelGGL(latent_image_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace dit

@@ -27,10 +27,16 @@ EXPORTS = ("dit_position_ids", "dit_workspace_bytes", "dit_status_string", "dit_
            "dit_dual_block_forward", "dit_single_block_forward", "dit_step_forward",
            "dit_denoise_forward", "dit_profile_begin", "dit_profile_end",
            "dit_modulation_forward_noalloc")
+# the latent decoder (include/dit_vae.h)
+VAE_EXPORTS = ("dit_vae_config_check", "dit_vae_config_default", "dit_vae_workspace_bytes",
+               "dit_vae_decode_forward", "dit_vae_conv_forward", "dit_vae_group_norm_ws_bytes",
+               "dit_vae_group_norm_forward")
 (K_GEMM, K_ATTENTION, K_MODNORM, K_QKV_PAD, K_GEMV, K_ROPE_TABLES, K_TIME, K_SPLIT_SUM, K_LATENT,
- K_ATTN_GEMM, K_COUNT) = range(11)
+ K_ATTN_GEMM, K_CONV, K_GROUPNORM, K_SOFTMAX, K_LATENT_IMAGE, K_COUNT) = range(15)
 KERNEL_NAMES = ("gemm", "attention", "modnorm", "qkv_pad", "gemv", "rope_tables", "time_features",
-                "split_sum", "latent", "attn_gemm")
+                "split_sum", "latent", "attn_gemm", "conv", "group_norm", "softmax",
+                "latent_image")
+VAE_MAX_LAYERS = 4
 MAX_STEPS = 64
 
 
@@ -70,6 +76,28 @@ class ModelWeightsC(C.Structure):
                 ("mod_final", C.c_void_p), ("x_embed", C.c_void_p), ("ctx_embed", C.c_void_p),
                 ("proj_out", C.c_void_p), ("dual", C.POINTER(DualWeightsC)),
                 ("single", C.POINTER(SingleWeightsC))]
+
+
+class VaeConfigC(C.Structure):
+    _fields_ = [("z_channels", C.c_int32), ("block_channels", C.c_int32 * 4),
+                ("layers", C.c_int32), ("groups", C.c_int32), ("eps", C.c_float)]
+
+
+class VaeResnetC(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in ("gn1_gamma", "gn1_beta", "conv1_w", "conv1_b",
+                                          "gn2_gamma", "gn2_beta", "conv2_w", "conv2_b",
+                                          "short_w", "short_b")]
+
+
+class VaeWeightsC(C.Structure):
+    _fields_ = [("lat_scale", C.c_void_p), ("lat_shift", C.c_void_p),
+                ("conv_in_w", C.c_void_p), ("conv_in_b", C.c_void_p),
+                ("mid", VaeResnetC * 2), ("attn_gn_gamma", C.c_void_p),
+                ("attn_gn_beta", C.c_void_p), ("attn_w", C.c_void_p * 4),
+                ("attn_b", C.c_void_p * 4), ("up", (VaeResnetC * VAE_MAX_LAYERS) * 4),
+                ("upconv_w", C.c_void_p * 3), ("upconv_b", C.c_void_p * 3),
+                ("norm_out_gamma", C.c_void_p), ("norm_out_beta", C.c_void_p),
+                ("conv_out_w", C.c_void_p), ("conv_out_b", C.c_void_p)]
 
 
 def library_path() -> str:
@@ -119,6 +147,24 @@ def lib() -> C.CDLL:
     L.dit_profile_begin.argtypes = []
     L.dit_profile_end.restype = C.c_int
     L.dit_profile_end.argtypes = [C.POINTER(KernelStats)]
+    pv = C.POINTER(VaeConfigC)
+    L.dit_vae_config_check.restype = C.c_int
+    L.dit_vae_config_check.argtypes = [pv]
+    L.dit_vae_config_default.restype = None
+    L.dit_vae_config_default.argtypes = [pv]
+    L.dit_vae_workspace_bytes.restype = sz
+    L.dit_vae_workspace_bytes.argtypes = [pv, i32, i32, i32]
+    L.dit_vae_decode_forward.restype = C.c_int
+    L.dit_vae_decode_forward.argtypes = [pv, C.POINTER(VaeWeightsC), vp, i32, i32, i32, vp, vp,
+                                         sz, vp]
+    L.dit_vae_conv_forward.restype = C.c_int
+    L.dit_vae_conv_forward.argtypes = [vp, i32, i32, i32, vp, vp, vp, i32, vp, vp, vp, i32, i32,
+                                       i32, i32, vp, i32, vp]
+    L.dit_vae_group_norm_ws_bytes.restype = sz
+    L.dit_vae_group_norm_ws_bytes.argtypes = [i32, i64, i32, i32]
+    L.dit_vae_group_norm_forward.restype = C.c_int
+    L.dit_vae_group_norm_forward.argtypes = [vp, vp, vp, vp, i32, i64, i32, i32, C.c_float, i32,
+                                             vp, sz, vp]
     _lib = L
     return L
 
@@ -379,3 +425,111 @@ def denoise(cfg: synth.DitConfig, w: ModelWeights, txt, z, ref, sigmas, cos, sin
         C.byref(c), C.byref(w.c), txt.data_ptr(), z.data_ptr(), _ptr(ref), sig.ctypes.data,
         n_steps, B, n_txt, n_img, n_ref, cos.data_ptr(), sin.data_ptr(), p, n, _stream()))
     return z
+
+
+# ---------------------------------------------------------------- latent decoder
+
+def vae_config(vcfg: synth.VaeConfig) -> VaeConfigC:
+    c = VaeConfigC()
+    c.z_channels = vcfg.z_channels
+    for i in range(4):
+        c.block_channels[i] = vcfg.block_channels[i]
+    c.layers, c.groups, c.eps = vcfg.layers, vcfg.groups, vcfg.eps
+    return c
+
+
+def vae_config_check(vcfg: synth.VaeConfig) -> None:
+    c = vae_config(vcfg)
+    _check(lib().dit_vae_config_check(C.byref(c)))
+
+
+def vae_workspace_bytes(vcfg: synth.VaeConfig, B: int, hp: int, wp: int) -> int:
+    c = vae_config(vcfg)
+    n = lib().dit_vae_workspace_bytes(C.byref(c), B, hp, wp)
+    if n == 0:
+        raise DitError(DIT_E_SHAPE, last_error())
+    return int(n)
+
+
+class VaeWeights:
+    """Device copy of synth.vae_weights: conv weights bf16 in their
+    [C_out, kh, kw, C_in] order, everything else fp32."""
+
+    def __init__(self, vcfg: synth.VaeConfig, w: Dict[str, np.ndarray]):
+        self.t = {k: (to_bf16_device(v) if k.endswith(".w") else to_f32_device(v))
+                  for k, v in w.items()}
+        t = self.t
+        g = lambda k: _ptr(t.get(k))
+        s = VaeWeightsC()
+        s.lat_scale, s.lat_shift = g("lat_scale"), g("lat_shift")
+        s.conv_in_w, s.conv_in_b = g("conv_in.w"), g("conv_in.b")
+
+        def res(dst, p):
+            for f, k in (("gn1_gamma", "gn1.g"), ("gn1_beta", "gn1.b"), ("conv1_w", "conv1.w"),
+                         ("conv1_b", "conv1.b"), ("gn2_gamma", "gn2.g"), ("gn2_beta", "gn2.b"),
+                         ("conv2_w", "conv2.w"), ("conv2_b", "conv2.b"), ("short_w", "short.w"),
+                         ("short_b", "short.b")):
+                setattr(dst, f, g(p + k))
+        res(s.mid[0], "mid.res0.")
+        res(s.mid[1], "mid.res1.")
+        s.attn_gn_gamma, s.attn_gn_beta = g("mid.attn.gn.g"), g("mid.attn.gn.b")
+        for i, n in enumerate("qkvo"):
+            s.attn_w[i] = g(f"mid.attn.{n}.w")
+            s.attn_b[i] = g(f"mid.attn.{n}.b")
+        for lv in range(4):
+            for r in range(vcfg.layers):
+                res(s.up[lv][r], f"up{lv}.res{r}.")
+        for lv in range(3):
+            s.upconv_w[lv] = g(f"up{lv}.upconv.w")
+            s.upconv_b[lv] = g(f"up{lv}.upconv.b")
+        s.norm_out_gamma, s.norm_out_beta = g("norm_out.g"), g("norm_out.b")
+        s.conv_out_w, s.conv_out_b = g("conv_out.w"), g("conv_out.b")
+        self.c = s
+
+
+def vae_decode(vcfg: synth.VaeConfig, w: VaeWeights, z, hp: int, wp: int,
+               ws: Optional[Workspace] = None, out=None):
+    """Image fp32 [B, 16 hp, 16 wp, 3] from tokens z fp32 [B, hp * wp, 4 Z]."""
+    torch = _torch()
+    B = z.shape[0]
+    if out is None:
+        out = torch.empty((B, 16 * hp, 16 * wp, 3), dtype=torch.float32, device="cuda")
+    ws = ws or Workspace()
+    p, n = ws.get(vae_workspace_bytes(vcfg, B, hp, wp))
+    c = vae_config(vcfg)
+    _check(lib().dit_vae_decode_forward(C.byref(c), C.byref(w.c), z.data_ptr(), B, hp, wp,
+                                        out.data_ptr(), p, n, _stream()))
+    return out
+
+
+def vae_conv(xin, c_in: int, ksize: int, up: int, w, bias, B: int, H: int, W: int, c_out: int,
+             xs=None, c_short: int = 0, short_w=None, short_b=None, resid=None,
+             out_f32: bool = False, out=None):
+    """One decoder convolution (dit_vae_conv_forward); tensors on the device,
+    activations channels-last bf16, weights bf16 [c_out, k, k, c_in]."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty((B, H, W, c_out), dtype=torch.float32 if out_f32 else torch.bfloat16,
+                          device="cuda")
+    _check(lib().dit_vae_conv_forward(
+        _ptr(xin), c_in, ksize, up, _ptr(w), _ptr(bias), _ptr(xs), c_short, _ptr(short_w),
+        _ptr(short_b), _ptr(resid), B, H, W, c_out, out.data_ptr(), 1 if out_f32 else 0,
+        _stream()))
+    return out
+
+
+def vae_group_norm(x, gamma, beta, B: int, HW: int, Cc: int, groups: int, eps: float,
+                   silu: bool, ws: Optional[Workspace] = None, out=None):
+    """y = act(GroupNorm(x)) (dit_vae_group_norm_forward), bf16 [B, HW, C]."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty((B, HW, Cc), dtype=torch.bfloat16, device="cuda")
+    n = lib().dit_vae_group_norm_ws_bytes(B, HW, Cc, groups)
+    if n == 0:
+        raise DitError(DIT_E_SHAPE, last_error())
+    ws = ws or Workspace()
+    p, cap = ws.get(int(n))
+    _check(lib().dit_vae_group_norm_forward(x.data_ptr(), out.data_ptr(), gamma.data_ptr(),
+                                            beta.data_ptr(), B, HW, Cc, groups, eps,
+                                            1 if silu else 0, p, cap, _stream()))
+    return out

@@ -24,17 +24,22 @@ def L():
     return dit.lib()
 
 
-def header_functions():
-    txt = open(os.path.join(ROOT, "include", "dit.h")).read()
+def header_functions(name):
+    txt = open(os.path.join(ROOT, "include", name)).read()
     txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
-    return sorted(set(re.findall(r"\b(dit_[a-z_]+)\s*\(", txt)))
+    return sorted(set(re.findall(r"\b(dit_[a-z_0-9]+)\s*\(", txt)))
 
 
 def test_exports_every_declared_function(L):
-    names = header_functions()
+    names = header_functions("dit.h")
     assert len(names) == 14, names
     assert sorted(dit.EXPORTS) == names
-    for n in names:
+    vae = header_functions("dit_vae.h")
+    assert len(vae) == 7, vae
+    assert sorted(dit.VAE_EXPORTS) == vae
+    headers = sorted(f for f in os.listdir(os.path.join(ROOT, "include")) if f.endswith(".h"))
+    assert headers == ["dit.h", "dit_vae.h"], headers
+    for n in names + vae:
         assert hasattr(L, n), f"{n} not exported"
 
 
@@ -267,3 +272,120 @@ def test_modulation_noalloc_validation_errors(L):
     assert call([0.5], 1) == dit.DIT_E_NULL
     assert "t_in" in dit.last_error()
     assert f(C.byref(c), C.byref(m), None, 1, FAKE, None) == dit.DIT_E_NULL
+
+
+# ---------------------------------------------------------------- latent decoder
+
+def _vcfg(**kw):
+    import dataclasses
+    return dit.vae_config(dataclasses.replace(synth.VAE_KLEIN, **kw))
+
+
+def test_vae_config_default_and_check(L):
+    c = dit.VaeConfigC()
+    L.dit_vae_config_default(C.byref(c))
+    assert (c.z_channels, list(c.block_channels), c.layers, c.groups) == (32, [128, 256, 512, 512], 3, 32)
+    assert abs(c.eps - 1e-6) < 1e-12
+    assert L.dit_vae_config_check(C.byref(c)) == dit.DIT_OK
+    assert L.dit_vae_config_check(None) == dit.DIT_E_NULL
+    for kw, st in ((dict(z_channels=12), dit.DIT_E_UNSUPPORTED),
+                   (dict(block_channels=(128, 256, 384, 512)), dit.DIT_E_UNSUPPORTED),
+                   (dict(block_channels=(16, 256, 512, 512)), dit.DIT_E_UNSUPPORTED),
+                   (dict(groups=24), dit.DIT_E_UNSUPPORTED),
+                   (dict(layers=0), dit.DIT_E_UNSUPPORTED),
+                   (dict(layers=5), dit.DIT_E_UNSUPPORTED),
+                   (dict(eps=0.0), dit.DIT_E_VALUE)):
+        c = _vcfg(**kw)
+        assert L.dit_vae_config_check(C.byref(c)) == st, kw
+
+
+def test_vae_workspace_bytes(L):
+    c = dit.vae_config(synth.VAE_KLEIN)
+    n1 = L.dit_vae_workspace_bytes(C.byref(c), 1, 64, 64)
+    # four activation buffers of the widest tensor (1024 x 1024 x 256 bf16),
+    # the fp32 scores of all 16384 queries and their bf16 probabilities
+    assert n1 >= 3 * 512 * 2 ** 20 + 256 * 2 ** 20 + 1.5 * 2 ** 30
+    assert L.dit_vae_workspace_bytes(C.byref(c), 2, 64, 64) > n1
+    assert L.dit_vae_workspace_bytes(C.byref(c), 0, 64, 64) == 0
+    assert L.dit_vae_workspace_bytes(C.byref(c), 1, 0, 64) == 0
+    assert L.dit_vae_workspace_bytes(C.byref(c), 1, 64, 3000) == 0
+    # 1920 x 1088: 32640 latent pixels, scores in chunks under 1 GiB
+    n = L.dit_vae_workspace_bytes(C.byref(c), 4, 68, 120)
+    assert 0 < n < 20 * 2 ** 30
+
+
+def test_vae_decode_validation_errors(L):
+    c = dit.vae_config(synth.VAE_TINY)
+    w = dit.VaeWeightsC()
+    fake = 1 << 20  # never dereferenced: validation fails first
+    st = L.dit_vae_decode_forward(C.byref(c), C.byref(w), fake, 1, 2, 2, fake, fake, 1 << 30, None)
+    assert st == dit.DIT_E_NULL and "weight" in dit.last_error()
+    st = L.dit_vae_decode_forward(C.byref(c), None, fake, 1, 2, 2, fake, fake, 1 << 30, None)
+    assert st == dit.DIT_E_NULL
+    # every weight present: shape, alignment and workspace errors
+    ptrs = iter(range(1 << 20, 1 << 40, 1 << 12))
+    vcfg = synth.VAE_TINY
+    for f, _ in dit.VaeWeightsC._fields_:
+        v = getattr(w, f)
+        if isinstance(v, int) or v is None:
+            setattr(w, f, next(ptrs))
+    for arr in (w.attn_w, w.attn_b, w.upconv_w, w.upconv_b):
+        for i in range(len(arr)):
+            arr[i] = next(ptrs)
+
+    def fill(r, ci, co):
+        for f, _ in dit.VaeResnetC._fields_:
+            if f.startswith("short") and ci == co:
+                setattr(r, f, None)
+            else:
+                setattr(r, f, next(ptrs))
+    for name, ci, co in vcfg.resnet_channels():
+        if name.startswith("mid"):
+            fill(w.mid[int(name[7])], ci, co)
+        else:
+            fill(w.up[int(name[2])][int(name[7])], ci, co)
+    need = L.dit_vae_workspace_bytes(C.byref(c), 1, 2, 2)
+    # (never a call whose arguments are all valid: it would launch kernels)
+    st = L.dit_vae_decode_forward(C.byref(c), C.byref(w), fake, 0, 2, 2, fake, fake, need, None)
+    assert st == dit.DIT_E_SHAPE
+    st = L.dit_vae_decode_forward(C.byref(c), C.byref(w), fake, 1, 2, 2, fake, fake, need - 1, None)
+    assert st == dit.DIT_E_WORKSPACE
+    st = L.dit_vae_decode_forward(C.byref(c), C.byref(w), fake + 4, 1, 2, 2, fake, fake, need, None)
+    assert st == dit.DIT_E_SHAPE and "aligned" in dit.last_error()
+    # a shortcut where the width is kept, and a missing one where it changes
+    w.mid[0].short_w = next(ptrs)
+    st = L.dit_vae_decode_forward(C.byref(c), C.byref(w), fake, 1, 2, 2, fake, fake, need, None)
+    assert st == dit.DIT_E_NULL and "shortcut" in dit.last_error()
+    w.mid[0].short_w = None
+    w.up[1][0].short_w = None
+    st = L.dit_vae_decode_forward(C.byref(c), C.byref(w), fake, 1, 2, 2, fake, fake, need, None)
+    assert st == dit.DIT_E_NULL
+
+
+def test_vae_conv_and_group_norm_validation_errors(L):
+    fake = 1 << 20
+    conv = L.dit_vae_conv_forward
+    ok = dict(xin=fake, c_in=64, ksize=3, up=0, w=fake, bias=fake, xs=None, c_short=0,
+              short_w=None, short_b=None, resid=None, B=1, H=8, W=8, c_out=64, out=fake,
+              out_f32=0, stream=None)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return conv(*a.values())
+    assert call(xin=None) == dit.DIT_E_NULL
+    assert call(c_in=12) == dit.DIT_E_SHAPE
+    assert call(ksize=5) == dit.DIT_E_SHAPE
+    assert call(up=1, H=7) == dit.DIT_E_SHAPE
+    assert call(xs=fake) == dit.DIT_E_NULL
+    assert call(B=0) == dit.DIT_E_SHAPE
+    assert call(H=1) == dit.DIT_E_SHAPE
+    assert call(out=fake + 8) == dit.DIT_E_SHAPE
+    gn = L.dit_vae_group_norm_forward
+    need = L.dit_vae_group_norm_ws_bytes(1, 100, 64, 32)
+    assert need > 0
+    assert gn(fake, fake + 4096, fake, fake, 1, 100, 48, 16, 1e-6, 1, fake, need, None) == dit.DIT_E_UNSUPPORTED
+    assert gn(fake, fake + 4096, fake, fake, 1, 100, 64, 24, 1e-6, 1, fake, need, None) == dit.DIT_E_UNSUPPORTED
+    assert gn(fake, fake, fake, fake, 1, 100, 64, 32, 1e-6, 1, fake, need, None) == dit.DIT_E_VALUE
+    assert gn(fake, fake + 4096, fake, fake, 1, 100, 64, 32, 0.0, 1, fake, need, None) == dit.DIT_E_VALUE
+    assert gn(fake, fake + 4096, fake, fake, 1, 100, 64, 32, 1e-6, 1, fake, need - 1, None) == dit.DIT_E_WORKSPACE
