@@ -12,7 +12,8 @@ stream. A second, separate pass records HIP events around every kernel
 launch (dit_profile_begin/end) to give per-kernel durations for the
 roofline; the headline number comes from the clean pass. The same run also
 times the step with one reference image (S = 8704) and the 1920x1088 batch-4
-step (S = 8672 per sample) under "workloads". The CPU baseline times the
+step (S = 8672 per sample) under "workloads", and the latent decoder at
+1024x1024 and at 1920x1088 batch 4 under "vae_decode". The CPU baseline times the
 oracle in fp32 NumPy on one whole step of the workload's first sample, after
 a one-block warm-up.
 """
@@ -226,6 +227,75 @@ def time_workload(dit, synth, torch, cfg, dw, wl, steps=10, warmup=2):
     return res
 
 
+def time_decode(dit, synth, torch, vwl, vdw, steps=5, warmup=1):
+    """The latent decoder on workload vwl: median / p95 ms of whole decodes
+    (HIP events on the launch stream), algorithmic TFLOP/s, and per-kernel
+    figures from one event pass (conv TFLOP/s and its fraction of the bf16
+    peak; GroupNorm and softmax GB/s)."""
+    vcfg = synth.VAE_KLEIN
+    hp, wp = vwl.grid
+    z = dit.to_f32_device(np.stack([synth.vae_latents(vcfg, b, hp, wp) for b in range(vwl.batch)]))
+    ws = dit.Workspace()
+    img = torch.empty((vwl.batch, 16 * hp, 16 * wp, 3), dtype=torch.float32, device="cuda")
+
+    def one():
+        dit.vae_decode(vcfg, vdw, z, hp, wp, ws=ws, out=img)
+
+    for _ in range(warmup):
+        one()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for e0, e1 in evs:
+        e0.record()
+        one()
+        e1.record()
+    torch.cuda.synchronize()
+    per = np.array([a.elapsed_time(b) for a, b in evs])
+    assert np.all(np.isfinite(img.cpu().numpy())), f"{vwl.name}: non-finite image"
+    dit.profile_begin()
+    one()
+    k = dit.profile_end()
+    flops = sum(s["flops"] for s in k.values())
+    med = float(np.median(per))
+    res = {"batch": vwl.batch, "image": [16 * hp, 16 * wp], "ms_median": round(med, 3),
+           "ms_p95": round(float(np.percentile(per, 95)), 3),
+           "tflop": round(flops / 1e12, 3), "tflops": round(flops / (med * 1e-3) / 1e12, 1),
+           "frac_of_bf16_peak": round(flops / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    for name in ("conv", "group_norm", "softmax", "latent_image"):
+        s = k[name]
+        if s["launches"] == 0:
+            continue
+        e = {"launches": s["launches"], "ms": round(s["total_ms"], 3),
+             "avg_launch_us": round(1000.0 * s["total_ms"] / s["launches"], 2)}
+        if s["flops"] > 0:
+            tf = s["flops"] / (s["total_ms"] * 1e-3) / 1e12
+            e["tflops"] = round(tf, 1)
+            e["frac_of_bf16_peak"] = round(tf / PEAK_BF16_TFLOPS, 4)
+            e["alg_bytes"] = s["bytes"]
+        else:
+            gbs = s["bytes"] / (s["total_ms"] * 1e-3) / 1e9
+            e["gbs"] = round(gbs, 1)
+            e["frac_of_hbm_peak"] = round(gbs / PEAK_HBM_GBS, 4)
+        res[name] = e
+    del ws, img, z
+    torch.cuda.empty_cache()
+    return res
+
+
+def decode_leg(dit, synth, torch, which):
+    """Decoder timings for the named workloads (weights drawn once)."""
+    vdw = dit.VaeWeights(synth.VAE_KLEIN, synth.vae_weights(synth.VAE_KLEIN, 0))
+    out = {}
+    for vwl in which:
+        log(f"decode {vwl.name}")
+        out[vwl.name] = time_decode(dit, synth, torch, vwl, vdw)
+        log(f"  {json.dumps(out[vwl.name])}")
+    del vdw
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -243,6 +313,10 @@ def main():
                     help="timed runs of the 4-step sampling loop, eager and graph-replayed")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="end with three device copies of COPY_CAL_BYTES (counter calibration)")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the latent decoder timings (1024x1024 and 1920x1088 batch 4)")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="time only the latent decoder and print its JSON record")
     ap.add_argument("--summarize", metavar="DIR",
                     help="print a markdown summary of rocprofv3 CSV output in DIR and exit")
     args = ap.parse_args()
@@ -262,6 +336,11 @@ def main():
         sys.exit(1)
     dit.lib()
     torch.cuda.set_device(0)
+    if args.decode_only:
+        which = (synth.V_DECODE_1024,) if args.no_extra_workloads else (
+            synth.V_DECODE_1024, synth.V_DECODE_1920x1088_B4)
+        print(json.dumps({"vae_decode": decode_leg(dit, synth, torch, which)}), flush=True)
+        return
     cfg = synth.FLUX2_KLEIN
     wl = {w.name: w for w in (synth.W_STEP_1024, synth.W_STEP_1024_REF, synth.W_STEP_1920x1088_B4,
                               synth.W_STEP_848x624_3REF, synth.W_STEP_512_REF)}[args.workload]
@@ -392,6 +471,12 @@ def main():
             extra[xw.name] = time_workload(dit, synth, torch, cfg, dw, xw)
             log(f"  {json.dumps(extra[xw.name])}")
 
+    dec = None
+    if not args.no_decode:
+        which = (synth.V_DECODE_1024,) if args.no_extra_workloads else (
+            synth.V_DECODE_1024, synth.V_DECODE_1920x1088_B4)
+        dec = decode_leg(dit, synth, torch, which)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("CPU baseline: the oracle in fp32 NumPy, one whole step after a one-block warm-up")
@@ -441,6 +526,7 @@ def main():
         "kernels": kern,
         "workloads": extra,
         "denoise_loop": den,
+        "vae_decode": dec,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

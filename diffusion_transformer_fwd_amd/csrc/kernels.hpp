@@ -251,7 +251,7 @@ struct ConvArgs {
   int64_t out_bs, resid_bs;
   int32_t nsrc, B, H, W, N, ldo, ldr, out_f32, bias_rows;
   int32_t vec;          // 16-byte epilogue stores allowed (set by conv_launch)
-  int32_t tiles_m, tiles_n, cfg;  // set by conv_launch
+  int32_t tiles_m, tiles_n, tiles_x, cfg;  // set by conv_launch
 };
 // Checks the shapes the kernel assumes (returns hipErrorInvalidValue on a
 // violation), picks the tile shape and launches.

@@ -30,6 +30,7 @@
 // bitwise independent.
 #include <algorithm>
 #include <cmath>
+#include <cstdlib>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -45,6 +46,123 @@ constexpr uint32_t OOB = 0x80000000u;  // beyond every buffer's range (< 2^31 by
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Epilogue of a conv tile: the lane holds tile rows wm*64 + 32 i + fr (i <
+// 2) and channels wn*32FN + 32 j + 8q + 4fg + 0..3 of its accumulators. Pass
+// p stages block i = p of every wave as fp32 [WM*32][BN] in LDS (16-byte
+// chunk c of row r at c ^ (r & SWM)); the caller's LDS must be free (the
+// main loop's last fragment reads came before its last barrier). pix(t) is
+// the output pixel of tile row t, or -1 for none. Bias(es) and the residual
+// are added in fp32 and the sum is rounded once (bf16) or stored fp32.
+template <int WM, int FN, class PixOf>
+__device__ __forceinline__ void conv_epilogue(const ConvArgs& a, f32x16 (&acc)[2][FN], char* T,
+                                              int b, int n0, int wm, int wn, int fr, int fg,
+                                              PixOf pix) {
+  constexpr int WN = 8 / WM;
+  constexpr int FM = 2;
+  constexpr int BN = 32 * FN * WN;
+  const int tid = threadIdx.x;
+  constexpr int SROW = BN * 4;
+  constexpr int SWM = (BN / 4 < 32 ? BN / 4 : 32) - 1;
+  constexpr int UPR = BN / 8;  // 8-channel units per stage row
+#pragma unroll
+  for (int pass = 0; pass < FM; ++pass) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = wm * 32 + fr;
+        const int c = (wn * 32 * FN + j * 32 + 8 * q + 4 * fg) >> 2;
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = acc[pass][j][4 * q + e];
+        *reinterpret_cast<f32x4*>(T + r * SROW + ((c ^ (r & SWM)) << 4)) = v;
+      }
+    __syncthreads();
+    for (int u = tid; u < WM * 32 * UPR; u += CNT) {
+      const int r = u / UPR, cu = u - r * UPR;
+      const int m = pix((r >> 5) * 64 + 32 * pass + (r & 31));
+      const int col = n0 + 8 * cu;
+      if (m < 0 || col >= a.N) continue;
+      const f32x4 v0 = *reinterpret_cast<const f32x4*>(T + r * SROW + (((2 * cu) ^ (r & SWM)) << 4));
+      const f32x4 v1 =
+          *reinterpret_cast<const f32x4*>(T + r * SROW + (((2 * cu + 1) ^ (r & SWM)) << 4));
+      float o[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+      const int nv = a.N - col < 8 ? a.N - col : 8;
+      const bool full = nv == 8 && a.vec;
+      if (a.bias) {
+        if (a.bias_rows) {
+          const float bb = a.bias[m];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[e] += bb;
+        } else if (full) {
+          const f32x4 b0 = *reinterpret_cast<const f32x4*>(a.bias + col);
+          const f32x4 b1 = *reinterpret_cast<const f32x4*>(a.bias + col + 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            o[e] += b0[e];
+            o[4 + e] += b1[e];
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (e < nv) o[e] += a.bias[col + e];
+        }
+      }
+      if (a.bias2) {
+        if (full) {
+          const f32x4 b0 = *reinterpret_cast<const f32x4*>(a.bias2 + col);
+          const f32x4 b1 = *reinterpret_cast<const f32x4*>(a.bias2 + col + 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            o[e] += b0[e];
+            o[4 + e] += b1[e];
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (e < nv) o[e] += a.bias2[col + e];
+        }
+      }
+      if (a.resid) {
+        const bf16_t* rp = a.resid + (int64_t)b * a.resid_bs + (int64_t)m * a.ldr + col;
+        if (full) {
+          const u32x4 rv = *reinterpret_cast<const u32x4*>(rp);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[e] += bf16_to_f32((rv[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (e < nv) o[e] += bf16_to_f32(rp[e]);
+        }
+      }
+      if (a.out_f32) {
+        float* op = static_cast<float*>(a.out) + (int64_t)b * a.out_bs + (int64_t)m * a.ldo + col;
+        if (full) {
+          *reinterpret_cast<f32x4*>(op) = f32x4{o[0], o[1], o[2], o[3]};
+          *reinterpret_cast<f32x4*>(op + 4) = f32x4{o[4], o[5], o[6], o[7]};
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (e < nv) op[e] = o[e];
+        }
+      } else {
+        bf16_t* op = static_cast<bf16_t*>(a.out) + (int64_t)b * a.out_bs + (int64_t)m * a.ldo + col;
+        const f32x8 ov = {o[0], o[1], o[2], o[3], o[4], o[5], o[6], o[7]};
+        const bf16x8 pv = pack_bf16x8(ov);
+        if (full) {
+          *reinterpret_cast<bf16x8*>(op) = pv;
+        } else {
+          const u32x4 pw = __builtin_bit_cast(u32x4, pv);
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (e < nv) op[e] = (bf16_t)((pw[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+        }
+      }
+    }
+    __syncthreads();  // the next pass overwrites the stage
+  }
+}
 
 // WM waves along the pixels (4 or 8), 8 / WM along the channels; wave tile
 // 64 x 32 FN.
@@ -116,6 +234,12 @@ __global__ __launch_bounds__(CNT, 1) void conv_kernel(const ConvArgs a) {
     const int j = kt - (s ? slices0 : 0);
     const int C = S.C, lda = S.lda, taps = S.taps, up = S.up;
     const int kend = taps * C;
+    // K order: a 3x3 conv over whole 64-channel slices runs slices outer and
+    // taps inner (slice j = 9 cs + tap), the order of the halo kernel, so
+    // either kernel gives the same bits; other sources run k = tap C + c in
+    // order, 64 at a time.
+    const bool cs_outer = taps == 9 && C % CBK == 0;
+    const int cs_u = cs_outer ? j / 9 : 0, tap_u = cs_outer ? j - 9 * cs_u : 0;
     // per chunk parity: tap offsets, channel, and whether k is in range
     int dy[2], dx[2], ci[2];
     bool kok[2];
@@ -123,12 +247,20 @@ __global__ __launch_bounds__(CNT, 1) void conv_kernel(const ConvArgs a) {
 #pragma unroll
     for (int par = 0; par < 2; ++par) {
       const int cl = lp ^ lr ^ par;
-      const int k = j * CBK + cl * 8;
+      int tap, c, k;
+      if (cs_outer) {
+        tap = tap_u;
+        c = cs_u * CBK + cl * 8;
+        k = tap * C + c;
+        kok[par] = true;
+      } else {
+        k = j * CBK + cl * 8;
+        kok[par] = k < kend;
+        tap = taps != 1 ? (int)(((float)k + 0.5f) * S.inv_c) : 0;
+        c = k - tap * C;
+      }
       kk[par] = k;
-      kok[par] = k < kend;
-      int tap = 0;
-      if (taps != 1) tap = (int)(((float)k + 0.5f) * S.inv_c);
-      ci[par] = k - tap * C;
+      ci[par] = c;
       const int ty = (tap * 11) >> 5;  // tap / 3 for tap < 9
       dy[par] = taps == 1 ? 0 : ty - 1;
       dx[par] = taps == 1 ? 0 : tap - 3 * ty - 1;
@@ -228,112 +360,193 @@ __global__ __launch_bounds__(CNT, 1) void conv_kernel(const ConvArgs a) {
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  // ---- epilogue. Lane holds pixel rows wm*64 + i*32 + fr (i < 2) and
-  // channels wn*32FN + j*32 + 8q + 4fg + 0..3. Pass p stages block i = p of
-  // every wave as fp32 [WM*32][BN] (16-byte chunk c of row r at
-  // c ^ (r & SWM)); the LDS is free (the loop's last fragment reads came
-  // before its last barrier).
-  char* const T = reinterpret_cast<char*>(lds);
-  constexpr int SROW = BN * 4;
-  constexpr int SWM = (BN / 4 < 32 ? BN / 4 : 32) - 1;
-  constexpr int UPR = BN / 8;  // 8-channel units per stage row
+  conv_epilogue<WM, FN>(a, acc, reinterpret_cast<char*>(lds), b, n0, wm, wn, fr, fg,
+                        [&](int t) { return m0 + t < M ? m0 + t : -1; });
+}
+
+// ------------------------------------------------------------------ halo conv
+// 3x3 convolution with the input halo of the tile resident in LDS: the
+// implicit GEMM above reloads a pixel's K slice once per tap; here an output
+// tile of 8 image rows x 32 columns loads its (8 + 2) x (32 + 2) input
+// pixels once per 64-channel slice and the 9 taps read shifted fragments of
+// it, so per channel slice the L2 -> LDS stream is the halo (44 KiB) plus
+// the 9 taps' weights (BN x 128 bytes each) instead of 9 x (256 + BN) rows.
+//  * K order: channel slices outer, taps inner (tap = 3 (dy + 1) + dx + 1),
+//    16-wide k-steps, the same for every tile: batch rows stay bitwise
+//    independent.
+//  * Steps (slice, tap): a tap's weights go to one of two W buffers, a
+//    slice's halo to one of two halo buffers, each loaded one step ahead
+//    (the halo at the step before the slice's first tap); one barrier per
+//    step. Out-of-image halo pixels (zero padding) read through an offset
+//    past the buffer's range. With `up`, the halo pixel (Y, X) of the output
+//    grid reads source pixel (Y / 2, X / 2).
+//  * Waves: 4 along the rows (two image rows = two 32-pixel MFMA blocks
+//    each) x 2 along the channels (32 FN each); BN = 64 FN.
+constexpr int HT_ROWS = 8, HT_COLS = 32;
+constexpr int HALO_W = HT_COLS + 2;
+constexpr int HALO_PIX = (HT_ROWS + 2) * HALO_W;       // 340
+constexpr int HALO_GROUPS = (HALO_PIX + 7) / 8;        // 8-pixel load groups: 43
+constexpr int HALO_U = HALO_GROUPS * 8 * ROW_U;        // LDS units per halo buffer
+
+template <int FN>
+__global__ __launch_bounds__(CNT, 1) void conv3_halo_kernel(const ConvArgs a) {
+  constexpr int WM = 4, FM = 2;
+  constexpr int BN = 64 * FN;
+  constexpr int W_U = BN * ROW_U;
+  constexpr int HG_PER = (HALO_GROUPS + 3) / 4;  // halo groups per loader wave (at most)
+  constexpr int WG_PER = BN / 8 / 4;             // weight-row groups per loader wave
+  __shared__ u32x4 lds[2 * HALO_U + 2 * W_U];    // halo 0 | halo 1 | W 0 | W 1
+  static_assert(WM * 32 * BN * 4 <= (2 * HALO_U + 2 * W_U) * 16, "epilogue stage fits");
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int per_b = a.tiles_m * a.tiles_n;
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  const int b = L / per_b;
+  const int rem = L - b * per_b;
+  const int tm = rem / a.tiles_n, tn = rem - tm * a.tiles_n;
+  const int ty = tm / a.tiles_x, tx = tm - ty * a.tiles_x;
+  const int y0 = ty * HT_ROWS, x0 = tx * HT_COLS, n0 = tn * BN;
+  const int H = a.H, W = a.W;
+  const ConvSource& S = a.src[0];
+  const int C = S.C, lda = S.lda, up = S.up;
+  const int Wi = up ? (W >> 1) : W;
+  const int nsteps = (C / CBK) * 9;
+  const __amdgpu_buffer_rsrc_t ar = make_rsrc(S.x + (int64_t)b * S.x_bs, S.x_bytes);
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(S.w + (int64_t)b * S.w_bs, S.w_bytes);
+
+  // ---- loaders (waves 4-7). Lane (lr, lp) of an 8-row load group g writes
+  // physical chunk lp of row 8g + lr (a halo pixel or a weight row), whose
+  // swizzle is swz(8g + lr) = lr ^ (g & 1): it fetches logical chunk
+  // lp ^ lr ^ (g & 1).
+  const int lr = lane >> 3, lp = lane & 7;
+  const bool loader = wave >= 4;
+  const int lw = wave - 4;
+  const uint32_t cofs[2] = {(uint32_t)((lp ^ lr) * 16), (uint32_t)((lp ^ lr ^ 1) * 16)};
+  uint32_t hoff[HG_PER];  // byte offset of channel 0 of the lane's halo pixels, or OOB
 #pragma unroll
-  for (int pass = 0; pass < FM; ++pass) {
+  for (int i = 0; i < HG_PER; ++i) {
+    const int g = lw + 4 * i;
+    const int p = 8 * g + lr;
+    const int hy = p / HALO_W, hx = p - hy * HALO_W;
+    const int Y = y0 - 1 + hy, X = x0 - 1 + hx;
+    const bool ok = g < HALO_GROUPS && p < HALO_PIX && (unsigned)Y < (unsigned)H &&
+                    (unsigned)X < (unsigned)W;
+    const int sy = up ? (Y >> 1) : Y, sx = up ? (X >> 1) : X;
+    hoff[i] = ok ? (uint32_t)((sy * Wi + sx) * lda) * 2u : OOB;
+  }
+  uint32_t woff[WG_PER];  // byte offset of the lane's weight rows, or OOB
+#pragma unroll
+  for (int i = 0; i < WG_PER; ++i) {
+    const int n = n0 + 8 * (lw + 4 * i) + lr;
+    woff[i] = n < a.N ? (uint32_t)(n * S.ldw) * 2u : OOB;
+  }
+  auto load_halo = [&](int cs, int buf) {
+    if (!loader) return;
+    u32x4* const dst = lds + buf * HALO_U;
+#pragma unroll
+    for (int i = 0; i < HG_PER; ++i) {
+      const int g = lw + 4 * i;
+      if (g >= HALO_GROUPS) break;
+      const uint32_t off = hoff[i] == OOB ? OOB : hoff[i] + (uint32_t)(cs * CBK * 2) + cofs[g & 1];
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, (lds_ptr_t)(dst + 8 * g * ROW_U), 16, off, 0,
+                                               0, 0);
+    }
+  };
+  auto load_w = [&](int cs, int tap, int buf) {
+    if (!loader) return;
+    u32x4* const dst = lds + 2 * HALO_U + buf * W_U;
+    const uint32_t kb = (uint32_t)((tap * C + cs * CBK) * 2);
+#pragma unroll
+    for (int i = 0; i < WG_PER; ++i) {
+      const int g = lw + 4 * i;
+      const uint32_t off = woff[i] == OOB ? OOB : woff[i] + kb + cofs[g & 1];
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_ptr_t)(dst + 8 * g * ROW_U), 16, off, 0,
+                                               0, 0);
+    }
+  };
+
+  // ---- fragments: block i of wave wm is image row 2 wm + i of the tile;
+  // for tap (dy, dx) its 32 pixels are halo pixels (2 wm + i + 1 + dy) *
+  // HALO_W + fr + 1 + dx
+  const int fr = lane & 31, fg = lane >> 5;
+  const int wm = wave & 3, wn = wave >> 2;
+  const int w_rd = (wn * 32 * FN + fr) * ROW_U;
+  const int sfr = swz(fr);
+  bf16x8 af[2][FM], wf[2][FN];
+  auto fload = [&](int cs, int tap, int step, int s, int buf) {
+    const int ty3 = (tap * 11) >> 5;
+    const int dy = ty3 - 1, dx = tap - 3 * ty3 - 1;
+    const u32x4* hb = lds + (cs & 1) * HALO_U;
+    const u32x4* wb = lds + 2 * HALO_U + (step & 1) * W_U;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int p = (2 * wm + i + 1 + dy) * HALO_W + fr + 1 + dx;
+      af[buf][i] = __builtin_bit_cast(bf16x8, hb[p * ROW_U + ((2 * s + fg) ^ swz(p))]);
+    }
 #pragma unroll
     for (int j = 0; j < FN; ++j)
+      wf[buf][j] = __builtin_bit_cast(bf16x8, wb[w_rd + j * 32 * ROW_U + ((2 * s + fg) ^ sfr)]);
+  };
+  f32x16 acc[FM][FN];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int r = wm * 32 + fr;
-        const int c = (wn * 32 * FN + j * 32 + 8 * q + 4 * fg) >> 2;
-        f32x4 v;
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = acc[pass][j][4 * q + e];
-        *reinterpret_cast<f32x4*>(T + r * SROW + ((c ^ (r & SWM)) << 4)) = v;
-      }
-    __syncthreads();
-    for (int u = tid; u < WM * 32 * UPR; u += CNT) {
-      const int r = u / UPR, cu = u - r * UPR;
-      const int m = m0 + (r >> 5) * 64 + 32 * pass + (r & 31);
-      const int col = n0 + 8 * cu;
-      if (m >= M || col >= a.N) continue;
-      const f32x4 v0 = *reinterpret_cast<const f32x4*>(T + r * SROW + (((2 * cu) ^ (r & SWM)) << 4));
-      const f32x4 v1 =
-          *reinterpret_cast<const f32x4*>(T + r * SROW + (((2 * cu + 1) ^ (r & SWM)) << 4));
-      float o[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-      const int nv = a.N - col < 8 ? a.N - col : 8;
-      const bool full = nv == 8 && a.vec;
-      if (a.bias) {
-        if (a.bias_rows) {
-          const float bb = a.bias[m];
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
+  auto mfmas = [&](int buf) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) o[e] += bb;
-        } else if (full) {
-          const f32x4 b0 = *reinterpret_cast<const f32x4*>(a.bias + col);
-          const f32x4 b1 = *reinterpret_cast<const f32x4*>(a.bias + col + 4);
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            o[e] += b0[e];
-            o[4 + e] += b1[e];
-          }
-        } else {
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] =
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[buf][j], af[buf][i], acc[i][j], 0, 0, 0);
+  };
+
+  load_halo(0, 0);
+  load_w(0, 0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (nsteps > 1) load_w(0, 1, 1);
+  fload(0, 0, 0, 0, 0);
+  int cs = 0, tap = 0;  // of the current step
+  for (int step = 0; step < nsteps; ++step) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (e < nv) o[e] += a.bias[col + e];
-        }
-      }
-      if (a.bias2) {
-        if (full) {
-          const f32x4 b0 = *reinterpret_cast<const f32x4*>(a.bias2 + col);
-          const f32x4 b1 = *reinterpret_cast<const f32x4*>(a.bias2 + col + 4);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            o[e] += b0[e];
-            o[4 + e] += b1[e];
-          }
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (e < nv) o[e] += a.bias2[col + e];
-        }
-      }
-      if (a.resid) {
-        const bf16_t* rp = a.resid + (int64_t)b * a.resid_bs + (int64_t)m * a.ldr + col;
-        if (full) {
-          const u32x4 rv = *reinterpret_cast<const u32x4*>(rp);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) o[e] += bf16_to_f32((rv[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (e < nv) o[e] += bf16_to_f32(rp[e]);
-        }
-      }
-      if (a.out_f32) {
-        float* op = static_cast<float*>(a.out) + (int64_t)b * a.out_bs + (int64_t)m * a.ldo + col;
-        if (full) {
-          *reinterpret_cast<f32x4*>(op) = f32x4{o[0], o[1], o[2], o[3]};
-          *reinterpret_cast<f32x4*>(op + 4) = f32x4{o[4], o[5], o[6], o[7]};
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (e < nv) op[e] = o[e];
-        }
-      } else {
-        bf16_t* op = static_cast<bf16_t*>(a.out) + (int64_t)b * a.out_bs + (int64_t)m * a.ldo + col;
-        const f32x8 ov = {o[0], o[1], o[2], o[3], o[4], o[5], o[6], o[7]};
-        const bf16x8 pv = pack_bf16x8(ov);
-        if (full) {
-          *reinterpret_cast<bf16x8*>(op) = pv;
-        } else {
-          const u32x4 pw = __builtin_bit_cast(u32x4, pv);
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (e < nv) op[e] = (bf16_t)((pw[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
-        }
-      }
+    for (int s = 0; s < CBK / 16 - 1; ++s) {
+      fload(cs, tap, step, s + 1, (s + 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas(s & 1);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __syncthreads();  // the next pass overwrites the stage
+    // every wave is done with this step's buffers; the next step's landed
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    __syncthreads();
+    int cs1 = cs, tap1 = tap + 1;
+    if (tap1 == 9) {
+      tap1 = 0;
+      ++cs1;
+    }
+    if (step + 2 < nsteps) {
+      int cs2 = cs1, tap2 = tap1 + 1;
+      if (tap2 == 9) {
+        tap2 = 0;
+        ++cs2;
+      }
+      load_w(cs2, tap2, step & 1);
+      if (tap2 == 0) load_halo(cs2, cs2 & 1);
+    }
+    if (step + 1 < nsteps) fload(cs1, tap1, step + 1, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas((CBK / 16 - 1) & 1);
+    __builtin_amdgcn_sched_barrier(0);
+    cs = cs1;
+    tap = tap1;
   }
+
+  conv_epilogue<WM, FN>(a, acc, reinterpret_cast<char*>(lds), b, n0, wm, wn, fr, fg,
+                        [&](int t) {
+                          const int y = y0 + (t >> 5), x = x0 + (t & 31);
+                          return (y < H && x < W) ? y * W + x : -1;
+                        });
 }
 
 // ------------------------------------------------------------------ GroupNorm
@@ -414,72 +627,94 @@ __global__ __launch_bounds__(GN_NT) void gn_stats_kernel(const GroupNormArgs g) 
   }
 }
 
-// Per sample: each wave reduces whole groups (lane l takes blocks l, l + 64,
-// ... in order, then a fixed shuffle tree), in double; then the per-channel
-// scale and shift.
+// One workgroup per (group, sample): thread t adds the partials of blocks
+// t, t + 256, ... in order, in double; a fixed shuffle tree and the four
+// waves in order give the totals; then the group's per-channel scale and
+// shift.
 __global__ __launch_bounds__(GN_NT) void gn_finalize_kernel(const GroupNormArgs g) {
-  __shared__ double mr[2 * 1024];
+  __shared__ double red[2][GN_NT / 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int b = blockIdx.x;
+  const int gg = blockIdx.x, b = blockIdx.y;
   const int cg = g.C / g.G;
-  const bf16_t* x = g.x + (int64_t)b * g.x_bs;
-  for (int gg = wave; gg < g.G; gg += GN_NT / 64) {
-    double a1 = 0.0, a2 = 0.0;
-    for (int k = lane; k < g.nblk; k += 64) {
-      const float* p = g.part + (((int64_t)b * g.nblk + k) * g.G + gg) * 2;
-      a1 += (double)p[0];
-      a2 += (double)p[1];
-    }
+  double a1 = 0.0, a2 = 0.0;
+  for (int k = tid; k < g.nblk; k += GN_NT) {
+    const float* p = g.part + (((int64_t)b * g.nblk + k) * g.G + gg) * 2;
+    a1 += (double)p[0];
+    a2 += (double)p[1];
+  }
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      a1 += __shfl_xor(a1, o, 64);
-      a2 += __shfl_xor(a2, o, 64);
-    }
-    if (lane == 0) {
-      const double n = (double)g.HW * (double)cg;
-      const double md = a1 / n;
-      double var = a2 / n - md * md;
-      if (var < 0.0) var = 0.0;
-      mr[2 * gg] = (double)bf16_to_f32(x[gg * cg]) + md;
-      mr[2 * gg + 1] = 1.0 / sqrt(var + (double)g.eps);
-    }
+  for (int o = 32; o >= 1; o >>= 1) {
+    a1 += __shfl_xor(a1, o, 64);
+    a2 += __shfl_xor(a2, o, 64);
+  }
+  if (lane == 0) {
+    red[0][wave] = a1;
+    red[1][wave] = a2;
   }
   __syncthreads();
-  for (int c = tid; c < g.C; c += GN_NT) {
-    const int gg = c / cg;
-    const double sc = (double)g.gamma[c] * mr[2 * gg + 1];
+  double s1 = 0.0, s2 = 0.0;
+#pragma unroll
+  for (int w = 0; w < GN_NT / 64; ++w) {
+    s1 += red[0][w];
+    s2 += red[1][w];
+  }
+  const bf16_t* x = g.x + (int64_t)b * g.x_bs;
+  const double n = (double)g.HW * (double)cg;
+  const double md = s1 / n;
+  double var = s2 / n - md * md;
+  if (var < 0.0) var = 0.0;
+  const double mean = (double)bf16_to_f32(x[gg * cg]) + md;
+  const double rstd = 1.0 / sqrt(var + (double)g.eps);
+  for (int c = gg * cg + tid; c < (gg + 1) * cg; c += GN_NT) {
+    const double sc = (double)g.gamma[c] * rstd;
     g.ab[((int64_t)b * g.C + c) * 2] = (float)sc;
-    g.ab[((int64_t)b * g.C + c) * 2 + 1] = (float)((double)g.beta[c] - mr[2 * gg] * sc);
+    g.ab[((int64_t)b * g.C + c) * 2 + 1] = (float)((double)g.beta[c] - mean * sc);
   }
 }
 
-// y = act(x a_c + s_c), 8 channels per thread and step.
+// y = act(x a_c + s_c), 8 channels per thread and step. Grid (., B): a
+// thread keeps one 8-channel chunk (the grid stride is a multiple of C / 8)
+// and its scale / shift in registers, and has four steps' loads in flight.
 __global__ __launch_bounds__(GN_NT) void gn_apply_kernel(const GroupNormArgs g) {
-  const int64_t units_b = (int64_t)g.HW * (g.C >> 3);
-  const int64_t total = units_b * g.B;
+  constexpr int U = 4;
+  const int b = blockIdx.y;
   const int cpt = g.C >> 3;
-  for (int64_t u = (int64_t)blockIdx.x * GN_NT + threadIdx.x; u < total;
-       u += (int64_t)gridDim.x * GN_NT) {
-    const int b = (int)(u / units_b);
-    const int64_t r = u - (int64_t)b * units_b;
-    const int64_t p = r / cpt;
-    const int cu = (int)(r - p * cpt);
-    const u32x4 v =
-        *reinterpret_cast<const u32x4*>(g.x + (int64_t)b * g.x_bs + p * g.C + 8 * cu);
-    const float* ab = g.ab + ((int64_t)b * g.C + 8 * cu) * 2;
-    const f32x4 q0 = *reinterpret_cast<const f32x4*>(ab);
-    const f32x4 q1 = *reinterpret_cast<const f32x4*>(ab + 4);
-    const f32x4 q2 = *reinterpret_cast<const f32x4*>(ab + 8);
-    const f32x4 q3 = *reinterpret_cast<const f32x4*>(ab + 12);
-    const float sc[8] = {q0[0], q0[2], q1[0], q1[2], q2[0], q2[2], q3[0], q3[2]};
-    const float sf[8] = {q0[1], q0[3], q1[1], q1[3], q2[1], q2[3], q3[1], q3[3]};
-    f32x8 y;
+  const int64_t units = (int64_t)g.HW * cpt;
+  const int64_t stride = (int64_t)gridDim.x * GN_NT;
+  int64_t u = (int64_t)blockIdx.x * GN_NT + threadIdx.x;
+  const int cu = (int)(u % cpt);
+  const float* ab = g.ab + ((int64_t)b * g.C + 8 * cu) * 2;
+  float sc[8], sf[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float t = fmaf(bf16_to_f32((v[e >> 1] >> (16 * (e & 1))) & 0xFFFFu), sc[e], sf[e]);
-      y[e] = g.silu ? silu_f(t) : t;
+  for (int q = 0; q < 4; ++q) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(ab + 4 * q);
+    sc[2 * q] = v[0];
+    sf[2 * q] = v[1];
+    sc[2 * q + 1] = v[2];
+    sf[2 * q + 1] = v[3];
+  }
+  const bf16_t* x = g.x + (int64_t)b * g.x_bs;
+  bf16_t* y = g.y + (int64_t)b * g.y_bs;
+  for (; u < units; u += U * stride) {
+    u32x4 v[U];
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+      const int64_t ui = u + i * stride;
+      if (ui < units) v[i] = *reinterpret_cast<const u32x4*>(x + ui * 8);
     }
-    *reinterpret_cast<bf16x8*>(g.y + (int64_t)b * g.y_bs + p * g.C + 8 * cu) = pack_bf16x8(y);
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+      const int64_t ui = u + i * stride;
+      if (ui >= units) break;
+      f32x8 r;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float t =
+            fmaf(bf16_to_f32((v[i][e >> 1] >> (16 * (e & 1))) & 0xFFFFu), sc[e], sf[e]);
+        r[e] = g.silu ? silu_f(t) : t;
+      }
+      *reinterpret_cast<bf16x8*>(y + ui * 8) = pack_bf16x8(r);
+    }
   }
 }
 
@@ -557,31 +792,61 @@ __global__ __launch_bounds__(256) void latent_image_kernel(const LatentImageArgs
 }
 
 // ------------------------------------------------------------------ host side
+// Tile shapes: 0-3 the implicit GEMM (rows x channels), 4-5 the halo conv
+// (8 x 32 pixels x channels; single-source 3x3 convs with 64-channel slices).
 struct TileCfg {
-  int wm, fn, bm, bn;
+  int bm, bn;
+  bool halo;
+  double eff;  // relative MFMA efficiency of the shape
 };
-constexpr TileCfg kCfgs[] = {{4, 4, 256, 256}, {8, 4, 512, 128}, {4, 2, 256, 128}, {8, 1, 512, 32}};
+constexpr TileCfg kCfgs[] = {{256, 256, false, 1.0}, {512, 128, false, 0.95},
+                             {256, 128, false, 0.8}, {512, 32, false, 0.5},
+                             {256, 256, true, 1.3},  {256, 128, true, 1.2}};
+constexpr int kNumCfgs = 6;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+bool halo_ok(const ConvArgs& a) {
+  return a.nsrc == 1 && a.src[0].taps == 9 && a.src[0].C % CBK == 0 && a.H > 1;
+}
+
+// Tile count of shape c for the launch.
+int64_t cfg_tiles(const ConvArgs& a, int c) {
+  const TileCfg& t = kCfgs[c];
+  if (t.halo)
+    return (int64_t)a.B * ceil_div(a.H, HT_ROWS) * ceil_div(a.W, HT_COLS) * ceil_div(a.N, t.bn);
+  return (int64_t)a.B * ceil_div((int64_t)a.H * a.W, t.bm) * ceil_div(a.N, t.bn);
+}
+
 // Tile shape: the modelled time is rounds of tiles over 256 CUs times a
-// tile's MFMA work divided by the shape's relative efficiency.
+// tile's MFMA work divided by the shape's relative efficiency. The choice
+// never changes a result: every shape of both kernels adds an output
+// element's terms in the same k-steps in the same order (for 3x3 convs over
+// 64-channel slices: slices outer, taps inner).
 int pick_cfg(const ConvArgs& a) {
-  const int64_t M = (int64_t)a.H * a.W;
-  static const double eff[] = {1.0, 0.95, 0.8, 0.5};
+  const bool halo = halo_ok(a);
   int best = 0;
   double best_t = 1e300;
-  for (int c = 0; c < 4; ++c) {
+  for (int c = 0; c < kNumCfgs; ++c) {
     const TileCfg& t = kCfgs[c];
-    const int64_t tiles = (int64_t)a.B * ceil_div(M, t.bm) * ceil_div(a.N, t.bn);
-    const double rounds = (double)ceil_div(tiles, 256);
-    const double time = rounds * t.bm * t.bn / eff[c];
+    if (t.halo && !halo) continue;
+    const double rounds = (double)ceil_div(cfg_tiles(a, c), 256);
+    const double time = rounds * t.bm * t.bn / t.eff;
     if (time < best_t * 0.999) {
       best_t = time;
       best = c;
     }
   }
   return best;
+}
+
+// DIT_CONV_TILE (tests): force tile shape c when it applies to the launch.
+int forced_cfg(const ConvArgs& a) {
+  const char* e = std::getenv("DIT_CONV_TILE");
+  if (!e || !*e) return -1;
+  const int c = std::atoi(e);
+  if (c < 0 || c >= kNumCfgs || (kCfgs[c].halo && !halo_ok(a))) return -1;
+  return c;
 }
 
 }  // namespace
@@ -615,10 +880,16 @@ hipError_t conv_launch(ConvArgs& a, hipStream_t stream) {
                         a.resid_bs % 8 == 0)) &&
           (!a.bias || a.bias_rows || reinterpret_cast<uintptr_t>(a.bias) % 16 == 0) &&
           (!a.bias2 || reinterpret_cast<uintptr_t>(a.bias2) % 16 == 0);
-  const int c = pick_cfg(a);
+  const int c = forced_cfg(a) >= 0 ? forced_cfg(a) : pick_cfg(a);
   const TileCfg& t = kCfgs[c];
   a.cfg = c;
-  a.tiles_m = (int)ceil_div(M, t.bm);
+  if (t.halo) {
+    a.tiles_x = (int)ceil_div(a.W, HT_COLS);
+    a.tiles_m = (int)ceil_div(a.H, HT_ROWS) * a.tiles_x;
+  } else {
+    a.tiles_x = 0;
+    a.tiles_m = (int)ceil_div(M, t.bm);
+  }
   a.tiles_n = (int)ceil_div(a.N, t.bn);
   const int64_t n_wg = (int64_t)a.B * a.tiles_m * a.tiles_n;
   if (n_wg > 0x7FFFFFFF) return hipErrorInvalidValue;
@@ -627,7 +898,9 @@ hipError_t conv_launch(ConvArgs& a, hipStream_t stream) {
     case 0: hipLaunchKernelGGL((conv_kernel<4, 4>), grid, dim3(CNT), 0, stream, a); break;
     case 1: hipLaunchKernelGGL((conv_kernel<8, 4>), grid, dim3(CNT), 0, stream, a); break;
     case 2: hipLaunchKernelGGL((conv_kernel<4, 2>), grid, dim3(CNT), 0, stream, a); break;
-    default: hipLaunchKernelGGL((conv_kernel<8, 1>), grid, dim3(CNT), 0, stream, a); break;
+    case 3: hipLaunchKernelGGL((conv_kernel<8, 1>), grid, dim3(CNT), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((conv3_halo_kernel<4>), grid, dim3(CNT), 0, stream, a); break;
+    default: hipLaunchKernelGGL((conv3_halo_kernel<2>), grid, dim3(CNT), 0, stream, a); break;
   }
   return hipGetLastError();
 }
@@ -642,12 +915,15 @@ hipError_t group_norm_launch(const GroupNormArgs& g, hipStream_t stream) {
                      stream, g);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(gn_finalize_kernel, dim3((unsigned)g.B), dim3(GN_NT), 0, stream, g);
+  hipLaunchKernelGGL(gn_finalize_kernel, dim3((unsigned)g.G, (unsigned)g.B), dim3(GN_NT), 0,
+                     stream, g);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t units = (int64_t)g.B * g.HW * cpt;
-  const int64_t blocks = std::min<int64_t>(ceil_div(units, GN_NT), 256 * 16);
-  hipLaunchKernelGGL(gn_apply_kernel, dim3((unsigned)blocks), dim3(GN_NT), 0, stream, g);
+  const int64_t units = (int64_t)g.HW * cpt;
+  const int64_t blocks = std::max<int64_t>(
+      1, std::min<int64_t>(ceil_div(units, GN_NT * 4), std::max<int64_t>(1, 4096 / g.B)));
+  hipLaunchKernelGGL(gn_apply_kernel, dim3((unsigned)blocks, (unsigned)g.B), dim3(GN_NT), 0,
+                     stream, g);
   return hipGetLastError();
 }
 

@@ -13,9 +13,16 @@ of minutes on a few cores) and stores the velocity:
   whose whole tensor would be 17 MB; there the whole-tensor check is the sum
   of squares per batch row.
 
+The latent decoder's workloads (oracle/vae_oracle.py, float64, one batch
+row at a time) store the image [B, H, W, 3]: whole (fp32) for the 1024x1024
+decode, every 16th pixel row (plus the last) of each batch row for the
+1920x1088 batch-4 decode (the whole tensor would be 100 MB), with the
+full-image sum of squares per batch row.
+
 Usage: python tests/golden/make_golden.py [step_1024px_s4608 ...]
-Output: tests/golden/<workload>.npz with rows (int64), v ([B, len(rows), C]),
-        and the oracle's full-tensor sum of squares and max-abs per batch row.
+Output: tests/golden/<workload>.npz with rows (int64), v ([B, len(rows), C])
+        or image ([B, len(rows), W, 3]), and the oracle's full-tensor sum of
+        squares and max-abs per batch row.
 """
 import os
 import sys
@@ -27,6 +34,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.dirname(os.path.abspath(__file__)
 sys.path.insert(0, ROOT)
 
 from oracle import dit_oracle as O  # noqa: E402
+from oracle import vae_oracle as V  # noqa: E402
 from diffusion_transformer_fwd_amd import synth  # noqa: E402
 
 # workload -> row stride of the stored velocity (1 = whole tensor, stored fp32)
@@ -36,6 +44,12 @@ WORKLOADS = {
     synth.W_STEP_1920x1088_B4.name: (synth.W_STEP_1920x1088_B4, 32),
     synth.W_STEP_848x624_3REF.name: (synth.W_STEP_848x624_3REF, 1),
     synth.W_STEP_512_REF.name: (synth.W_STEP_512_REF, 1),
+}
+
+# decoder workload -> pixel-row stride of the stored image
+VAE_WORKLOADS = {
+    synth.V_DECODE_1024.name: (synth.V_DECODE_1024, 1),
+    synth.V_DECODE_1920x1088_B4.name: (synth.V_DECODE_1920x1088_B4, 16),
 }
 
 
@@ -71,6 +85,27 @@ def run(name: str) -> None:
     print(f"wrote {out} in {time.time() - t0:.0f}s", flush=True)
 
 
+def run_vae(name: str) -> None:
+    wl, stride = VAE_WORKLOADS[name]
+    vcfg = synth.VAE_KLEIN
+    w = synth.vae_weights(vcfg, 0)
+    hp, wp = wl.grid
+    rows = sample_rows(16 * hp, stride)
+    t0 = time.time()
+    imgs, sumsq, maxabs = [], [], []
+    for b in range(wl.batch):
+        z = synth.vae_latents(vcfg, b, hp, wp)[None]
+        img = V.decode(vcfg, w, z, hp, wp)[0]
+        imgs.append(img[rows].astype(np.float32))
+        sumsq.append(float((img * img).sum()))
+        maxabs.append(float(np.abs(img).max()))
+        print(f"  {name}: batch row {b} done at {time.time() - t0:.0f}s", flush=True)
+    out = os.path.join(os.path.dirname(os.path.abspath(__file__)), f"{name}.npz")
+    np.savez(out, rows=rows, image=np.stack(imgs), sumsq=np.asarray(sumsq),
+             maxabs=np.asarray(maxabs), seconds=time.time() - t0)
+    print(f"wrote {out} in {time.time() - t0:.0f}s", flush=True)
+
+
 if __name__ == "__main__":
-    for n in (sys.argv[1:] or list(WORKLOADS)):
-        run(n)
+    for n in (sys.argv[1:] or list(WORKLOADS) + list(VAE_WORKLOADS)):
+        run_vae(n) if n in VAE_WORKLOADS else run(n)
