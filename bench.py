@@ -262,7 +262,7 @@ def time_decode(dit, synth, torch, vwl, vdw, steps=5, warmup=1):
            "ms_p95": round(float(np.percentile(per, 95)), 3),
            "tflop": round(flops / 1e12, 3), "tflops": round(flops / (med * 1e-3) / 1e12, 1),
            "frac_of_bf16_peak": round(flops / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
-    for name in ("conv", "group_norm", "softmax", "latent_image"):
+    for name in ("conv_halo", "conv", "group_norm", "softmax", "latent_image"):
         s = k[name]
         if s["launches"] == 0:
             continue
@@ -278,6 +278,17 @@ def time_decode(dit, synth, torch, vwl, vdw, steps=5, warmup=1):
             e["gbs"] = round(gbs, 1)
             e["frac_of_hbm_peak"] = round(gbs / PEAK_HBM_GBS, 4)
         res[name] = e
+    # the decoder's dominant kernel against the bf16 MFMA peak
+    h = k["conv_halo"]
+    if h["launches"] > 0:
+        per_launch = h["flops"] / h["launches"]
+        avg_s = h["total_ms"] / h["launches"] * 1e-3
+        res["roofline"] = {"bound": "mfma", "kernel": "conv3_halo_kernel",
+                           "achieved": round(per_launch / avg_s / 1e12, 1),
+                           "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                           "frac": round(per_launch / avg_s / 1e12 / PEAK_BF16_TFLOPS, 4),
+                           "per_launch_flop": per_launch, "avg_launch_us": round(avg_s * 1e6, 2),
+                           "traffic": None}
     del ws, img, z
     torch.cuda.empty_cache()
     return res

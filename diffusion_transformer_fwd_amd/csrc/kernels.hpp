@@ -249,6 +249,12 @@ struct ConvArgs {
   const float* bias2;   // [N], may be null
   const bf16_t* resid;  // [B][M][ldr] bf16, may be null; may alias out
   int64_t out_bs, resid_bs;
+  // GroupNorm folded into the input of the halo kernel (source 0 only):
+  // when gn_ab is set, source 0 is read as act(x a_c + s_c) rounded to bf16
+  // (act = SiLU when gn_silu), zero padding kept zero; gn_ab [B][C][2]
+  // holds (a_c, s_c) per sample and channel. Only the halo kernel takes it.
+  const float* gn_ab;
+  int32_t gn_silu;
   int32_t nsrc, B, H, W, N, ldo, ldr, out_f32, bias_rows;
   int32_t vec;          // 16-byte epilogue stores allowed (set by conv_launch)
   int32_t tiles_m, tiles_n, tiles_x, cfg;  // set by conv_launch
@@ -256,6 +262,8 @@ struct ConvArgs {
 // Checks the shapes the kernel assumes (returns hipErrorInvalidValue on a
 // violation), picks the tile shape and launches.
 hipError_t conv_launch(ConvArgs& a, hipStream_t stream);
+// Whether conv_launch will run a's convolution on the halo-tiled kernel.
+bool conv_uses_halo(const ConvArgs& a);
 
 // GroupNorm (+ optional SiLU), channels last, per sample over H * W pixels:
 // statistics from per-block partial sums around a per-group shift (the
@@ -270,6 +278,7 @@ struct GroupNormArgs {
   const float* beta;
   int64_t x_bs, y_bs;   // sample strides (elements)
   int32_t B, HW, C, G, ppb, nblk, silu;
+  int32_t apply;        // 0: statistics and scale / shift only (y unused)
   float eps;
 };
 // ppb / nblk: pixels per statistics block (a multiple of 256 / (C / 8)) and

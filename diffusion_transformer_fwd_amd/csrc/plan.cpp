@@ -376,7 +376,6 @@ int validate_denoise(const dit_config* cfg, const dit_model_weights* w, const vo
 namespace {
 bool pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
 constexpr int64_t kMaxSampleBytes = 0x7FFFFFFFll;  // conv offsets and the zero-read marker
-constexpr int64_t kScoreChunkBytes = 1ll << 30;    // fp32 attention scores per chunk
 }  // namespace
 
 void gn_blocks(int64_t HW, int C, int* ppb, int* nblk) {
@@ -442,8 +441,12 @@ VaeLayout vae_layout(const dit_vae_config& c, int64_t B, int64_t hp, int64_t wp)
   }
   L.ld = round_up(L.n0, 8);
   L.mq = L.n0;
-  if (L.n0 * L.ld * 4 > kScoreChunkBytes)
-    L.mq = std::max<int64_t>(256, kScoreChunkBytes / (L.ld * 4) / 256 * 256);
+  // query rows per chunk: all of them while the bf16 probabilities (the
+  // product's A operand, read with 32-bit buffer offsets) stay under 2^31
+  // bytes (every size up to 32768 latent pixels, e.g. 1920x1088); fewer
+  // rows mean fewer tiles for the P V product, which has only C columns
+  if (L.n0 * L.ld * 2 > kMaxSampleBytes)
+    L.mq = std::max<int64_t>(256, kMaxSampleBytes / (L.ld * 2) / 256 * 256);
   // DIT_VAE_ATTN_ROWS (tests): a smaller positive multiple of 256 query rows
   // per chunk, so that small images exercise the chunked path
   if (const char* e = std::getenv("DIT_VAE_ATTN_ROWS")) {

@@ -38,6 +38,13 @@
 namespace dit {
 namespace {
 
+// SiLU of the decoder's GroupNorm: v / (1 + e^-v) with the hardware
+// reciprocal (1 ulp) instead of an IEEE divide; the normalize kernel and the
+// halo conv's folded normalization both use it, so they agree bit for bit.
+__device__ __forceinline__ float gn_silu(float v) {
+  return v * __builtin_amdgcn_rcpf(1.0f + __expf(-v));
+}
+
 constexpr int CBK = 64;            // K slice
 constexpr int CNT = 512;           // 8 waves
 constexpr int ROW_U = CBK / 8;     // 16-byte units per LDS row
@@ -387,6 +394,7 @@ constexpr int HALO_W = HT_COLS + 2;
 constexpr int HALO_PIX = (HT_ROWS + 2) * HALO_W;       // 340
 constexpr int HALO_GROUPS = (HALO_PIX + 7) / 8;        // 8-pixel load groups: 43
 constexpr int HALO_U = HALO_GROUPS * 8 * ROW_U;        // LDS units per halo buffer
+constexpr int AB_U = 64;                               // GroupNorm scale / shift of a slice
 
 template <int FN>
 __global__ __launch_bounds__(CNT, 1) void conv3_halo_kernel(const ConvArgs a) {
@@ -395,7 +403,9 @@ __global__ __launch_bounds__(CNT, 1) void conv3_halo_kernel(const ConvArgs a) {
   constexpr int W_U = BN * ROW_U;
   constexpr int HG_PER = (HALO_GROUPS + 3) / 4;  // halo groups per loader wave (at most)
   constexpr int WG_PER = BN / 8 / 4;             // weight-row groups per loader wave
-  __shared__ u32x4 lds[2 * HALO_U + 2 * W_U];    // halo 0 | halo 1 | W 0 | W 1
+  // halo 0 | halo 1 | W 0 | W 1 | GroupNorm (a, s) 0 | 1
+  __shared__ u32x4 lds[2 * HALO_U + 2 * W_U + 2 * AB_U];
+  constexpr int AB0 = 2 * HALO_U + 2 * W_U;
   static_assert(WM * 32 * BN * 4 <= (2 * HALO_U + 2 * W_U) * 16, "epilogue stage fits");
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -453,6 +463,54 @@ __global__ __launch_bounds__(CNT, 1) void conv3_halo_kernel(const ConvArgs a) {
                                                0, 0);
     }
   };
+  // GroupNorm folded into the input: the slice's 64 (a_c, s_c) pairs go to
+  // LDS with the halo (one load instruction, lanes 32-63 read zeros), and
+  // the landed halo is transformed in place once, before its first tap.
+  const bool gn = a.gn_ab != nullptr;
+  const __amdgpu_buffer_rsrc_t abr =
+      make_rsrc(gn ? a.gn_ab + (int64_t)b * C * 2 : a.gn_ab, gn ? (uint32_t)(C * 2 * 4) : 0u);
+  auto load_ab = [&](int cs, int buf) {
+    if (!gn || wave != 4) return;
+    const uint32_t off = lane < 32 ? (uint32_t)((cs * CBK * 2 + lane * 4) * 4) : OOB;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(abr, (lds_ptr_t)(lds + AB0 + buf * AB_U), 16, off, 0,
+                                             0, 0);
+  };
+  // act(x a_c + s_c) of the in-image halo pixels of buffer buf, in place
+  // (the formula of the normalize kernel, so either path gives the same
+  // bits); out-of-image pixels stay zero. Part `part` of XF_PARTS: 16-byte
+  // chunks [part XF_CH, (part + 1) XF_CH), one per thread.
+  constexpr int XF_PARTS = 8;
+  constexpr int XF_CH = (HALO_PIX * 8 + XF_PARTS - 1) / XF_PARTS;  // 340 chunks
+  static_assert(XF_CH <= CNT, "one chunk per thread and part");
+  auto transform = [&](int buf, int part) {
+    u32x4* const hb = lds + buf * HALO_U;
+    const float* const abl = reinterpret_cast<const float*>(lds + AB0 + buf * AB_U);
+    {
+      if (tid >= XF_CH) return;
+      const int u = part * XF_CH + tid;
+      const int p = u >> 3;
+      if (p >= HALO_PIX) return;
+      const int hy = p / HALO_W, hx = p - hy * HALO_W;
+      const int Y = y0 - 1 + hy, X = x0 - 1 + hx;
+      if ((unsigned)Y >= (unsigned)H || (unsigned)X >= (unsigned)W) return;
+      const int lc = (u & 7) ^ swz(p);
+      const u32x4 v = hb[u];
+      const f32x4 q0 = *reinterpret_cast<const f32x4*>(abl + lc * 16);
+      const f32x4 q1 = *reinterpret_cast<const f32x4*>(abl + lc * 16 + 4);
+      const f32x4 q2 = *reinterpret_cast<const f32x4*>(abl + lc * 16 + 8);
+      const f32x4 q3 = *reinterpret_cast<const f32x4*>(abl + lc * 16 + 12);
+      const float sc[8] = {q0[0], q0[2], q1[0], q1[2], q2[0], q2[2], q3[0], q3[2]};
+      const float sf[8] = {q0[1], q0[3], q1[1], q1[3], q2[1], q2[3], q3[1], q3[3]};
+      f32x8 r;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float t =
+            fmaf(bf16_to_f32((v[e >> 1] >> (16 * (e & 1))) & 0xFFFFu), sc[e], sf[e]);
+        r[e] = a.gn_silu ? gn_silu(t) : t;
+      }
+      hb[u] = __builtin_bit_cast(u32x4, pack_bf16x8(r));
+    }
+  };
   auto load_w = [&](int cs, int tap, int buf) {
     if (!loader) return;
     u32x4* const dst = lds + 2 * HALO_U + buf * W_U;
@@ -502,20 +560,42 @@ __global__ __launch_bounds__(CNT, 1) void conv3_halo_kernel(const ConvArgs a) {
             __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[buf][j], af[buf][i], acc[i][j], 0, 0, 0);
   };
 
+  // Schedule: the weights of step j are loaded during step j - 1; the halo
+  // (and GroupNorm pairs) of slice c + 1 during step 9c, the slice's first
+  // tap, and with GroupNorm folded in, transformed one eighth at a time
+  // during its taps 1-8, between their MFMAs. Every step ends with all
+  // loads landed and one barrier.
+  const int CS = C / CBK;
   load_halo(0, 0);
+  load_ab(0, 0);
   load_w(0, 0, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (nsteps > 1) load_w(0, 1, 1);
+  if (CS > 1) {
+    load_halo(1, 1);
+    load_ab(1, 1);
+  }
+  if (gn) {
+#pragma unroll 1
+    for (int part = 0; part < XF_PARTS; ++part) transform(0, part);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
   fload(0, 0, 0, 0, 0);
   int cs = 0, tap = 0;  // of the current step
   for (int step = 0; step < nsteps; ++step) {
+    const bool xform = gn && tap >= 1 && cs + 1 < CS;
 #pragma unroll
     for (int s = 0; s < CBK / 16 - 1; ++s) {
       fload(cs, tap, step, s + 1, (s + 1) & 1);
       __builtin_amdgcn_sched_barrier(0);
       mfmas(s & 1);
       __builtin_amdgcn_sched_barrier(0);
+      if (s == 0 && xform) {
+        transform((cs + 1) & 1, tap - 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     // every wave is done with this step's buffers; the next step's landed
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
@@ -532,7 +612,12 @@ __global__ __launch_bounds__(CNT, 1) void conv3_halo_kernel(const ConvArgs a) {
         ++cs2;
       }
       load_w(cs2, tap2, step & 1);
-      if (tap2 == 0) load_halo(cs2, cs2 & 1);
+    }
+    // the next step starts slice cs1: the halo of slice cs1 + 1 goes into
+    // the buffer slice cs1 - 1 used
+    if (tap1 == 0 && cs1 + 1 < CS) {
+      load_halo(cs1 + 1, (cs1 + 1) & 1);
+      load_ab(cs1 + 1, (cs1 + 1) & 1);
     }
     if (step + 1 < nsteps) fload(cs1, tap1, step + 1, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
@@ -711,7 +796,7 @@ __global__ __launch_bounds__(GN_NT) void gn_apply_kernel(const GroupNormArgs g) 
       for (int e = 0; e < 8; ++e) {
         const float t =
             fmaf(bf16_to_f32((v[i][e >> 1] >> (16 * (e & 1))) & 0xFFFFu), sc[e], sf[e]);
-        r[e] = g.silu ? silu_f(t) : t;
+        r[e] = g.silu ? gn_silu(t) : t;
       }
       *reinterpret_cast<bf16x8*>(y + ui * 8) = pack_bf16x8(r);
     }
@@ -799,8 +884,12 @@ struct TileCfg {
   bool halo;
   double eff;  // relative MFMA efficiency of the shape
 };
-constexpr TileCfg kCfgs[] = {{256, 256, false, 1.0}, {512, 128, false, 0.95},
-                             {256, 128, false, 0.8}, {512, 32, false, 0.5},
+// The implicit GEMM's loop is paced by the L2 -> LDS stream of (rows +
+// columns) x 128 bytes per K slice, so its efficiency follows
+// rows x columns / (rows + columns): 1, 0.85, 0.7, 0.25 of the 256 x 256
+// tile; the halo shapes are MFMA-bound (measured 1.3 and 1.2).
+constexpr TileCfg kCfgs[] = {{256, 256, false, 1.0}, {512, 128, false, 0.85},
+                             {256, 128, false, 0.7}, {512, 32, false, 0.25},
                              {256, 256, true, 1.3},  {256, 128, true, 1.2}};
 constexpr int kNumCfgs = 6;
 
@@ -818,19 +907,23 @@ int64_t cfg_tiles(const ConvArgs& a, int c) {
   return (int64_t)a.B * ceil_div((int64_t)a.H * a.W, t.bm) * ceil_div(a.N, t.bn);
 }
 
-// Tile shape: the modelled time is rounds of tiles over 256 CUs times a
-// tile's MFMA work divided by the shape's relative efficiency. The choice
+// Tile shape: the modelled time is the rounds of tiles over 256 CUs (at
+// least one; a partial last round counts by its fraction, since its tiles
+// run faster with fewer neighbours) times a tile's MFMA work divided by the
+// shape's relative efficiency (measured on the decoder's layers: the halo
+// shapes reach 1.1-1.2 PFLOP/s at 256 and 512 channels). The choice
 // never changes a result: every shape of both kernels adds an output
 // element's terms in the same k-steps in the same order (for 3x3 convs over
 // 64-channel slices: slices outer, taps inner).
 int pick_cfg(const ConvArgs& a) {
+  if (a.N <= 32) return 3;  // narrow outputs (conv_out): wider tiles only waste columns
   const bool halo = halo_ok(a);
   int best = 0;
   double best_t = 1e300;
   for (int c = 0; c < kNumCfgs; ++c) {
     const TileCfg& t = kCfgs[c];
     if (t.halo && !halo) continue;
-    const double rounds = (double)ceil_div(cfg_tiles(a, c), 256);
+    const double rounds = std::max(1.0, (double)cfg_tiles(a, c) / 256.0);
     const double time = rounds * t.bm * t.bn / t.eff;
     if (time < best_t * 0.999) {
       best_t = time;
@@ -850,6 +943,12 @@ int forced_cfg(const ConvArgs& a) {
 }
 
 }  // namespace
+
+bool conv_uses_halo(const ConvArgs& a) {
+  if (a.N <= 0 || a.nsrc < 1) return false;
+  const int f = forced_cfg(a);
+  return kCfgs[f >= 0 ? f : pick_cfg(a)].halo;
+}
 
 hipError_t conv_launch(ConvArgs& a, hipStream_t stream) {
   const int64_t M = (int64_t)a.H * a.W;
@@ -882,6 +981,7 @@ hipError_t conv_launch(ConvArgs& a, hipStream_t stream) {
           (!a.bias2 || reinterpret_cast<uintptr_t>(a.bias2) % 16 == 0);
   const int c = forced_cfg(a) >= 0 ? forced_cfg(a) : pick_cfg(a);
   const TileCfg& t = kCfgs[c];
+  if (a.gn_ab && !t.halo) return hipErrorInvalidValue;  // only the halo kernel folds GroupNorm
   a.cfg = c;
   if (t.halo) {
     a.tiles_x = (int)ceil_div(a.W, HT_COLS);
@@ -919,6 +1019,7 @@ hipError_t group_norm_launch(const GroupNormArgs& g, hipStream_t stream) {
                      stream, g);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (!g.apply) return hipSuccess;
   const int64_t units = (int64_t)g.HW * cpt;
   const int64_t blocks = std::max<int64_t>(
       1, std::min<int64_t>(ceil_div(units, GN_NT * 4), std::max<int64_t>(1, 4096 / g.B)));

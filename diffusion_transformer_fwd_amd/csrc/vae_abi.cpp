@@ -47,16 +47,23 @@ dit::ConvSource image_src(const void* x, int C, int64_t pix_in, const void* w, i
   return s;
 }
 
-int run_conv(dit::ConvArgs& a, double flops, double bytes, hipStream_t st) {
-  VAE_TRY(timed(DIT_K_CONV, flops, bytes, st, [&] { return dit::conv_launch(a, st); }));
+struct Conv {
+  dit::ConvArgs a{};
+  double flops = 0.0, bytes = 0.0;
+};
+
+int run_conv(Conv& c, hipStream_t st) {
+  const int kind = dit::conv_uses_halo(c.a) ? DIT_K_CONV_HALO : DIT_K_CONV;
+  VAE_TRY(timed(kind, c.flops, c.bytes, st, [&] { return dit::conv_launch(c.a, st); }));
   return DIT_OK;
 }
 
 // out[B][H][W][N] = conv(x) (+ 1x1 conv of xs) + bias (+ bias2) (+ resid).
-int conv_image(const void* x, int C, int taps, int up, const void* w, const float* bias,
-               const void* xs, int Cs, const void* ws, const float* bias2, const void* resid,
-               int B, int H, int W, int N, void* out, int out_f32, hipStream_t st) {
-  dit::ConvArgs a{};
+Conv image_conv(const void* x, int C, int taps, int up, const void* w, const float* bias,
+                const void* xs, int Cs, const void* ws, const float* bias2, const void* resid,
+                int B, int H, int W, int N, void* out, int out_f32) {
+  Conv c;
+  dit::ConvArgs& a = c.a;
   const int64_t pix = (int64_t)H * W, pix_in = up ? pix / 4 : pix;
   a.src[0] = image_src(x, C, pix_in, w, taps, N, up);
   a.nsrc = 1;
@@ -78,12 +85,18 @@ int conv_image(const void* x, int C, int taps, int up, const void* w, const floa
   a.ldr = N;
   a.out_f32 = out_f32;
   const double K = (double)taps * C + (xs ? Cs : 0);
-  const double flops = 2.0 * B * pix * N * K;
-  const double bytes =
-      (double)B * (pix_in * C * 2.0 + (xs ? pix * Cs * 2.0 : 0.0) +
-                   pix * N * (out_f32 ? 4.0 : 2.0) + (resid ? pix * N * 2.0 : 0.0)) +
-      N * K * 2.0;
-  return run_conv(a, flops, bytes, st);
+  c.flops = 2.0 * B * pix * N * K;
+  c.bytes = (double)B * (pix_in * C * 2.0 + (xs ? pix * Cs * 2.0 : 0.0) +
+                         pix * N * (out_f32 ? 4.0 : 2.0) + (resid ? pix * N * 2.0 : 0.0)) +
+            N * K * 2.0;
+  return c;
+}
+
+int conv_image(const void* x, int C, int taps, int up, const void* w, const float* bias,
+               const void* xs, int Cs, const void* ws, const float* bias2, const void* resid,
+               int B, int H, int W, int N, void* out, int out_f32, hipStream_t st) {
+  Conv c = image_conv(x, C, taps, up, w, bias, xs, Cs, ws, bias2, resid, B, H, W, N, out, out_f32);
+  return run_conv(c, st);
 }
 
 // out[b][m][n] = sum_{k < K} A[b][m][k] W[b][n][k] (+ bias[n], or bias[m]
@@ -92,7 +105,8 @@ int conv_image(const void* x, int C, int taps, int up, const void* w, const floa
 int gemm_rows(const void* A, int64_t lda, int64_t a_bs, int64_t M, const void* Wt, int64_t ldw,
               int64_t w_bs, int64_t w_rows, int64_t N, int64_t K, int B, void* out, int64_t ldo,
               int64_t out_bs, int out_f32, const float* bias, int bias_rows, hipStream_t st) {
-  dit::ConvArgs a{};
+  Conv c;
+  dit::ConvArgs& a = c.a;
   dit::ConvSource& s = a.src[0];
   s.x = bf(A);
   s.w = bf(Wt);
@@ -117,13 +131,15 @@ int gemm_rows(const void* A, int64_t lda, int64_t a_bs, int64_t M, const void* W
   a.ldo = (int32_t)ldo;
   a.ldr = (int32_t)ldo;
   a.out_f32 = out_f32;
-  const double flops = 2.0 * B * M * N * K;
-  const double bytes = (double)B * (M * K * 2.0 + (w_bs ? N * K * 2.0 : 0.0) +
-                                    M * N * (out_f32 ? 4.0 : 2.0)) +
-                       (w_bs ? 0.0 : N * K * 2.0);
-  return run_conv(a, flops, bytes, st);
+  c.flops = 2.0 * B * M * N * K;
+  c.bytes = (double)B * (M * K * 2.0 + (w_bs ? N * K * 2.0 : 0.0) +
+                         M * N * (out_f32 ? 4.0 : 2.0)) +
+            (w_bs ? 0.0 : N * K * 2.0);
+  return run_conv(c, st);
 }
 
+// y = act(GroupNorm(x)); with y == nullptr only the statistics and the
+// per-channel scale / shift (ab) are computed, for a conv that folds them in.
 int group_norm(const void* x, void* y, const float* gamma, const float* beta, int B, int64_t HW,
                int C, int G, float eps, int silu, float* part, float* ab, hipStream_t st) {
   dit::GroupNormArgs a{};
@@ -140,10 +156,11 @@ int group_norm(const void* x, void* y, const float* gamma, const float* beta, in
   a.C = C;
   a.G = G;
   a.silu = silu;
+  a.apply = y != nullptr;
   a.eps = eps;
   gn_blocks(HW, C, &a.ppb, &a.nblk);
   // statistics read x once, the normalization reads it again and writes y
-  const double bytes = (double)B * HW * C * 2.0 * 3.0;
+  const double bytes = (double)B * HW * C * 2.0 * (a.apply ? 3.0 : 1.0);
   VAE_TRY(timed(DIT_K_GROUPNORM, 0.0, bytes, st, [&] { return dit::group_norm_launch(a, st); }));
   return DIT_OK;
 }
@@ -173,19 +190,39 @@ int decode(const dit_vae_config& c, const dit_vae_weights& w, const float* z, in
   DIT_CHECK(conv_image(lat, Z, 9, 0, w.conv_in_w, w.conv_in_b, nullptr, 0, nullptr, nullptr,
                        nullptr, B, H, W, top, P, 0, st));
 
+  // conv c over SiLU(GN(x)) (c's source 0 is x): on the halo kernel the
+  // normalization is folded into the conv's input, otherwise it is written
+  // to T first; both give the same bits
+  auto norm_conv = [&](Conv& c, const void* x, int C, const float* gamma, const float* beta,
+                       int64_t pix) -> int {
+    c.a.src[0].x = bf(x);
+    c.a.gn_ab = ab;
+    c.a.gn_silu = 1;
+    if (dit::conv_uses_halo(c.a)) {
+      DIT_CHECK(group_norm(x, nullptr, gamma, beta, B, pix, C, G, eps, 1, part, ab, st));
+      return run_conv(c, st);
+    }
+    c.a.src[0].x = bf(T);
+    c.a.gn_ab = nullptr;
+    DIT_CHECK(group_norm(x, T, gamma, beta, B, pix, C, G, eps, 1, part, ab, st));
+    return run_conv(c, st);
+  };
+
   // x (in P) <- s(x) + conv2(SiLU(GN2(conv1(SiLU(GN1(x))))))
   auto resnet = [&](const dit_vae_resnet& r, int ci, int co) -> int {
     const int64_t pix = (int64_t)H * W;
-    DIT_CHECK(group_norm(P, T, r.gn1_gamma, r.gn1_beta, B, pix, ci, G, eps, 1, part, ab, st));
-    DIT_CHECK(conv_image(T, ci, 9, 0, r.conv1_w, r.conv1_b, nullptr, 0, nullptr, nullptr,
-                         nullptr, B, H, W, co, Hh, 0, st));
-    DIT_CHECK(group_norm(Hh, T, r.gn2_gamma, r.gn2_beta, B, pix, co, G, eps, 1, part, ab, st));
-    if (ci == co)  // identity shortcut: added in the epilogue, in place
-      return conv_image(T, co, 9, 0, r.conv2_w, r.conv2_b, nullptr, 0, nullptr, nullptr, P, B, H,
-                        W, co, P, 0, st);
+    Conv c1 = image_conv(P, ci, 9, 0, r.conv1_w, r.conv1_b, nullptr, 0, nullptr, nullptr, nullptr,
+                         B, H, W, co, Hh, 0);
+    DIT_CHECK(norm_conv(c1, P, ci, r.gn1_gamma, r.gn1_beta, pix));
+    if (ci == co) {  // identity shortcut: added in the epilogue, in place
+      Conv c2 = image_conv(Hh, co, 9, 0, r.conv2_w, r.conv2_b, nullptr, 0, nullptr, nullptr, P, B,
+                           H, W, co, P, 0);
+      return norm_conv(c2, Hh, co, r.gn2_gamma, r.gn2_beta, pix);
+    }
     // 1x1 shortcut: a second K range of the same launch
-    DIT_CHECK(conv_image(T, co, 9, 0, r.conv2_w, r.conv2_b, P, ci, r.short_w, r.short_b,
-                         nullptr, B, H, W, co, Q, 0, st));
+    Conv c2 = image_conv(Hh, co, 9, 0, r.conv2_w, r.conv2_b, P, ci, r.short_w, r.short_b, nullptr,
+                         B, H, W, co, Q, 0);
+    DIT_CHECK(norm_conv(c2, Hh, co, r.gn2_gamma, r.gn2_beta, pix));
     std::swap(P, Q);
     return DIT_OK;
   };
@@ -238,10 +275,9 @@ int decode(const dit_vae_config& c, const dit_vae_weights& w, const float* z, in
     }
   }
   const int c0 = vae_level_channels(c, 3);
-  DIT_CHECK(group_norm(P, T, w.norm_out_gamma, w.norm_out_beta, B, (int64_t)H * W, c0, G, eps, 1,
-                       part, ab, st));
-  return conv_image(T, c0, 9, 0, w.conv_out_w, w.conv_out_b, nullptr, 0, nullptr, nullptr,
-                    nullptr, B, H, W, DIT_VAE_OUT_CHANNELS, image, 1, st);
+  Conv co = image_conv(P, c0, 9, 0, w.conv_out_w, w.conv_out_b, nullptr, 0, nullptr, nullptr,
+                       nullptr, B, H, W, DIT_VAE_OUT_CHANNELS, image, 1);
+  return norm_conv(co, P, c0, w.norm_out_gamma, w.norm_out_beta, (int64_t)H * W);
 }
 
 }  // namespace

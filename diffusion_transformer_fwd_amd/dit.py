@@ -32,10 +32,10 @@ VAE_EXPORTS = ("dit_vae_config_check", "dit_vae_config_default", "dit_vae_worksp
                "dit_vae_decode_forward", "dit_vae_conv_forward", "dit_vae_group_norm_ws_bytes",
                "dit_vae_group_norm_forward")
 (K_GEMM, K_ATTENTION, K_MODNORM, K_QKV_PAD, K_GEMV, K_ROPE_TABLES, K_TIME, K_SPLIT_SUM, K_LATENT,
- K_ATTN_GEMM, K_CONV, K_GROUPNORM, K_SOFTMAX, K_LATENT_IMAGE, K_COUNT) = range(15)
+ K_ATTN_GEMM, K_CONV, K_GROUPNORM, K_SOFTMAX, K_LATENT_IMAGE, K_CONV_HALO, K_COUNT) = range(16)
 KERNEL_NAMES = ("gemm", "attention", "modnorm", "qkv_pad", "gemv", "rope_tables", "time_features",
                 "split_sum", "latent", "attn_gemm", "conv", "group_norm", "softmax",
-                "latent_image")
+                "latent_image", "conv_halo")
 VAE_MAX_LAYERS = 4
 MAX_STEPS = 64
 

@@ -292,8 +292,9 @@ enum { DIT_K_GEMM = 0, DIT_K_ATTENTION = 1, DIT_K_MODNORM = 2, DIT_K_QKV_PAD = 3
        DIT_K_GEMV = 4, DIT_K_ROPE_TABLES = 5, DIT_K_TIME = 6, DIT_K_SPLIT_SUM = 7,
        DIT_K_LATENT = 8, DIT_K_ATTN_GEMM = 9 /* attention fused with GEMM tiles */,
        /* latent decoder (dit_vae.h) */
-       DIT_K_CONV = 10, DIT_K_GROUPNORM = 11, DIT_K_SOFTMAX = 12, DIT_K_LATENT_IMAGE = 13,
-       DIT_K_COUNT = 14 };
+       DIT_K_CONV = 10 /* implicit-GEMM conv and the attention products */,
+       DIT_K_GROUPNORM = 11, DIT_K_SOFTMAX = 12, DIT_K_LATENT_IMAGE = 13,
+       DIT_K_CONV_HALO = 14 /* halo-tiled 3x3 conv */, DIT_K_COUNT = 15 };
 
 typedef struct dit_kernel_stats {
   int32_t kind;     /* DIT_K_* */

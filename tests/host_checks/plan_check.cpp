@@ -5,6 +5,7 @@
 // checks accept, position ids, the K-split rule and the GEMM tile map. Exits
 // non-zero on the first failed expectation; prints one "layout" line per
 // workspace query so the caller can compare them with the built library.
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
@@ -295,6 +296,167 @@ static void split_and_tile_checks() {
   }
 }
 
+// ---------------------------------------------------------------- decoder
+static dit_vae_config vae_cfg(int ci) {
+  dit_vae_config c{};
+  dit_vae_config_default(&c);
+  if (ci == 1) {  // small widths, two layers
+    const int w[4] = {32, 64, 64, 128};
+    for (int i = 0; i < 4; ++i) c.block_channels[i] = w[i];
+    c.layers = 2;
+  } else if (ci == 2) {  // the widest the check accepts, four layers
+    const int w[4] = {256, 512, 1024, 2048};
+    for (int i = 0; i < 4; ++i) c.block_channels[i] = w[i];
+    c.layers = 4;
+  }
+  return c;
+}
+
+static void fill_resnet(dit_vae_resnet& r, uintptr_t& k, bool shortcut) {
+  const void** f[] = {(const void**)&r.gn1_gamma, (const void**)&r.gn1_beta, &r.conv1_w,
+                      (const void**)&r.conv1_b, (const void**)&r.gn2_gamma,
+                      (const void**)&r.gn2_beta, &r.conv2_w, (const void**)&r.conv2_b};
+  for (auto p : f) *p = fake(k++);
+  r.short_w = shortcut ? fake(k++) : nullptr;
+  r.short_b = shortcut ? ffake(k++) : nullptr;
+}
+
+static dit_vae_weights vae_weights(const dit_vae_config& c) {
+  dit_vae_weights w{};
+  uintptr_t k = 1;
+  w.lat_scale = ffake(k++);
+  w.lat_shift = ffake(k++);
+  w.conv_in_w = fake(k++);
+  w.conv_in_b = ffake(k++);
+  fill_resnet(w.mid[0], k, false);
+  fill_resnet(w.mid[1], k, false);
+  w.attn_gn_gamma = ffake(k++);
+  w.attn_gn_beta = ffake(k++);
+  for (int i = 0; i < 4; ++i) {
+    w.attn_w[i] = fake(k++);
+    w.attn_b[i] = ffake(k++);
+  }
+  for (int l = 0; l < 4; ++l)
+    for (int r = 0; r < c.layers; ++r)
+      fill_resnet(w.up[l][r], k, vae_resnet_in(c, l, r) != vae_level_channels(c, l));
+  for (int l = 0; l < 3; ++l) {
+    w.upconv_w[l] = fake(k++);
+    w.upconv_b[l] = ffake(k++);
+  }
+  w.norm_out_gamma = ffake(k++);
+  w.norm_out_beta = ffake(k++);
+  w.conv_out_w = fake(k++);
+  w.conv_out_b = ffake(k++);
+  return w;
+}
+
+static void vae_checks() {
+  // configuration rules
+  dit_vae_config c = vae_cfg(0);
+  EXPECT(check_vae_config(&c) == DIT_OK);
+  EXPECT(check_vae_config(nullptr) == DIT_E_NULL);
+  c.block_channels[2] = 384;
+  EXPECT(check_vae_config(&c) == DIT_E_UNSUPPORTED);
+  c = vae_cfg(0);
+  c.groups = 48;
+  EXPECT(check_vae_config(&c) == DIT_E_UNSUPPORTED);
+  c = vae_cfg(0);
+  c.eps = NAN;
+  EXPECT(check_vae_config(&c) == DIT_E_VALUE);
+  c = vae_cfg(0);
+  c.layers = 5;
+  EXPECT(check_vae_config(&c) == DIT_E_UNSUPPORTED);
+
+  // GroupNorm blocks cover the pixels exactly once
+  for (int C : {8, 32, 128, 512, 2048})
+    for (int64_t HW : {1ll, 77ll, 4096ll, 16384ll, 1048576ll, 8355840ll}) {
+      int ppb, nblk;
+      gn_blocks(HW, C, &ppb, &nblk);
+      EXPECT(ppb % (256 / (C / 8)) == 0 && ppb > 0);
+      EXPECT((int64_t)nblk * ppb >= HW && (int64_t)(nblk - 1) * ppb < HW);
+    }
+
+  // layouts: regions disjoint and aligned; one line per query
+  const int grids[][2] = {{1, 1}, {2, 3}, {3, 5}, {32, 32}, {64, 64}, {68, 120}, {39, 53}};
+  for (int ci = 0; ci < 3; ++ci) {
+    const dit_vae_config vc = vae_cfg(ci);
+    int cmax = 0;
+    for (int i = 0; i < 4; ++i) cmax = std::max(cmax, vc.block_channels[i]);
+    for (int B : {1, 2, 4, 64})
+      for (const auto& g : grids) {
+        const VaeLayout L = vae_layout(vc, B, g[0], g[1]);
+        regions({{L.p, (size_t)(B * L.act * 2)}, {L.q, (size_t)(B * L.act * 2)},
+                 {L.t, (size_t)(B * L.act * 2)}, {L.h, (size_t)(B * L.act_h * 2)},
+                 {L.lat, (size_t)(B * L.n0 * vc.z_channels * 2)},
+                 {L.part, (size_t)(B * L.gn_nblk * vc.groups * 2 * 4)},
+                 {L.ab, (size_t)(B * cmax * 2 * 4)},
+                 {L.s, (size_t)(L.mq * L.ld * 4)}, {L.pm, (size_t)(L.mq * L.ld * 2)},
+                 {L.vt, (size_t)(B * vc.block_channels[3] * L.ld * 2)}},
+                L.total);
+        EXPECT(L.ld % 8 == 0 && L.ld >= L.n0 && L.mq >= 1 && L.mq <= L.n0);
+        EXPECT(L.mq == L.n0 || L.mq % 256 == 0);
+        EXPECT(L.mq * L.ld * 2 <= 0x7FFFFFFFll || L.mq == 256);
+        std::printf("vae_layout %d %d %d %d %zu\n", ci, B, g[0], g[1], L.total);
+      }
+  }
+
+  // decode validation: each error before any launch
+  const dit_vae_config vc = vae_cfg(0);
+  dit_vae_weights w = vae_weights(vc);
+  const float* z = ffake(9000);
+  float* img = static_cast<float*>(fake(9001));
+  void* ws = fake(9002);
+  const size_t need = vae_layout(vc, 1, 4, 4).total;
+  EXPECT(validate_vae_decode(&vc, &w, z, 1, 4, 4, img, ws, need) == DIT_OK);
+  EXPECT(validate_vae_decode(nullptr, &w, z, 1, 4, 4, img, ws, need) == DIT_E_NULL);
+  EXPECT(validate_vae_decode(&vc, nullptr, z, 1, 4, 4, img, ws, need) == DIT_E_NULL);
+  EXPECT(validate_vae_decode(&vc, &w, nullptr, 1, 4, 4, img, ws, need) == DIT_E_NULL);
+  EXPECT(validate_vae_decode(&vc, &w, z, 0, 4, 4, img, ws, need) == DIT_E_SHAPE);
+  EXPECT(validate_vae_decode(&vc, &w, z, 65, 4, 4, img, ws, need) == DIT_E_SHAPE);
+  EXPECT(validate_vae_decode(&vc, &w, z, 1, 0, 4, img, ws, need) == DIT_E_SHAPE);
+  EXPECT(validate_vae_decode(&vc, &w, z, 1, 4, 3000, img, ws, need) == DIT_E_SHAPE);
+  EXPECT(validate_vae_decode(&vc, &w, z, 1, 200, 200, img, ws, need) == DIT_E_UNSUPPORTED);
+  EXPECT(validate_vae_decode(&vc, &w, z, 1, 4, 4, img, ws, need - 1) == DIT_E_WORKSPACE);
+  EXPECT(validate_vae_decode(&vc, &w, z, 1, 4, 4, img, fake(9003) , need) == DIT_OK);
+  EXPECT(validate_vae_decode(&vc, &w, ffake(9000) + 1, 1, 4, 4, img, ws, need) == DIT_E_SHAPE);
+  dit_vae_weights w2 = w;
+  w2.up[2][1].conv2_w = nullptr;
+  EXPECT(validate_vae_decode(&vc, &w2, z, 1, 4, 4, img, ws, need) == DIT_E_NULL);
+  w2 = w;
+  w2.up[1][0].short_w = fake(9100);  // 512 -> 512 keeps its width
+  EXPECT(validate_vae_decode(&vc, &w2, z, 1, 4, 4, img, ws, need) == DIT_E_NULL);
+  w2 = w;
+  w2.up[2][0].short_b = nullptr;  // 512 -> 256 needs its shortcut
+  EXPECT(validate_vae_decode(&vc, &w2, z, 1, 4, 4, img, ws, need) == DIT_E_NULL);
+  w2 = w;
+  w2.attn_b[3] = nullptr;
+  EXPECT(validate_vae_decode(&vc, &w2, z, 1, 4, 4, img, ws, need) == DIT_E_NULL);
+
+  // the building blocks
+  const void* x = fake(9200);
+  EXPECT(validate_vae_conv(x, 64, 3, 0, x, ffake(1), nullptr, 0, nullptr, nullptr, nullptr, 1, 8, 8,
+                           64, fake(9201)) == DIT_OK);
+  EXPECT(validate_vae_conv(x, 60, 3, 0, x, ffake(1), nullptr, 0, nullptr, nullptr, nullptr, 1, 8, 8,
+                           64, fake(9201)) == DIT_E_SHAPE);
+  EXPECT(validate_vae_conv(x, 64, 3, 1, x, ffake(1), nullptr, 0, nullptr, nullptr, nullptr, 1, 7, 8,
+                           64, fake(9201)) == DIT_E_SHAPE);
+  EXPECT(validate_vae_conv(x, 64, 3, 0, x, ffake(1), x, 0, x, nullptr, nullptr, 1, 8, 8, 64,
+                           fake(9201)) == DIT_E_SHAPE);
+  EXPECT(validate_vae_conv(x, 64, 3, 0, x, ffake(1), x, 64, nullptr, nullptr, nullptr, 1, 8, 8, 64,
+                           fake(9201)) == DIT_E_NULL);
+  EXPECT(validate_vae_conv(x, 512, 3, 0, x, ffake(1), nullptr, 0, nullptr, nullptr, nullptr, 1,
+                           32000, 32000, 64, fake(9201)) == DIT_E_UNSUPPORTED);
+  const size_t gws = vae_group_norm_ws(2, 1000, 128, 32);
+  EXPECT(validate_vae_group_norm(x, fake(9300), ffake(1), ffake(2), 2, 1000, 128, 32, 1e-6f, ws,
+                                 gws) == DIT_OK);
+  EXPECT(validate_vae_group_norm(x, x, ffake(1), ffake(2), 2, 1000, 128, 32, 1e-6f, ws, gws) ==
+         DIT_E_VALUE);
+  EXPECT(validate_vae_group_norm(x, fake(9300), ffake(1), ffake(2), 2, 1000, 96, 32, 1e-6f, ws,
+                                 gws) == DIT_E_UNSUPPORTED);
+  EXPECT(validate_vae_group_norm(x, fake(9300), ffake(1), ffake(2), 2, 1000, 128, 32, 1e-6f, ws,
+                                 gws - 1) == DIT_E_WORKSPACE);
+}
+
 int main() {
   config_checks();
   layout_checks();
@@ -302,6 +464,7 @@ int main() {
   validation_checks();
   position_checks();
   split_and_tile_checks();
+  vae_checks();
   std::printf(g_fail ? "plan_check: FAILED\n" : "plan_check: ok\n");
   return g_fail;
 }

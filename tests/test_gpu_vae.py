@@ -244,6 +244,21 @@ def test_decode_batch_rows_bitwise_independent():
         assert torch.equal(one[0], both[b]), f"batch row {b} differs when decoded alone"
 
 
+def test_decode_tile_plan_and_folded_group_norm_bitwise():
+    """The decode with every conv on the implicit GEMM's 256 x 256 tiles and
+    every GroupNorm written out by its own pass equals the planned decode
+    (halo convs with the GroupNorm folded into their input), bit for bit."""
+    vcfg = synth.VAE_KLEIN
+    _, dev = vae_weights(vcfg)
+    hp, wp = 5, 7
+    z = dit.to_f32_device(np.stack([synth.vae_latents(vcfg, b, hp, wp) for b in range(2)]))
+    planned = dit.vae_decode(vcfg, dev, z, hp, wp)
+    with conv_tile(0):
+        plain = dit.vae_decode(vcfg, dev, z, hp, wp)
+    torch.cuda.synchronize()
+    assert torch.equal(planned, plain), "tile plan / folded GroupNorm changed the decode"
+
+
 def test_decode_chunked_attention_matches_whole():
     # 16 x 16 tokens = 32 x 32 latent pixels = 1024 queries, run as four
     # chunks of 256 rows

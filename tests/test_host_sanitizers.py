@@ -59,3 +59,18 @@ def test_sanitized_layouts_equal_the_library(plan_check):
         assert dit.workspace_bytes(CONFIGS[ci], kind, B, S) == total, line
         n += 1
     assert n > 300
+
+
+def test_sanitized_decoder_layouts_equal_the_library(plan_check):
+    import dataclasses
+    cfgs = [synth.VAE_KLEIN,
+            dataclasses.replace(synth.VAE_KLEIN, block_channels=(32, 64, 64, 128), layers=2),
+            dataclasses.replace(synth.VAE_KLEIN, block_channels=(256, 512, 1024, 2048), layers=4)]
+    n = 0
+    for line in plan_check.stdout.splitlines():
+        if not line.startswith("vae_layout "):
+            continue
+        ci, B, hp, wp, total = (int(v) for v in line.split()[1:])
+        assert dit.vae_workspace_bytes(cfgs[ci], B, hp, wp) == total, line
+        n += 1
+    assert n == 3 * 4 * 7
