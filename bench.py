@@ -166,6 +166,31 @@ def cpu_baseline(cfg, mw, wl):
     return sec, threads, flops
 
 
+def decode_cpu_baseline(hp=32, wp=32):
+    """The decoder oracle as it stands, in fp32 NumPy (its dtype switch), on a
+    bounded sample: one decode of an hp x wp token grid (a 512 x 512 image by
+    default, 2.6 TFLOP, about 8-25 s on the hosts measured), after a
+    64 x 64-image warm-up. Returns (seconds, threads, FLOPs of the sample, FLOPs of a
+    1024 x 1024 decode)."""
+    from oracle import vae_oracle as V
+    from diffusion_transformer_fwd_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    vcfg = synth.VAE_KLEIN
+    w = synth.vae_weights(vcfg, 0)
+    V.decode(vcfg, w, synth.vae_latents(vcfg, 0, 4, 4)[None], 4, 4, dtype=np.float32)
+    z = synth.vae_latents(vcfg, 0, hp, wp)[None]
+    t0 = time.perf_counter()
+    img = V.decode(vcfg, w, z, hp, wp, dtype=np.float32)
+    sec = time.perf_counter() - t0
+    assert np.all(np.isfinite(img))
+    gh, gw = synth.V_DECODE_1024.grid
+    return sec, threads, V.decode_flops(vcfg, 1, hp, wp), V.decode_flops(vcfg, 1, gh, gw)
+
+
 def matrix_tflops(k):
     """TFLOP/s of the GEMM and attention launches together (plain GEMM,
     plain attention, and attention fused with GEMM tiles), from a per-kernel
@@ -487,6 +512,17 @@ def main():
         which = (synth.V_DECODE_1024,) if args.no_extra_workloads else (
             synth.V_DECODE_1024, synth.V_DECODE_1920x1088_B4)
         dec = decode_leg(dit, synth, torch, which)
+        if not args.no_cpu_baseline:
+            log("decoder CPU baseline: the oracle in fp32 NumPy on a 512 x 512 decode")
+            sec, threads, fl, fl_1024 = decode_cpu_baseline()
+            dec[synth.V_DECODE_1024.name]["cpu_baseline"] = {
+                "value": round(sec * fl_1024 / fl * 1000.0, 1), "unit": "ms", "cores": threads,
+                "kind": "oracle", "gflops": round(fl / sec / 1e9, 1),
+                "sample": f"one 512 x 512 decode (32 x 32 tokens, {fl / 1e12:.2f} TFLOP), "
+                          f"oracle in fp32 NumPy, timed once after a small warm-up, "
+                          f"{sec:.1f} s; scaled by FLOPs to one 1024 x 1024 decode "
+                          f"({fl_1024 / 1e12:.2f} TFLOP)"}
+            log(f"decoder CPU baseline {sec:.1f} s for the sample")
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -376,7 +376,11 @@ hipError_t time_features_launch(const TimeArgs& a, hipStream_t stream) {
 
 hipError_t gemv_launch(const GemvArgs& a, hipStream_t stream) {
   if (a.B > kGemvMaxB || a.K > kGemvMaxK || (a.K & 7)) return hipErrorInvalidValue;
-  const int blocks = min(2048, (a.total_rows + 3) / 4);
+  // 1024 workgroups (4 per CU): every workgroup first copies x into LDS, so
+  // more of them cost more than their extra loads in flight bring (the
+  // three modulation GEMVs: 84 us at 1024, 87-90 at 2048, 104 at 512, 122
+  // at one row per wave)
+  const int blocks = min(1024, (a.total_rows + 3) / 4);
   const size_t lds = (size_t)a.B * a.K * sizeof(float);
   hipLaunchKernelGGL(gemv_kernel, dim3((unsigned)blocks), dim3(256), lds, stream, a);
   return hipGetLastError();

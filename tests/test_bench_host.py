@@ -86,3 +86,13 @@ def test_cpu_baseline_times_one_whole_fp32_step():
     blk = 2 * S * D * (3 * D + 2 * F) + 2 * S * (D + F) * D + 4 * S * S * D
     rest = 2 * D * (16 * 256 + 16 * 128 + 16 * 128)
     assert flops == 8 * blk + rest
+
+
+def test_decode_cpu_baseline_times_one_fp32_decode():
+    # a small grid keeps the test quick; the bench uses 32 x 32 tokens
+    sec, threads, fl, fl_1024 = bench.decode_cpu_baseline(hp=2, wp=3)
+    assert sec > 0 and threads >= 1
+    from oracle import vae_oracle as V
+    assert fl == V.decode_flops(synth.VAE_KLEIN, 1, 2, 3)
+    assert fl_1024 == V.decode_flops(synth.VAE_KLEIN, 1, 64, 64)
+    assert 10.4e12 < fl_1024 < 10.6e12
