@@ -139,20 +139,29 @@ def conv_tile(c):
 TILE_SHAPES = range(6)
 
 
-@pytest.mark.parametrize("case", [("c128_up", 2, 12, 40, 128, 1, 192), ("c256_ragged", 1, 13, 37, 256, 0, 72),
-                                  ("c64", 1, 9, 70, 64, 0, 128)], ids=lambda c: c[0])
+@pytest.mark.parametrize("case", [("c128_up", 2, 12, 40, 128, 1, 192, 0), ("c256_ragged", 1, 13, 37, 256, 0, 72, 0),
+                                  ("c64", 1, 9, 70, 64, 0, 128, 0),
+                                  ("c256_short128_b2", 2, 11, 45, 256, 0, 256, 128),
+                                  ("c128_short64_ragged", 1, 9, 35, 128, 0, 40, 64)], ids=lambda c: c[0])
 def test_conv_tile_shapes_bitwise(case):
     """Every tile shape (both kernels) gives the same bits for one conv: the
-    same k-steps in the same order, whatever the tiling."""
-    name, B, H, W, ci, up, co = case
+    same k-steps in the same order, whatever the tiling, the 1x1 shortcut's
+    slices after the 3x3 slices. (A conv with a shortcut has no halo shape:
+    asking for one falls back to the planned implicit tile.)"""
+    name, B, H, W, ci, up, co, cs = case
     Hi, Wi = (H // 2, W // 2) if up else (H, W)
     x = dit.to_bf16_device(np.stack([synth.normal(b, "t.tile.x", (Hi, Wi, ci)) for b in range(B)]))
     w = dit.to_bf16_device(synth._conv_w(0, "t.tile.w", co, 3, ci))
     bias = dit.to_f32_device(synth.normal(0, "t.tile.b", (co,), std=0.1))
+    kw = {}
+    if cs:
+        kw = dict(xs=dit.to_bf16_device(np.stack([synth.normal(b, "t.tile.xs", (H, W, cs)) for b in range(B)])),
+                  c_short=cs, short_w=dit.to_bf16_device(synth._conv_w(0, "t.tile.ws", co, 1, cs)),
+                  short_b=dit.to_f32_device(synth.normal(0, "t.tile.bs", (co,), std=0.1)))
     outs = []
     for c in TILE_SHAPES:
         with conv_tile(c):
-            outs.append(dit.vae_conv(x, ci, 3, up, w, bias, B, H, W, co))
+            outs.append(dit.vae_conv(x, ci, 3, up, w, bias, B, H, W, co, **kw))
     torch.cuda.synchronize()
     for c in TILE_SHAPES[1:]:
         assert torch.equal(outs[0], outs[c]), f"{name}: tile shape {c} differs from shape 0"
@@ -255,8 +264,15 @@ def test_decode_tile_plan_and_folded_group_norm_bitwise():
     planned = dit.vae_decode(vcfg, dev, z, hp, wp)
     with conv_tile(0):
         plain = dit.vae_decode(vcfg, dev, z, hp, wp)
+    # every 3x3 conv without a shortcut on one halo shape, GroupNorm folded
+    forced = []
+    for c in (4, 5):
+        with conv_tile(c):
+            forced.append(dit.vae_decode(vcfg, dev, z, hp, wp))
     torch.cuda.synchronize()
     assert torch.equal(planned, plain), "tile plan / folded GroupNorm changed the decode"
+    for c, img in zip((4, 5), forced):
+        assert torch.equal(img, plain), f"halo shape {c} with folded GroupNorm changed the decode"
 
 
 def test_decode_chunked_attention_matches_whole():
