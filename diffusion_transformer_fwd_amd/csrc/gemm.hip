@@ -664,19 +664,28 @@ int device_cus() {
   return cached[dev];
 }
 
-// ---- launch plan: tile width of the launch and tile height per problem.
+// ---- launch plan: tile width of the launch and, per problem, the tile
+// height of its rows (a problem whose rows form one segment may have its
+// first rows in 384-row tiles and the rest in 256-row tiles: two parts).
 // A tile's time per K slice is modelled from what a loader wave does in it:
 // its load instructions (4 FM + 8) and its own MFMAs (FM x 4 k-steps x its
 // active column blocks), weighted 4 : 3. Fitted to kernel traces at 4608
 // rows (a 384-row tile takes 1.40x a 256-row one: 116 vs 83 us at K = 3072).
-// The launch time is modelled as one XCD's share of every problem (a
-// problem's tiles are dealt evenly to the 8 XCDs), in launch order, placed
-// greedily on that XCD's CUs, which reproduces the traced launch times of
-// the step within 3 %; plans are cached per launch shape.
+// The launch time is modelled as one XCD's share of every part (a part's
+// tiles are dealt evenly to the 8 XCDs), in launch order, placed greedily on
+// that XCD's CUs, which reproduces the traced launch times of the step
+// within 3 %; plans are cached per launch shape.
+struct Part {
+  int prob;   // problem of the batch
+  int row0;   // its first row
+  int rows;
+  int fm;     // tile height 128 fm
+};
+
 struct Plan {
   int bnt;
-  int fm[kMaxGemmProblems];
-  int order[kMaxGemmProblems];
+  int nparts;
+  Part part[kMaxGemmProblems];  // launch order
 };
 
 int64_t tile_cost(int fm, int bnt, int64_t K) {
@@ -695,8 +704,7 @@ struct Prefix {
   int64_t cost = 0;   // model cost of one
 };
 
-int64_t model_time(const GemmBatch& b, const int* fm, const int* order, int bnt, int cus_per_xcd,
-                   const Prefix& pre) {
+int64_t model_time(const GemmBatch& b, const Plan& pl, int cus_per_xcd, const Prefix& pre) {
   std::vector<int64_t> cu((size_t)std::max(cus_per_xcd, 1), 0);
   auto place = [&](int64_t n, int64_t c) {
     for (int64_t t = 0; t < n; ++t) {
@@ -705,12 +713,13 @@ int64_t model_time(const GemmBatch& b, const int* fm, const int* order, int bnt,
     }
   };
   place((pre.units + 7) / 8, pre.cost);
-  for (int oi = 0; oi < b.count; ++oi) {
-    const GemmProblem& p = b.p[order[oi]];
-    const int cols = p.epi == EPI_SWIGLU ? BN / 2 : bnt;
-    const int64_t n = (int64_t)((p.M + 128 * fm[order[oi]] - 1) / (128 * fm[order[oi]])) *
+  for (int k = 0; k < pl.nparts; ++k) {
+    const Part& pt = pl.part[k];
+    const GemmProblem& p = b.p[pt.prob];
+    const int cols = p.epi == EPI_SWIGLU ? BN / 2 : pl.bnt;
+    const int64_t n = (int64_t)((pt.rows + 128 * pt.fm - 1) / (128 * pt.fm)) *
                       ((p.N + cols - 1) / cols);
-    place((n + 7) / 8, tile_cost(fm[order[oi]], bnt, p.K));
+    place((n + 7) / 8, tile_cost(pt.fm, pl.bnt, p.K));
   }
   return *std::max_element(cu.begin(), cu.end());
 }
@@ -725,39 +734,99 @@ int forced_rows() {
   return v == 256 || v == 384 ? v : 0;
 }
 
+// DIT_GEMM_SPLIT_ROWS=a (a positive multiple of 384) forces the split of
+// every launch's largest one-segment problem with more than a rows at row a
+// (tests compare it bit for bit with the other tilings); 0 when unset.
+int forced_split() {
+  const char* e = std::getenv("DIT_GEMM_SPLIT_ROWS");
+  if (!e) return 0;
+  const int v = std::atoi(e);
+  return v > 0 && v % 384 == 0 ? v : 0;
+}
+
+// Parts in launch order: taller tiles first (stable), so each XCD ends on
+// its short tiles.
+void order_parts(Plan& pl) {
+  std::stable_sort(pl.part, pl.part + pl.nparts,
+                   [](const Part& x, const Part& y) { return x.fm > y.fm; });
+}
+
 Plan make_plan(const GemmBatch& b, int cus, int forced, const Prefix& pre, int64_t* time) {
   bool narrow_ok = true;
   for (int i = 0; i < b.count; ++i)
     if (b.p[i].epi == EPI_SWIGLU || b.p[i].epi == EPI_QKV) narrow_ok = false;
   // candidates: 384-row tiles for any subset of the (at most three) largest
-  // problems with at least 384 rows; everything else 256 rows
-  int big[3], nbig = 0;
+  // problems with at least 384 rows, everything else 256 rows; and the
+  // largest problem whose rows form one segment split into a 384-row part
+  // (a multiple of 384 rows) and a 256-row part
+  int big[3], nbig = 0, split = -1;
   if (!forced) {
     std::vector<std::pair<int64_t, int>> sz;
     for (int i = 0; i < b.count; ++i)
       if (b.p[i].M >= 384) sz.push_back({-(int64_t)b.p[i].M * b.p[i].N * b.p[i].K, i});
     std::sort(sz.begin(), sz.end());
     for (size_t j = 0; j < sz.size() && nbig < 3; ++j) big[nbig++] = sz[j].second;
+    for (size_t j = 0; j < sz.size() && split < 0; ++j)
+      if (b.p[sz[j].second].seg_len >= b.p[sz[j].second].M && b.p[sz[j].second].M > 384)
+        split = sz[j].second;
+    if (b.count >= kMaxGemmProblems) split = -1;  // no slot for a second part
+  }
+  const int fsplit = forced ? 0 : forced_split();
+  if (fsplit > 0 && split >= 0 && b.p[split].M > fsplit) {
+    // the forced split, every other problem in 256-row tiles
+    Plan ps{};
+    ps.bnt = BN;
+    for (int i = 0; i < b.count; ++i) {
+      if (i != split) {
+        ps.part[ps.nparts++] = Part{i, 0, b.p[i].M, 2};
+      } else {
+        ps.part[ps.nparts++] = Part{i, 0, fsplit, 3};
+        ps.part[ps.nparts++] = Part{i, fsplit, b.p[i].M - fsplit, 2};
+      }
+    }
+    order_parts(ps);
+    if (time) *time = model_time(b, ps, std::max(1, cus / 8), pre);
+    return ps;
   }
   Plan best{};
   int64_t best_t = -1;
   const int cpx = std::max(1, cus / 8);
+  auto consider = [&](const Plan& pl) {
+    const int64_t t = model_time(b, pl, cpx, pre);
+    if (best_t < 0 || t < best_t) {
+      best_t = t;
+      best = pl;
+    }
+  };
   for (int bnt : {256, 224}) {
     if (bnt == 224 && !narrow_ok) continue;
     for (int mask = 0; mask < (1 << nbig); ++mask) {
+      int fm[kMaxGemmProblems];
+      for (int i = 0; i < kMaxGemmProblems; ++i) fm[i] = forced == 384 ? 3 : 2;
+      for (int j = 0; j < nbig; ++j)
+        if (mask >> j & 1) fm[big[j]] = 3;
       Plan pl{};
       pl.bnt = bnt;
-      for (int i = 0; i < kMaxGemmProblems; ++i) pl.fm[i] = forced == 384 ? 3 : 2;
-      for (int j = 0; j < nbig; ++j)
-        if (mask >> j & 1) pl.fm[big[j]] = 3;
-      // taller tiles first (stable), so each XCD ends on its short tiles
-      for (int i = 0; i < b.count; ++i) pl.order[i] = i;
-      std::stable_sort(pl.order, pl.order + b.count,
-                       [&](int x, int y) { return pl.fm[x] > pl.fm[y]; });
-      const int64_t t = model_time(b, pl.fm, pl.order, bnt, cpx, pre);
-      if (best_t < 0 || t < best_t) {
-        best_t = t;
-        best = pl;
+      pl.nparts = b.count;
+      for (int i = 0; i < b.count; ++i) pl.part[i] = Part{i, 0, b.p[i].M, fm[i]};
+      order_parts(pl);
+      consider(pl);
+      if (split < 0) continue;
+      const int M = b.p[split].M;
+      for (int a = 384; a < M; a += 384) {
+        Plan ps{};
+        ps.bnt = bnt;
+        ps.nparts = 0;
+        for (int i = 0; i < b.count; ++i) {
+          if (i != split) {
+            ps.part[ps.nparts++] = Part{i, 0, b.p[i].M, fm[i]};
+          } else {
+            ps.part[ps.nparts++] = Part{i, 0, a, 3};
+            ps.part[ps.nparts++] = Part{i, a, M - a, 2};
+          }
+        }
+        order_parts(ps);
+        consider(ps);
       }
     }
   }
@@ -769,6 +838,7 @@ using PlanKey = std::tuple<int, int, int64_t, int, std::vector<int64_t>>;
 
 Plan cached_plan(const GemmBatch& b, int cus, const Prefix& pre = Prefix{}) {
   const int forced = forced_rows();
+  const int fsplit = forced_split();
   static std::mutex mu;
   static std::map<PlanKey, Plan> cache;
   std::vector<int64_t> shape;
@@ -777,7 +847,7 @@ Plan cached_plan(const GemmBatch& b, int cus, const Prefix& pre = Prefix{}) {
     shape.insert(shape.end(), {(int64_t)p.M, (int64_t)p.N, (int64_t)p.K, (int64_t)p.epi});
   }
   shape.insert(shape.end(), {pre.units, pre.cost});
-  PlanKey key{cus, forced, 0, b.count, shape};
+  PlanKey key{cus, forced, fsplit, b.count, shape};
   std::lock_guard<std::mutex> lock(mu);
   auto it = cache.find(key);
   if (it != cache.end()) return it->second;
@@ -792,19 +862,30 @@ namespace {
 
 bool is_f32_epi(int epi) { return epi == EPI_F32 || epi == EPI_RESID; }
 
-// Applies plan pl to a copy of batch: launch order, tile heights and counts.
+// Applies plan pl to a copy of batch: one problem per part, in launch
+// order, with its tile height and counts. A part that starts at row r0 of
+// its (one-segment) problem reads A from row r0 and writes output rows (and
+// QKV tokens) from seg_off + r0.
 // Returns the tile count (< 0 if it does not fit the grid).
 int64_t prepare(const GemmBatch& batch, const Plan& pl, GemmBatch& b) {
   b = batch;
-  for (int i = 0; i < batch.count; ++i) {
-    b.p[i] = batch.p[pl.order[i]];
-    b.qkv.q_gain[i] = batch.qkv.q_gain[pl.order[i]];
-    b.qkv.k_gain[i] = batch.qkv.k_gain[pl.order[i]];
+  b.count = pl.nparts;
+  for (int k = 0; k < pl.nparts; ++k) {
+    const Part& pt = pl.part[k];
+    GemmProblem p = batch.p[pt.prob];
+    if (pt.row0 != 0 || pt.rows != p.M) {
+      p.A += (int64_t)pt.row0 * p.lda;
+      p.seg_off += pt.row0;
+      p.M = pt.rows;
+    }
+    b.p[k] = p;
+    b.qkv.q_gain[k] = batch.qkv.q_gain[pt.prob];
+    b.qkv.k_gain[k] = batch.qkv.k_gain[pt.prob];
   }
   int64_t total = 0;
-  for (int i = 0; i < b.count; ++i) {
-    GemmProblem& p = b.p[i];
-    p.fm = pl.fm[pl.order[i]];
+  for (int k = 0; k < b.count; ++k) {
+    GemmProblem& p = b.p[k];
+    p.fm = pl.part[k].fm;
     const int cols = p.epi == EPI_SWIGLU ? BN / 2 : pl.bnt;
     p.tiles_m = (p.M + 128 * p.fm - 1) / (128 * p.fm);
     p.tiles_n = (p.N + cols - 1) / cols;
@@ -878,7 +959,7 @@ int64_t fused_split_rows(const GemmProblem& first, const GemmProblem& rest, int6
   static std::mutex mu;
   static std::map<std::vector<int64_t>, int64_t> cache;
   const int cus = device_cus(), forced = forced_rows();
-  const std::vector<int64_t> key{cus, forced, row_step, first.M, first.N, first.K, first.epi,
+  const std::vector<int64_t> key{cus, forced, forced_split(), row_step, first.M, first.N, first.K, first.epi,
                                  rest.M, rest.N, rest.K, rest.epi, a.S, a.B, a.H};
   {
     std::lock_guard<std::mutex> lock(mu);
@@ -904,7 +985,11 @@ int64_t fused_split_rows(const GemmProblem& first, const GemmProblem& rest, int6
     int64_t t1 = 0, t2 = 0;
     make_plan(b1, cus, forced, Prefix{}, &t1);
     if (b2.count) make_plan(b2, cus, forced, pre, &t2);
-    else t2 = model_time(b2, nullptr, nullptr, BN, std::max(1, cus / 8), pre);
+    else {
+      Plan none{};
+      none.bnt = BN;
+      t2 = model_time(b2, none, std::max(1, cus / 8), pre);
+    }
     if (best_t < 0 || t1 + t2 < best_t) {
       best_t = t1 + t2;
       best_rows = m1;

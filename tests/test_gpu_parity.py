@@ -292,8 +292,11 @@ def test_gemm_tile_heights_bitwise(case):
     wd = dit.DualWeights(synth.dual_weights(cfg, 0, 0))
     wsn = dit.SingleWeights(synth.single_weights(cfg, 0, 0))
     outs = {}
-    for rows in (256, 384, None):
-        ctx = gemm_tile_rows(rows) if rows else contextlib.nullcontext()
+    for rows in (256, 384, None, "split"):
+        if rows == "split":
+            ctx = gemm_split_rows(384)
+        else:
+            ctx = gemm_tile_rows(rows) if rows else contextlib.nullcontext()
         with ctx:
             x = torch.from_numpy(xs).cuda()
             dit.dual_block(cfg, wd, x, n_txt, mod_d, cos_d, sin_d)
@@ -303,6 +306,22 @@ def test_gemm_tile_heights_bitwise(case):
         log(f"tiles {name}: {rows or 'plan'} rows done")
     assert np.array_equal(outs[256], outs[384]), "256- and 384-row tiles differ"
     assert np.array_equal(outs[256], outs[None]), "the launch plan's tiles differ"
+    assert np.array_equal(outs[256], outs["split"]), "problems split into 384- and 256-row parts differ"
+
+
+@contextlib.contextmanager
+def gemm_split_rows(rows):
+    """Force every launch's largest one-segment problem with more than `rows`
+    rows into a 384-row-tile part of `rows` rows and a 256-row-tile rest."""
+    old = os.environ.get("DIT_GEMM_SPLIT_ROWS")
+    os.environ["DIT_GEMM_SPLIT_ROWS"] = str(rows)
+    try:
+        yield
+    finally:
+        if old is None:
+            del os.environ["DIT_GEMM_SPLIT_ROWS"]
+        else:
+            os.environ["DIT_GEMM_SPLIT_ROWS"] = old
 
 
 @contextlib.contextmanager
@@ -355,21 +374,25 @@ def test_single_block_fused_split_bitwise(case):
     check_block(xs, outs[None], want, f"single fused {name}")
 
 
-def test_gemm_tile_heights_bitwise_step():
+@pytest.mark.parametrize("B", [2, 1])
+def test_gemm_tile_heights_bitwise_step(B):
     """A small step (embeddings with a K-split, final projection, fp32
-    epilogues) with 256-row and 384-row tiles: bitwise equal."""
+    epilogues) with 256-row tiles, 384-row tiles and (one batch row, where
+    every problem is one segment) problems split into 384- and 256-row
+    parts: bitwise equal."""
     cfg = small_cfg(hidden=1024, heads=8, mlp_hidden=3072, txt_channels=4096)
     mw = synth.ModelWeights(cfg, 0, cache=True)
     dw = dit.ModelWeights(mw)
-    wl = synth.Workload("s", 2, 48, (20, 21), ((6, 5),), 0.6)
+    wl = synth.Workload("s", B, 48, (20, 21), ((6, 5),), 0.6)
     pos = dit.position_ids(wl.n_txt, wl.img_grid, wl.ref_grids)
     cos_d, sin_d = dit.rope_tables(cfg, pos)
     got = {}
-    for rows in (256, 384):
-        with gemm_tile_rows(rows):
+    for rows in (256, 384, "split"):
+        with (gemm_split_rows(384) if rows == "split" else gemm_tile_rows(rows)):
             v, _ = run_step(cfg, dw, wl, cos_d, sin_d)
         got[rows] = to_np(v)
     assert np.array_equal(got[256], got[384])
+    assert np.array_equal(got[256], got["split"])
 
 
 # ---------------------------------------------------------------- steps
