@@ -209,7 +209,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(const GemvArgs a) {
   // so the lanes of a wave, which take consecutive chunks c, read consecutive
   // 16-byte words (a plain [B][K] layout has them 32 bytes apart, which
   // conflicts on the LDS banks)
-  extern __shared__ float xs_dyn[];
+  extern __shared__ __attribute__((aligned(16))) float xs_dyn[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int K8 = a.K >> 3;
   for (int i = tid; i < a.B * a.K; i += 256) {
