@@ -331,10 +331,21 @@ __device__ __forceinline__ void gemm_tile(const GemmBatch& args, const GemmProbl
   // lane: stores straight from the MFMA layout would be 16-byte pieces of 32
   // rows per instruction. Every wave reaches every barrier below.
   char* const T = reinterpret_cast<char*>(lds);
+  // The problem's output fields, read once: through the reference into the
+  // kernel arguments they would be read again after every store (a store
+  // could alias them), one scalar-load round trip per 16 bytes written.
+  const int seg_len = P.seg_len, seg_off = P.seg_off;
+  const int64_t seg_stride = P.seg_stride, ldc = P.ldc;
+  void* const Cp = P.C;
+  // A tile's rows lie in one segment unless a segment is shorter than the
+  // tile; then output row and batch row come without a division.
+  const int b_first = m0 / seg_len, b_last = (min(M, m0 + BM) - 1) / seg_len;
+  const bool one_seg = b_first == b_last;
+  auto batch_of = [&](int gr) -> int { return one_seg ? b_first : gr / seg_len; };
   // bf16 stage [rows][256]: 16-byte chunk c of row r at c ^ (r & 31)
   auto out_row_of = [&](int gr, int& b) -> int64_t {
-    b = gr / P.seg_len;
-    return (int64_t)b * P.seg_stride + P.seg_off + (gr - b * P.seg_len);
+    b = batch_of(gr);
+    return (int64_t)b * seg_stride + seg_off + (gr - b * seg_len);
   };
 
   if (EK == EK_F32) {
@@ -366,6 +377,8 @@ __device__ __forceinline__ void gemm_tile(const GemmBatch& args, const GemmProbl
       asm volatile("" : "+s"(m0p));
       const int c = lane, col = tn * BNT + c * 4;
       const bool col_ok = c * 4 < BNT && col < N;
+      const float* const gate = P.gate;
+      const int64_t gate_bs = P.gate_bstride;
 #pragma unroll
       for (int half = 0; half < 16 / RF; ++half) {
         float* dst[RF];
@@ -377,9 +390,9 @@ __device__ __forceinline__ void gemm_tile(const GemmBatch& args, const GemmProbl
           dst[k] = nullptr;
           if (col_ok && gr < M) {
             int b;
-            dst[k] = static_cast<float*>(P.C) + out_row_of(gr, b) * P.ldc + col;
+            dst[k] = static_cast<float*>(Cp) + out_row_of(gr, b) * ldc + col;
             if (epi == EPI_RESID) {
-              g[k] = *reinterpret_cast<const f32x4*>(P.gate + (int64_t)b * P.gate_bstride + col);
+              g[k] = *reinterpret_cast<const f32x4*>(gate + (int64_t)b * gate_bs + col);
               x[k] = *reinterpret_cast<const f32x4*>(dst[k]);
             }
           }
@@ -405,11 +418,21 @@ __device__ __forceinline__ void gemm_tile(const GemmBatch& args, const GemmProbl
     // row in LDS (outside every pass's stage); a row's 128 values of a head
     // sit in lanes l and l ^ 32, so the sum of squares needs one cross-half
     // exchange.
-    const QkvEpilogue& E = args.qkv;
+    // the shared operands, read once (see above)
+    bf16_t* const eq = args.qkv.q;
+    bf16_t* const ek = args.qkv.k;
+    bf16_t* const evt = args.qkv.vt;
+    const float* const cos_t = args.qkv.cos_t;
+    const float* const sin_t = args.qkv.sin_t;
+    const float* const q_gain = args.qkv.q_gain[pi];
+    const float* const k_gain = args.qkv.k_gain[pi];
+    const int64_t S_pad = args.qkv.S_pad;
+    const int EH = args.qkv.H, ED = args.qkv.D;
+    const float eps = args.qkv.eps, q_scale = args.qkv.q_scale;
     float* const row_scale = reinterpret_cast<float*>(T + RS_BYTE);  // [2][BM]
     const int wcol0 = tn * BN + wn * WTN;  // first projection column of the wave
-    if (wcol0 < N && wcol0 / E.D < 2) {
-      const float sc = wcol0 / E.D == 0 ? E.q_scale : 1.f;
+    if (wcol0 < N && wcol0 / ED < 2) {
+      const float sc = wcol0 / ED == 0 ? q_scale : 1.f;
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         float ss = 0.f;
@@ -419,7 +442,7 @@ __device__ __forceinline__ void gemm_tile(const GemmBatch& args, const GemmProbl
           for (int e = 0; e < 16; ++e) ss += acc[i][j][e] * acc[i][j][e];
         ss = half_sum(ss);
         if (fg == 0)
-          row_scale[wn * BM + wm * WTM + i * 32 + fr] = rsqrtf(ss * (1.f / 128.f) + E.eps) * sc;
+          row_scale[wn * BM + wm * WTM + i * 32 + fr] = rsqrtf(ss * (1.f / 128.f) + eps) * sc;
       }
     }
 #pragma unroll
@@ -446,13 +469,13 @@ __device__ __forceinline__ void gemm_tile(const GemmBatch& args, const GemmProbl
       for (int hh = 0; hh < 2; ++hh) {
         const int col0 = tn * BN + hh * 128;
         if (col0 >= N) break;
-        const int part = col0 / E.D;
-        const int h = (col0 - part * E.D) >> 7;
+        const int part = col0 / ED;
+        const int h = (col0 - part * ED) >> 7;
         if (part < 2) {
           // q / k rows to [b, h, s, :]: 16 lanes per token row, 8 columns (4
           // rotation pairs) per lane
-          bf16_t* base = part == 0 ? E.q : E.k;
-          const float* gain = part == 0 ? E.q_gain[pi] : E.k_gain[pi];
+          bf16_t* base = part == 0 ? eq : ek;
+          const float* gain = part == 0 ? q_gain : k_gain;
           const int cl = (tid & 15) * 8;  // column within the head
           const f32x4 g0 = *reinterpret_cast<const f32x4*>(gain + cl);
           const f32x4 g1 = *reinterpret_cast<const f32x4*>(gain + cl + 4);
@@ -462,13 +485,13 @@ __device__ __forceinline__ void gemm_tile(const GemmBatch& args, const GemmProbl
             const int tr = tile_row(r);
             const int gr = m0 + tr;
             if (gr >= M) continue;
-            const int b = gr / P.seg_len;
-            const int s = P.seg_off + (gr - b * P.seg_len);
+            const int b = batch_of(gr);
+            const int s = seg_off + (gr - b * seg_len);
             const f32x4 v0 = *reinterpret_cast<const f32x4*>(stage_f32(r, hh * 128 + cl));
             const f32x4 v1 = *reinterpret_cast<const f32x4*>(stage_f32(r, hh * 128 + cl + 4));
             const float rsc = row_scale[hh * BM + tr];
-            const f32x4 co = *reinterpret_cast<const f32x4*>(E.cos_t + (int64_t)s * 64 + (cl >> 1));
-            const f32x4 si = *reinterpret_cast<const f32x4*>(E.sin_t + (int64_t)s * 64 + (cl >> 1));
+            const f32x4 co = *reinterpret_cast<const f32x4*>(cos_t + (int64_t)s * 64 + (cl >> 1));
+            const f32x4 si = *reinterpret_cast<const f32x4*>(sin_t + (int64_t)s * 64 + (cl >> 1));
             f32x8 y;
 #pragma unroll
             for (int pr = 0; pr < 4; ++pr) {
@@ -481,7 +504,7 @@ __device__ __forceinline__ void gemm_tile(const GemmBatch& args, const GemmProbl
               y[2 * pr] = x0 * co[pr] - x1 * si[pr];
               y[2 * pr + 1] = x0 * si[pr] + x1 * co[pr];
             }
-            *reinterpret_cast<bf16x8*>(base + (((int64_t)b * E.H + h) * E.S_pad + s) * 128 + cl) =
+            *reinterpret_cast<bf16x8*>(base + (((int64_t)b * EH + h) * S_pad + s) * 128 + cl) =
                 pack_bf16x8(y);
           }
         } else {
@@ -496,19 +519,19 @@ __device__ __forceinline__ void gemm_tile(const GemmBatch& args, const GemmProbl
             const bf16x8 tb = pack_bf16x8(tv);
             const int r0 = m0 + tile_row(tg * 8);  // 8 stage rows = 8 tile rows
             if (r0 >= M) continue;
-            const int b0 = r0 / P.seg_len;
-            const int s0 = P.seg_off + (r0 - b0 * P.seg_len);
-            if (r0 + 7 < M && (r0 + 7) / P.seg_len == b0 && (s0 & 7) == 0) {
-              *reinterpret_cast<bf16x8*>(E.vt + (((int64_t)b0 * E.H + h) * 128 + d) * E.S_pad + s0) = tb;
+            const int b0 = batch_of(r0);
+            const int s0 = seg_off + (r0 - b0 * seg_len);
+            if (r0 + 7 < M && batch_of(r0 + 7) == b0 && (s0 & 7) == 0) {
+              *reinterpret_cast<bf16x8*>(evt + (((int64_t)b0 * EH + h) * 128 + d) * S_pad + s0) = tb;
             } else {
               const u32x4 tw = __builtin_bit_cast(u32x4, tb);
 #pragma unroll
               for (int e = 0; e < 8; ++e) {
                 const int gr = r0 + e;
                 if (gr >= M) break;
-                const int b = gr / P.seg_len;
-                const int s = P.seg_off + (gr - b * P.seg_len);
-                E.vt[(((int64_t)b * E.H + h) * 128 + d) * E.S_pad + s] =
+                const int b = batch_of(gr);
+                const int s = seg_off + (gr - b * seg_len);
+                evt[(((int64_t)b * EH + h) * 128 + d) * S_pad + s] =
                     (bf16_t)((tw[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
               }
             }
@@ -579,19 +602,39 @@ __device__ __forceinline__ void gemm_tile(const GemmBatch& args, const GemmProbl
     }
     __syncthreads();
 
-    // phase B: whole rows out, 16 bytes per lane
+    // phase B: whole rows out, 16 bytes per lane; unit u = it NT + tid is
+    // row u / upr, chunk u % upr, stepped without a division
     const int ncol = epi == EPI_SWIGLU ? BN / 2 : BNT;  // output columns of the tile
     const int upr = ncol / 8;                          // 16-byte units per row
-#pragma unroll 4
-    for (int it = 0; it < 256 * (BN / 8) / NT; ++it) {
-      const int u = it * NT + tid;
-      if (u >= prow * upr) break;
-      const int r = u / upr, c = u - r * upr;
-      const int gr = m0 + tile_row(r), col = tn * ncol + c * 8;
-      if (gr >= M || col >= N) continue;
-      int b;
-      *reinterpret_cast<u32x4*>(static_cast<bf16_t*>(P.C) + out_row_of(gr, b) * P.ldc + col) =
-          *reinterpret_cast<const u32x4*>(T + r * 512 + ((c ^ (r & 31)) << 4));
+    // (prow upr is a multiple of NT for every tile shape: no partial step);
+    // the LDS reads of four units go out before their four stores
+    const int r_step = NT / upr, c_step = NT - r_step * upr;
+    const int n_it = prow * upr / NT;
+    int r = tid / upr, c = tid - (tid / upr) * upr;
+    for (int it0 = 0; it0 < n_it; it0 += 4) {
+      u32x4 v[4];
+      bf16_t* dst[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        dst[k] = nullptr;
+        if (it0 + k < n_it) {
+          const int gr = m0 + tile_row(r), col = tn * ncol + c * 8;
+          v[k] = *reinterpret_cast<const u32x4*>(T + r * 512 + ((c ^ (r & 31)) << 4));
+          if (gr < M && col < N) {
+            int b;
+            dst[k] = static_cast<bf16_t*>(Cp) + out_row_of(gr, b) * ldc + col;
+          }
+          r += r_step;
+          c += c_step;
+          if (c >= upr) {
+            c -= upr;
+            ++r;
+          }
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (dst[k] != nullptr) *reinterpret_cast<u32x4*>(dst[k]) = v[k];
     }
     if (pass + 1 < NPASS) __syncthreads();  // the next pass overwrites the stage
   }
