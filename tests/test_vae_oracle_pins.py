@@ -13,7 +13,11 @@ never against the oracle's own formulas retyped.
     convs as well, the whole decoder reduces to
     conv_out(SiLU(GN(up(up(up(conv_in(u))))))), computed with the loop
     primitives;
-  * planted mistakes that one of the pins must catch.
+  * planted mistakes that one of the pins must catch: slips put into the
+    oracle module itself (a dropped bias, a flipped kernel, eps outside the
+    root, unbiased or per-row GroupNorm statistics, SiLU as a sigmoid, an
+    upsample off by one row, a sliced shortcut, SiLU before the norm, a
+    1 / C score scale, softmax over queries, a channel-major patch order).
 The layer list itself is a reading with nothing on the pages to check it
 against.
 """
@@ -282,3 +286,115 @@ def test_planted_per_channel_norm_is_caught():
     wrong = V.group_norm(x, g, b, 8, 1e-6)   # stats per channel instead of per group of 2
     ref = np.array(brute.group_norm_image(x[0], g, b, 4, 1e-6))
     assert np.abs(wrong[0] - ref).max() > 1e-3
+
+
+# Planted mistakes in the oracle module itself: each mutant below is a
+# plausible slip in one oracle function, patched into the module; at least one
+# of the listed pins (which compare against loops and closed forms, not the
+# oracle's own formulas) must then fail.
+_conv2d, _group_norm, _silu, _upsample2x = V.conv2d, V.group_norm, V.silu, V.upsample2x
+_resnet, _attention, _unpatchify = V.resnet, V.attention, V.unpatchify
+
+
+def _gn_eps_outside_root(x, gamma, beta, groups, eps):
+    B, H, W, C = x.shape
+    xr = x.reshape(B, H * W, groups, C // groups)
+    d = xr - xr.mean(axis=(1, 3), keepdims=True)
+    sd = np.sqrt((d * d).mean(axis=(1, 3), keepdims=True))
+    return (d / (sd + eps)).reshape(B, H, W, C) * gamma + beta
+
+
+def _gn_unbiased(x, gamma, beta, groups, eps):
+    B, H, W, C = x.shape
+    xr = x.reshape(B, H * W, groups, C // groups)
+    d = xr - xr.mean(axis=(1, 3), keepdims=True)
+    n = H * W * (C // groups)
+    var = (d * d).sum(axis=(1, 3), keepdims=True) / (n - 1)
+    return (d / np.sqrt(var + eps)).reshape(B, H, W, C) * gamma + beta
+
+
+def _gn_stats_over_width_only(x, gamma, beta, groups, eps):
+    # statistics per (sample, row, group) instead of per (sample, group)
+    B, H, W, C = x.shape
+    xr = x.reshape(B, H, W, groups, C // groups)
+    d = xr - xr.mean(axis=(2, 4), keepdims=True)
+    var = (d * d).mean(axis=(2, 4), keepdims=True)
+    return (d / np.sqrt(var + eps)).reshape(B, H, W, C) * gamma + beta
+
+
+def _resnet_no_shortcut_conv(x, w, p, groups, eps):
+    h = _conv2d(_silu(_group_norm(x, w[p + "gn1.g"], w[p + "gn1.b"], groups, eps)),
+                w[p + "conv1.w"], w[p + "conv1.b"])
+    h = _conv2d(_silu(_group_norm(h, w[p + "gn2.g"], w[p + "gn2.b"], groups, eps)),
+                w[p + "conv2.w"], w[p + "conv2.b"])
+    if (p + "short.w") in w:
+        return h + x[..., :h.shape[-1]]
+    return x + h
+
+
+def _resnet_silu_before_norm(x, w, p, groups, eps):
+    h = _conv2d(_group_norm(_silu(x), w[p + "gn1.g"], w[p + "gn1.b"], groups, eps),
+                w[p + "conv1.w"], w[p + "conv1.b"])
+    h = _conv2d(_silu(_group_norm(h, w[p + "gn2.g"], w[p + "gn2.b"], groups, eps)),
+                w[p + "conv2.w"], w[p + "conv2.b"])
+    s = x if (p + "short.w") not in w else _conv2d(x, w[p + "short.w"], w[p + "short.b"])
+    return s + h
+
+
+def _attention_scale_by_c(q, k, v, chunk=2048):
+    return _attention(q * math.sqrt(q.shape[-1]) / q.shape[-1], k, v, chunk)
+
+
+def _attention_softmax_over_queries(q, k, v, chunk=2048):
+    s = (q @ k.T) / math.sqrt(q.shape[-1])
+    e = np.exp(s - s.max(axis=0, keepdims=True))
+    return (e / e.sum(axis=0, keepdims=True)) @ v
+
+
+def _unpatchify_channel_major(z, hp, wp, z_ch):
+    B = z.shape[0]
+    x = z.reshape(B, hp, wp, 2, 2, z_ch).transpose(0, 1, 3, 2, 4, 5)
+    return x.reshape(B, 2 * hp, 2 * wp, z_ch)
+
+
+_MUTANTS = {
+    "conv_without_bias": ("conv2d", lambda x, w, b, band=64: _conv2d(x, w, None, band),
+                          [test_conv_matches_loops_3x3_and_1x1, test_conv_1x1_is_matrix_product]),
+    "conv_true_convolution": ("conv2d",
+                              lambda x, w, b, band=64: _conv2d(x, w[:, ::-1, ::-1, :], b, band),
+                              [test_conv_impulse_fixes_orientation]),
+    "gn_eps_outside_root": ("group_norm", _gn_eps_outside_root,
+                            [test_group_norm_closed_forms]),
+    "gn_unbiased_variance": ("group_norm", _gn_unbiased, [test_group_norm_closed_forms]),
+    "gn_stats_per_row": ("group_norm", _gn_stats_over_width_only,
+                         [lambda: test_group_norm_matches_loops(2), test_group_norm_closed_forms]),
+    "silu_as_sigmoid": ("silu", lambda x: 1.0 / (1.0 + np.exp(-x)),
+                        [test_resnet_and_attention_blocks_match_loops]),
+    "upsample_offset_by_one": ("upsample2x",
+                               lambda x: np.concatenate([_upsample2x(x)[:, 1:], _upsample2x(x)[:, -1:]], 1),
+                               [test_upsample_index_map]),
+    "resnet_shortcut_sliced": ("resnet", _resnet_no_shortcut_conv,
+                               [test_resnet_and_attention_blocks_match_loops]),
+    "resnet_silu_before_norm": ("resnet", _resnet_silu_before_norm,
+                                [test_resnet_and_attention_blocks_match_loops]),
+    "attention_scaled_by_c": ("attention", _attention_scale_by_c,
+                              [test_resnet_and_attention_blocks_match_loops]),
+    "attention_softmax_over_queries": ("attention", _attention_softmax_over_queries,
+                                       [test_attention_matches_loops_and_closed_forms]),
+    "unpatchify_channel_major": ("unpatchify", _unpatchify_channel_major,
+                                 [test_unpatchify_inverts_loop_patchify,
+                                  test_decoder_reduces_to_conv_in_upsample_conv_out]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(_MUTANTS))
+def test_planted_decoder_mistake_is_caught(name, monkeypatch):
+    attr, mutant, pins = _MUTANTS[name]
+    monkeypatch.setattr(V, attr, mutant)
+    caught = 0
+    for pin in pins:
+        try:
+            pin()
+        except AssertionError:
+            caught += 1
+    assert caught > 0, f"no pin caught the planted mistake {name}"
