@@ -8,8 +8,11 @@ Kinds of pin used here:
     key permutation, scale/shift invariance of the norms, batch independence);
   * an independent brute-force float64 re-derivation on tiny inputs
     (oracle/brute.py: loops, complex-number RoPE, explicit softmax);
-  * planted mistakes: a plausible slip put into a copy of the oracle must be
-    caught by one of the pins above.
+  * planted mistakes: a plausible slip put into a copy of the oracle (the
+    Euler step, head split, attention scale) or patched into the module in
+    place of one page rule (position ids, RoPE ladder, timestep features,
+    pre-norm, modulation, QK-norm, SwiGLU) must be caught by one of the pins
+    above.
 """
 import math
 import os
@@ -546,3 +549,87 @@ def test_planted_euler_mistakes_are_caught(monkeypatch):
         monkeypatch.setattr(O, "euler", bad)
         got = O.denoise(lambda z, s: n - x0, z0, sig)
         assert not np.allclose(got, x0, atol=1e-6)
+
+
+# Slips in the page-fixed rules (position ids, RoPE, timestep features, the
+# AdaLN modulation, SwiGLU), patched into the oracle module: each must fail at
+# least one of the listed pins, which check the pages' examples, closed forms
+# and loop versions rather than the oracle's own formulas.
+_O_pos, _O_angles, _O_feat = O.position_ids, O.rope_angles, O.timestep_features
+_O_prenorm, _O_mod = O.prenorm, O.modulation
+
+
+def _pos_ref_from_zero(n_txt, img_grid, ref_grids=()):
+    p = _O_pos(n_txt, img_grid, ref_grids)
+    p[:, 0] = np.where(p[:, 0] > 0, p[:, 0] - 10, p[:, 0])   # t = 10 i
+    return p
+
+
+def _pos_rows_cols_swapped(n_txt, img_grid, ref_grids=()):
+    p = _O_pos(n_txt, img_grid, ref_grids)
+    return p[:, [0, 2, 1, 3]]
+
+
+def _rope_exponent_without_two(pos, axes_dim=(32, 32, 32, 32), theta=2000.0):
+    pos = np.asarray(pos, dtype=np.float64)
+    cols = [pos[:, a:a + 1] * theta ** (-np.arange(d // 2) / d)[None, :]
+            for a, d in enumerate(axes_dim)]
+    return np.concatenate(cols, axis=1)
+
+
+def _modulation_chunks_swapped(gw, sigma, channels=256, dtype=np.float64):
+    m = _O_mod(gw, sigma, channels, dtype)
+    m["dual_img"] = m["dual_img"][:, [1, 0, 2, 4, 3, 5]]        # scale and shift swapped
+    return m
+
+
+_PAGE_MUTANTS = {
+    "ref_t_from_zero": ("position_ids", _pos_ref_from_zero,
+                        [test_position_ids_reference_rule, test_position_ids_fixture]),
+    "grid_rows_cols_swapped": ("position_ids", _pos_rows_cols_swapped,
+                               [test_position_ids_reference_rule, test_position_ids_fixture]),
+    "rope_theta_10000": ("rope_angles",
+                         lambda pos, axes_dim=(32, 32, 32, 32), theta=2000.0:
+                         _O_angles(pos, axes_dim, 10000.0),
+                         [test_rope_frequency_ladder,
+                          test_rope_preserves_pair_norms_and_matches_complex_product]),
+    "rope_exponent_without_two": ("rope_angles", _rope_exponent_without_two,
+                                  [test_rope_frequency_ladder,
+                                   test_rope_preserves_pair_norms_and_matches_complex_product]),
+    "features_sin_first": ("timestep_features",
+                           lambda sigma, channels=256, dtype=np.float64:
+                           _O_feat(sigma, channels, dtype)[:, ::-1],
+                           [test_timestep_features_closed_forms]),
+    "rms_eps_outside_root": ("prenorm",
+                             lambda x, kind=O.PRENORM_RMS, eps=1e-6:
+                             _O_prenorm(x, kind, 0.0) if kind == O.PRENORM_LAYER else
+                             x / (np.sqrt((x * x).mean(axis=-1, keepdims=True)) + eps),
+                             [test_rms_norm_identities]),
+    "modulate_without_one": ("modulate",
+                             lambda x, shift, scale, kind=O.PRENORM_RMS, eps=1e-6:
+                             _O_prenorm(x, kind, eps) * scale + shift,
+                             [test_modulate_zero_scale_is_plain_norm_and_minus_one_zeroes]),
+    "modulation_chunks_swapped": ("modulation", _modulation_chunks_swapped,
+                                  [test_modulation_matches_brute_force]),
+    "qk_norm_over_all_heads": ("qk_rmsnorm",
+                               lambda x, g, eps=1e-6:
+                               x / np.sqrt((x * x).mean(axis=(-3, -1), keepdims=True) + eps) * g,
+                               [lambda: test_dual_block_matches_brute_force(False),
+                                lambda: test_single_block_matches_brute_force(False)]),
+    "swiglu_halves_swapped": ("swiglu", lambda u: O.silu(u[..., u.shape[-1] // 2:]) *
+                              u[..., :u.shape[-1] // 2],
+                              [test_swiglu_closed_form]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(_PAGE_MUTANTS))
+def test_planted_page_rule_mistake_is_caught(name, monkeypatch):
+    attr, mutant, pins = _PAGE_MUTANTS[name]
+    monkeypatch.setattr(O, attr, mutant)
+    caught = 0
+    for pin in pins:
+        try:
+            pin()
+        except AssertionError:
+            caught += 1
+    assert caught > 0, f"no pin caught the planted mistake {name}"
