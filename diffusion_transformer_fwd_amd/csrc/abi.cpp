@@ -678,6 +678,15 @@ int dit_step_forward(const dit_config* cfg, const dit_model_weights* w, const vo
                      sin_dev, v_out, ws, reinterpret_cast<hipStream_t>(stream));
 }
 
+int dit_linear_forward(const void* a, const void* w, float* y, int64_t M, int32_t N,
+                       int32_t K, dit_stream_t stream) {
+  DIT_CHECK(validate_linear(a, w, y, M, N, K));
+  if (M == 0) return DIT_OK;
+  dit::GemmBatch g{};
+  g.p[g.count++] = problem(a, K, w, K, (int)M, N, K, dit::EPI_F32, y, N);
+  return run_gemm(g, reinterpret_cast<hipStream_t>(stream));
+}
+
 int dit_denoise_forward(const dit_config* cfg, const dit_model_weights* w, const void* txt,
                         float* z, const void* ref, const float* sigmas_host, int32_t n_steps,
                         int32_t B, int64_t n_txt, int64_t n_img, int64_t n_ref,

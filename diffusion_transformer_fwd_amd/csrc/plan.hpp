@@ -105,6 +105,8 @@ int validate_step(const dit_config* cfg, const dit_model_weights* w, const void*
                   const void* latents, const float* sigma_host, int32_t B, int64_t n_txt,
                   int64_t n_img, int64_t n_ref, const float* cos_dev, const float* sin_dev,
                   const float* v_out, const void* ws, size_t ws_bytes);
+int validate_linear(const void* a, const void* w, const float* y, int64_t M, int32_t N,
+                    int32_t K);
 int validate_denoise(const dit_config* cfg, const dit_model_weights* w, const void* txt,
                      const float* z, const void* ref, const float* sigmas_host, int32_t n_steps,
                      int32_t B, int64_t n_txt, int64_t n_img, int64_t n_ref,

@@ -26,7 +26,7 @@ EXPORTS = ("dit_position_ids", "dit_workspace_bytes", "dit_status_string", "dit_
            "dit_config_check", "dit_rope_tables_build", "dit_modulation_forward",
            "dit_dual_block_forward", "dit_single_block_forward", "dit_step_forward",
            "dit_denoise_forward", "dit_profile_begin", "dit_profile_end",
-           "dit_modulation_forward_noalloc")
+           "dit_modulation_forward_noalloc", "dit_linear_forward")
 # the latent decoder (include/dit_vae.h)
 VAE_EXPORTS = ("dit_vae_config_check", "dit_vae_config_default", "dit_vae_workspace_bytes",
                "dit_vae_decode_forward", "dit_vae_conv_forward", "dit_vae_group_norm_ws_bytes",
@@ -144,6 +144,8 @@ def lib() -> C.CDLL:
     L.dit_denoise_forward.argtypes = [pc, C.POINTER(ModelWeightsC), vp, vp, vp, vp, i32, i32, i64,
                                       i64, i64, vp, vp, vp, sz, vp]
     L.dit_profile_begin.restype = C.c_int
+    L.dit_linear_forward.restype = C.c_int
+    L.dit_linear_forward.argtypes = [vp, vp, vp, i64, i32, i32, vp]
     L.dit_profile_begin.argtypes = []
     L.dit_profile_end.restype = C.c_int
     L.dit_profile_end.argtypes = [C.POINTER(KernelStats)]
@@ -425,6 +427,17 @@ def denoise(cfg: synth.DitConfig, w: ModelWeights, txt, z, ref, sigmas, cos, sin
         C.byref(c), C.byref(w.c), txt.data_ptr(), z.data_ptr(), _ptr(ref), sig.ctypes.data,
         n_steps, B, n_txt, n_img, n_ref, cos.data_ptr(), sin.data_ptr(), p, n, _stream()))
     return z
+
+
+def linear(a, w, out=None):
+    """y = a w^T in fp32 for bf16 device tensors a [M, K] and w [N, K]."""
+    torch = _torch()
+    M, K = a.shape
+    N = w.shape[0]
+    out = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=a.device)
+    _check(lib().dit_linear_forward(a.data_ptr(), w.data_ptr(), out.data_ptr(), M, N, K,
+                                    _stream()))
+    return out
 
 
 # ---------------------------------------------------------------- latent decoder

@@ -285,6 +285,24 @@ int dit_denoise_forward(const dit_config* cfg, const dit_model_weights* w,
                         const float* cos_dev, const float* sin_dev, void* ws,
                         size_t ws_bytes, dit_stream_t stream);
 
+/* One bias-free linear layer, y = a w^T, through the GEMM every projection of
+ * the step uses (the input embeddings, each block's projections and the
+ * final projection of "tt_flux2_klein - Python reference", Modules), with its
+ * fp32 output epilogue and no K chunking.
+ *   a: dev bf16 [M, K] row-major; w: dev bf16 [N, K] row-major (a layer's
+ *   weight as stored: out_features rows); y: dev fp32 [M, N] row-major,
+ *   overwritten; a, w, y 16-byte aligned and y not overlapping a or w.
+ *   0 <= M < 2^31; N a positive multiple of 4; K a positive multiple of 64;
+ *   M K and N K bf16 elements each addressable with 32-bit byte offsets.
+ * Products are accumulated in fp32 over k in increasing 16-deep steps; the
+ * tile shape the planner picks for M, N and K (256- or 384-row tiles,
+ * 224- or 256-column tiles) never changes an element's result, so a row
+ * of y depends on its row of a only. Returns DIT_E_NULL / DIT_E_SHAPE /
+ * DIT_E_UNSUPPORTED (sizes) or DIT_E_VALUE (y overlaps a or w) before any
+ * launch, DIT_E_HIP if the launch fails; M = 0 launches nothing. */
+int dit_linear_forward(const void* a, const void* w, float* y, int64_t M, int32_t N,
+                       int32_t K, dit_stream_t stream);
+
 /* ------------------------------------------------------------- profiling */
 
 /* Kernel families, for dit_kernel_stats.kind. */

@@ -182,6 +182,22 @@ static void validation_checks() {
   float sig[64];
   for (int i = 0; i < 64; ++i) sig[i] = 0.5f;
   const size_t big = (size_t)1 << 40;
+  // one linear layer: sizes, 32-bit operand offsets, overlap of y with a / w
+  {
+    const void* a = fake(0);
+    const void* wl = reinterpret_cast<const void*>((uintptr_t)1 << 32);
+    const float* y = reinterpret_cast<const float*>((uintptr_t)1 << 36);
+    EXPECT(validate_linear(a, wl, y, 4608, 3072, 12288) == DIT_OK);
+    EXPECT(validate_linear(a, wl, y, 0, 3072, 12288) == DIT_OK);
+    EXPECT(validate_linear(a, wl, y, 4608, 3070, 12288) == DIT_E_SHAPE);
+    EXPECT(validate_linear(a, wl, y, 4608, 3072, 12280) == DIT_E_SHAPE);
+    EXPECT(validate_linear(a, wl, y, (int64_t)1 << 31, 128, 64) == DIT_E_SHAPE);
+    EXPECT(validate_linear(a, wl, y, 174763, 128, 12288) == DIT_E_UNSUPPORTED);  // 4 GiB + of a
+    EXPECT(validate_linear(a, wl, y, 174762, 128, 12288) == DIT_OK);
+    EXPECT(validate_linear(a, wl, ffake(3), 4608, 3072, 12288) == DIT_E_VALUE);  // y inside a
+    EXPECT(validate_linear(a, wl, ffake(3), 0, 3072, 12288) == DIT_OK);
+    EXPECT(validate_linear(nullptr, wl, y, 1, 4, 64) == DIT_E_NULL);
+  }
   // rope tables
   EXPECT(validate_rope(&c, static_cast<const int32_t*>(fake()), 10, ffake(), ffake()) == DIT_OK);
   EXPECT(validate_rope(&c, nullptr, 10, ffake(), ffake()) == DIT_E_NULL);

@@ -32,7 +32,7 @@ def header_functions(name):
 
 def test_exports_every_declared_function(L):
     names = header_functions("dit.h")
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     assert sorted(dit.EXPORTS) == names
     vae = header_functions("dit_vae.h")
     assert len(vae) == 7, vae
@@ -390,3 +390,19 @@ def test_vae_conv_and_group_norm_validation_errors(L):
     assert gn(fake, fake, fake, fake, 1, 100, 64, 32, 1e-6, 1, fake, need, None) == dit.DIT_E_VALUE
     assert gn(fake, fake + 4096, fake, fake, 1, 100, 64, 32, 0.0, 1, fake, need, None) == dit.DIT_E_VALUE
     assert gn(fake, fake + 4096, fake, fake, 1, 100, 64, 32, 1e-6, 1, fake, need - 1, None) == dit.DIT_E_WORKSPACE
+
+
+def test_linear_validation_errors(L):
+    fake = 1 << 20
+    f = L.dit_linear_forward
+    y = fake + (1 << 24)
+    assert f(None, fake, y, 256, 256, 128, None) == dit.DIT_E_NULL
+    assert f(fake, fake, None, 256, 256, 128, None) == dit.DIT_E_NULL
+    assert f(fake + 8, fake, y, 256, 256, 128, None) == dit.DIT_E_SHAPE   # unaligned a
+    assert f(fake, fake, y, -1, 256, 128, None) == dit.DIT_E_SHAPE
+    assert f(fake, fake, y, 256, 254, 128, None) == dit.DIT_E_SHAPE       # N % 4
+    assert f(fake, fake, y, 256, 256, 96, None) == dit.DIT_E_SHAPE        # K % 64
+    assert f(fake, fake, y, 256, 0, 128, None) == dit.DIT_E_SHAPE
+    assert f(fake, fake, y, 1 << 22, 256, 1024, None) == dit.DIT_E_UNSUPPORTED  # 8 GiB of a
+    assert f(fake, fake, fake + 4096, 256, 256, 128, None) == dit.DIT_E_VALUE   # y inside a
+    assert f(fake, fake, y, 0, 256, 128, None) == dit.DIT_OK              # nothing to launch

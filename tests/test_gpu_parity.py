@@ -269,6 +269,52 @@ def gemm_tile_rows(rows):
             os.environ["DIT_GEMM_TILE_ROWS"] = old
 
 
+LINEAR_CASES = [
+    # (name, M, N, K): one row; ragged rows against both tile heights; N
+    # that is not a multiple of the tile width; long K; the 1024x1024 step's
+    # image-stream output projection and single-block output projection
+    ("one_row", 1, 128, 64),
+    ("m257_n3072_k192", 257, 3072, 192),
+    ("m385_n256_k128", 385, 256, 128),
+    ("m300_n136_k12288", 300, 136, 12288),
+    ("m4608_n3072_k3072", 4608, 3072, 3072),
+    ("m4608_n3072_k12288", 4608, 3072, 12288),
+]
+
+
+@pytest.mark.parametrize("case", LINEAR_CASES, ids=[c[0] for c in LINEAR_CASES])
+def test_linear_fp32_against_oracle(case):
+    """dit_linear_forward with bf16-exact operands against the oracle's
+    float64 product, held to fp32 accumulation error rather than the bf16
+    tolerance: every product of two bf16 values is exact in fp32, so what
+    remains is the rounding of K fp32 additions. Bounds: each element within
+    K 2^-24 (|a| |w|^T) of the float64 result (the standard bound for a
+    K-term fp32 sum), and rel-L2 <= 1e-5 over the output. A wrong row,
+    column or k index would be off by O(1) relative. Tile heights 256, 384
+    and the planner's choice give the same bits."""
+    name, M, N, K = case
+    rng = np.random.default_rng(M * 7 + N * 3 + K)
+    a = synth.bf16_round(rng.standard_normal((M, K)).astype(np.float32))
+    w = synth.bf16_round((rng.standard_normal((N, K)) / np.sqrt(K)).astype(np.float32))
+    a_d, w_d = dit.to_bf16_device(a), dit.to_bf16_device(w)
+    outs = {}
+    for rows in (None, 256, 384):
+        with gemm_tile_rows(rows) if rows else contextlib.nullcontext():
+            outs[rows] = to_np(dit.linear(a_d, w_d))
+    a64, w64 = a.astype(np.float64), w.astype(np.float64)
+    want = O.linear(a64, w64)
+    bound = K * 2.0 ** -24 * (np.abs(a64) @ np.abs(w64).T)
+    got = outs[None]
+    err = np.abs(got.astype(np.float64) - want)
+    _, rl = stats(got, want)
+    log(f"linear {name}: max |err| / bound {np.max(err / np.maximum(bound, 1e-300)):.3e}, "
+        f"max |err| {err.max():.3e}, rel_l2 {rl:.3e}")
+    assert np.all(err <= bound + 1e-30), f"{name}: error above the fp32 summation bound"
+    assert rl <= 1e-5, f"{name}: rel_l2 {rl:.3e}"
+    for rows in (256, 384):
+        assert np.array_equal(outs[rows], got), f"{name}: {rows}-row tiles differ"
+
+
 TILE_CASES = [
     # (name, cfg kwargs, n_txt, grid, refs, B): ragged row counts, a batch,
     # and the 1024x1024 shape, where the launch plan mixes both heights
