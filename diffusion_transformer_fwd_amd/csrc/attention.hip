@@ -19,10 +19,14 @@
 //    softmax phase (exp2 and bf16 packing of tile t: vector ALU only), each
 //    closed by a workgroup barrier, so one wave's MFMAs run under its
 //    partner's softmax.
-//  * Waves 0-3 alone issue the K/V tile loads (tile t + 2, spread through
-//    their matrix phase for tile t) and wait for tile t + 1 at the end of
-//    their softmax phase; the stage a load overwrites was last read by the
-//    lagging waves before the barrier that precedes the load.
+//  * The tile loads ride in the softmax phases, which have slack against the
+//    partner's matrix phase (a load instruction can hold its wave back, and
+//    the matrix phase sets the pace): waves 0-3 request the V^T rows of tile
+//    t + 2, waves 4-7 the K rows of tile t + 3 (tiles 0 and 1 come whole
+//    from waves 0-3 before the loop, the K rows of tile 2 from waves 4-7).
+//    Each wave waits for its own older loads at the end of its softmax phase
+//    and the barrier after it publishes them; a load only overwrites a stage
+//    whose last reads ended before an earlier barrier.
 //  * Workgroups walk (batch, head, query block) XCD-contiguously, so a
 //    head's K and V^T are shared through one XCD's L2.
 //  * Scores are computed transposed, S^T = K Q^T, with
