@@ -566,18 +566,19 @@ int validate_vae_conv(const void* xin, int32_t c_in, int32_t ksize, int32_t up, 
 
 int validate_linear(const void* a, const void* w, const float* y, int64_t M, int32_t N,
                     int32_t K) {
-  DIT_CHECK(check_ptr(a, "a"));
-  DIT_CHECK(check_ptr(w, "w"));
-  DIT_CHECK(check_ptr(y, "y"));
   if (M < 0 || M > INT32_MAX) return fail(DIT_E_SHAPE, "M %lld out of [0, 2^31)", (long long)M);
   if (N < 4 || N % 4) return fail(DIT_E_SHAPE, "N %d: a positive multiple of 4", N);
   if (K < 64 || K % 64) return fail(DIT_E_SHAPE, "K %d: a positive multiple of 64", K);
   if ((uint64_t)M * K * 2 > kMaxBufferBytes || (uint64_t)N * K * 2 > kMaxBufferBytes)
     return fail(DIT_E_UNSUPPORTED, "an operand exceeds 32-bit byte offsets");
+  if (M == 0) return DIT_OK;  // nothing to read or write
+  DIT_CHECK(check_ptr(a, "a"));
+  DIT_CHECK(check_ptr(w, "w"));
+  DIT_CHECK(check_ptr(y, "y"));
   const uintptr_t y0 = reinterpret_cast<uintptr_t>(y), y1 = y0 + (uint64_t)M * N * 4;
   const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), a1 = a0 + (uint64_t)M * K * 2;
   const uintptr_t w0 = reinterpret_cast<uintptr_t>(w), w1 = w0 + (uint64_t)N * K * 2;
-  if (M > 0 && ((y0 < a1 && a0 < y1) || (y0 < w1 && w0 < y1)))
+  if ((y0 < a1 && a0 < y1) || (y0 < w1 && w0 < y1))
     return fail(DIT_E_VALUE, "y overlaps a or w");
   return DIT_OK;
 }

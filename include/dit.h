@@ -299,7 +299,8 @@ int dit_denoise_forward(const dit_config* cfg, const dit_model_weights* w,
  * 224- or 256-column tiles) never changes an element's result, so a row
  * of y depends on its row of a only. Returns DIT_E_NULL / DIT_E_SHAPE /
  * DIT_E_UNSUPPORTED (sizes) or DIT_E_VALUE (y overlaps a or w) before any
- * launch, DIT_E_HIP if the launch fails; M = 0 launches nothing. */
+ * launch, DIT_E_HIP if the launch fails; M = 0 launches nothing and
+ * accepts NULL pointers. */
 int dit_linear_forward(const void* a, const void* w, float* y, int64_t M, int32_t N,
                        int32_t K, dit_stream_t stream);
 

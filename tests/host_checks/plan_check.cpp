@@ -197,6 +197,7 @@ static void validation_checks() {
     EXPECT(validate_linear(a, wl, ffake(3), 4608, 3072, 12288) == DIT_E_VALUE);  // y inside a
     EXPECT(validate_linear(a, wl, ffake(3), 0, 3072, 12288) == DIT_OK);
     EXPECT(validate_linear(nullptr, wl, y, 1, 4, 64) == DIT_E_NULL);
+    EXPECT(validate_linear(nullptr, nullptr, nullptr, 0, 4, 64) == DIT_OK);
   }
   // rope tables
   EXPECT(validate_rope(&c, static_cast<const int32_t*>(fake()), 10, ffake(), ffake()) == DIT_OK);

@@ -406,3 +406,5 @@ def test_linear_validation_errors(L):
     assert f(fake, fake, y, 1 << 22, 256, 1024, None) == dit.DIT_E_UNSUPPORTED  # 8 GiB of a
     assert f(fake, fake, fake + 4096, 256, 256, 128, None) == dit.DIT_E_VALUE   # y inside a
     assert f(fake, fake, y, 0, 256, 128, None) == dit.DIT_OK              # nothing to launch
+    assert f(None, None, None, 0, 256, 128, None) == dit.DIT_OK
+    assert f(None, None, None, 0, 254, 128, None) == dit.DIT_E_SHAPE
