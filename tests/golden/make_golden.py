@@ -13,6 +13,10 @@ of minutes on a few cores) and stores the velocity:
   whose whole tensor would be 17 MB; there the whole-tensor check is the sum
   of squares per batch row.
 
+The 4-step sampling loop at 1024x1024 (the pages' four steps; schedule 1,
+0.75, 0.5, 0.25, 0 from the workload's noise latent, no reference) stores the
+whole latent after the last Euler update (fp32, [1, 4096, 128]).
+
 The latent decoder's workloads (oracle/vae_oracle.py, float64, one batch
 row at a time) store the image [B, H, W, 3]: whole (fp32) for the 1024x1024
 decode, every 16th pixel row (plus the last) of each batch row for the
@@ -20,9 +24,9 @@ decode, every 16th pixel row (plus the last) of each batch row for the
 full-image sum of squares per batch row.
 
 Usage: python tests/golden/make_golden.py [step_1024px_s4608 ...]
-Output: tests/golden/<workload>.npz with rows (int64), v ([B, len(rows), C])
-        or image ([B, len(rows), W, 3]), and the oracle's full-tensor sum of
-        squares and max-abs per batch row.
+Output: tests/golden/<workload>.npz with rows (int64), v ([B, len(rows), C]),
+        z ([B, n_img, C], the loop) or image ([B, len(rows), W, 3]), and the
+        oracle's full-tensor sum of squares and max-abs per batch row.
 """
 import os
 import sys
@@ -44,6 +48,11 @@ WORKLOADS = {
     synth.W_STEP_1920x1088_B4.name: (synth.W_STEP_1920x1088_B4, 32),
     synth.W_STEP_848x624_3REF.name: (synth.W_STEP_848x624_3REF, 1),
     synth.W_STEP_512_REF.name: (synth.W_STEP_512_REF, 1),
+}
+
+# sampling-loop workload -> (step workload whose inputs it starts from, schedule)
+DENOISE_WORKLOADS = {
+    "denoise4_1024px_s4608": (synth.W_STEP_1024, [1.0, 0.75, 0.5, 0.25, 0.0]),
 }
 
 # decoder workload -> pixel-row stride of the stored image
@@ -85,6 +94,31 @@ def run(name: str) -> None:
     print(f"wrote {out} in {time.time() - t0:.0f}s", flush=True)
 
 
+def run_denoise(name: str) -> None:
+    wl, sched = DENOISE_WORKLOADS[name]
+    cfg = synth.FLUX2_KLEIN
+    weights = synth.ModelWeights(cfg, 0, cache=False)
+    ins = synth.step_inputs(cfg, wl, batch_row=0)
+    txt = ins["txt"][None]
+    z0 = ins["latents"][None, :wl.n_img]
+    pos = O.position_ids(wl.n_txt, wl.img_grid, wl.ref_grids)
+    sigmas = np.asarray([sched], dtype=np.float64)
+    t0 = time.time()
+    done = [0]
+
+    def velocity(z, sig):
+        v = O.step(cfg, weights, txt, z, sig, wl.n_img, pos)
+        done[0] += 1
+        print(f"  {name}: step {done[0]} done at {time.time() - t0:.0f}s", flush=True)
+        return v
+
+    z = O.denoise(velocity, z0, sigmas)
+    out = os.path.join(os.path.dirname(os.path.abspath(__file__)), f"{name}.npz")
+    np.savez(out, z=z.astype(np.float32), sigmas=sigmas, sumsq=(z * z).sum(axis=(1, 2)),
+             maxabs=np.abs(z).max(axis=(1, 2)), seconds=time.time() - t0)
+    print(f"wrote {out} in {time.time() - t0:.0f}s", flush=True)
+
+
 def run_vae(name: str) -> None:
     wl, stride = VAE_WORKLOADS[name]
     vcfg = synth.VAE_KLEIN
@@ -107,5 +141,10 @@ def run_vae(name: str) -> None:
 
 
 if __name__ == "__main__":
-    for n in (sys.argv[1:] or list(WORKLOADS) + list(VAE_WORKLOADS)):
-        run_vae(n) if n in VAE_WORKLOADS else run(n)
+    for n in (sys.argv[1:] or list(WORKLOADS) + list(DENOISE_WORKLOADS) + list(VAE_WORKLOADS)):
+        if n in VAE_WORKLOADS:
+            run_vae(n)
+        elif n in DENOISE_WORKLOADS:
+            run_denoise(n)
+        else:
+            run(n)

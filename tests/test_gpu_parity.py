@@ -712,6 +712,45 @@ def test_step_full_size_against_oracle(wl, klein):
     assert np.all(rel <= 1e-2)
 
 
+DENOISE_GOLDEN = "denoise4_1024px_s4608"
+
+
+@pytest.mark.slow
+def test_denoise_full_size_against_oracle(klein):
+    """The 4-step sampling loop at 1024x1024 as the bench runs it (the step
+    workload's noise latent, schedule 1, 0.75, 0.5, 0.25, 0): every element
+    of the final latent against the oracle's loop, and the loop equal bit for
+    bit to four dit_step_forward calls on bf16(z) with the Euler update
+    z + (sigma_next - sigma) v between them (reference update in extended
+    precision, rounded once to fp32 like the device's fma)."""
+    path = os.path.join(GOLDEN, f"{DENOISE_GOLDEN}.npz")
+    if not os.path.exists(path):
+        pytest.skip(f"{path} not generated (tests/golden/make_golden.py)")
+    g = np.load(path)
+    cfg, wl = synth.FLUX2_KLEIN, synth.W_STEP_1024
+    sig = g["sigmas"].astype(np.float32)
+    ins = synth.step_inputs(cfg, wl, batch_row=0)
+    txt_d = dit.to_bf16_device(ins["txt"][None])
+    z0 = ins["latents"][None, :wl.n_img]
+    pos = dit.position_ids(wl.n_txt, wl.img_grid, wl.ref_grids)
+    cos_d, sin_d = dit.rope_tables(cfg, pos)
+    z = dit.to_f32_device(z0)
+    log(f"denoise 1024x1024: {sig.shape[1] - 1} steps")
+    dit.denoise(cfg, klein, txt_d, z, None, sig, cos_d, sin_d)
+    torch.cuda.synchronize()
+    got = to_np(z)
+    assert np.all(np.isfinite(got))
+    assert_close(got, g["z"], what="4-step loop at 1024x1024 (every element)")
+    zs = z0.astype(np.float32).copy()
+    for i in range(sig.shape[1] - 1):
+        v = to_np(dit.step(cfg, klein, txt_d, dit.to_bf16_device(synth.bf16_round(zs)),
+                           sig[:, i], wl.n_img, cos_d, sin_d))
+        d = (sig[:, i + 1] - sig[:, i]).astype(np.float32)
+        zs = (zs.astype(np.longdouble) + d[:, None, None].astype(np.longdouble) *
+              v.astype(np.longdouble)).astype(np.float32)
+    assert np.array_equal(zs, got), "sampling loop differs from separate steps + Euler"
+
+
 @pytest.mark.slow
 def test_step_deterministic_bitwise(klein):
     wl = synth.W_STEP_1024
