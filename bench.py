@@ -166,6 +166,63 @@ def cpu_baseline(cfg, mw, wl):
     return sec, threads, flops
 
 
+def cpu_block_baselines(mw):
+    """The oracle as it stands, in fp32 NumPy, on the two block workloads:
+    the 1024 x 1024 single block (512 text + 64 x 64 image rows, block 0 of
+    the step's weights, already in host memory), median of 3 runs after the
+    step's timing warmed the same shapes; and the small dual block (hidden
+    256, 32 text + 8 x 8 image rows, sigma 0.5) on one BLAS thread, median of
+    20 after one warm-up. Returns two dicts of ms and GFLOP/s."""
+    from oracle import dit_oracle as O
+    from diffusion_transformer_fwd_amd import synth
+    from threadpoolctl import threadpool_limits
+
+    def block_flops(S, D, F, dual):
+        per_row = 2.0 * D * (4 * D + 3 * F) if dual else 2.0 * D * (3 * D + 2 * F) + 2.0 * (D + F) * D
+        return S * per_row + 4.0 * S * S * D
+
+    def setup(cfg, gw, wl):
+        pos = O.position_ids(wl.n_txt, wl.img_grid, wl.ref_grids)
+        mod = O.modulation(gw, np.array([wl.sigma]), cfg.time_channels, np.float32)
+        cos, sin = O.rope_tables(pos, cfg.axes_dim, cfg.theta)
+        x = synth.residual(cfg, 0, pos.shape[0])[None]
+        return pos.shape[0], mod, cos.astype(np.float32), sin.astype(np.float32), x
+
+    cfg, wl = synth.FLUX2_KLEIN, synth.W_SINGLE_1024
+    S, mod, cos, sin, x = setup(cfg, mw.glob, wl)
+    ts = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        y = O.single_block(x, mw.single(0), mod["single"], cos, sin, cfg.heads, cfg.eps,
+                           cfg.prenorm, np.float32)
+        ts.append(time.perf_counter() - t0)
+    assert np.all(np.isfinite(y))
+    sec = float(np.median(ts))
+    fl = block_flops(S, cfg.hidden, cfg.mlp_hidden, False)
+    single = {"workload": wl.name, "ms": round(sec * 1000.0, 1), "reps": 3,
+              "gflops": round(fl / sec / 1e9, 1)}
+
+    c1 = synth.DitConfig(hidden=256, heads=2, head_dim=128, mlp_hidden=768, n_dual=1,
+                         n_single=1, in_channels=128, txt_channels=256)
+    wl1 = synth.W_DUAL_TINY
+    S1, mod1, cos1, sin1, x1 = setup(c1, synth.global_weights(c1, 0), wl1)
+    w1 = synth.dual_weights(c1, 0, 0)
+    ts = []
+    with threadpool_limits(limits=1):
+        for i in range(21):
+            t0 = time.perf_counter()
+            y = O.dual_block(x1, wl1.n_txt, w1, mod1["dual_txt"], mod1["dual_img"], cos1, sin1,
+                             c1.heads, c1.eps, c1.prenorm, np.float32)
+            if i:
+                ts.append(time.perf_counter() - t0)
+    assert np.all(np.isfinite(y))
+    sec = float(np.median(ts))
+    fl = block_flops(S1, c1.hidden, c1.mlp_hidden, True)
+    dual = {"workload": wl1.name, "ms": round(sec * 1000.0, 3), "reps": 20, "threads": 1,
+            "gflops": round(fl / sec / 1e9, 2)}
+    return single, dual
+
+
 def decode_cpu_baseline(hp=32, wp=32):
     """The decoder oracle as it stands, in fp32 NumPy (its dtype switch), on a
     bounded sample: one decode of an hp x wp token grid (a 512 x 512 image by
@@ -535,6 +592,10 @@ def main():
                          f"NumPy, timed once after a one-block warm-up"
                          + (f"; the GPU step covers {B} such rows" if B > 1 else "")}
         log(f"CPU baseline {sec:.1f} s/step ({threads} threads, {cpu['gflops']} GFLOP/s)")
+        single, dual = cpu_block_baselines(mw)
+        cpu["blocks"] = {"single_block_1024px": single, "dual_block_d256_1thread": dual}
+        log(f"CPU block baselines: single block {single['ms']} ms, small dual block "
+            f"{dual['ms']} ms on one thread")
 
     if args.copy_calibration:
         # a fill (writes COPY_CAL_BYTES) and elementwise negations (read and
