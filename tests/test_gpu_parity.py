@@ -282,6 +282,18 @@ LINEAR_CASES = [
 ]
 
 
+def _random_linear_shapes(n, seed=5):
+    """Seeded shapes for the planner's corners: rows 1-5000 (both tile heights
+    and their mixes, ragged ends), widths of 4-4096 columns (multiples of 4:
+    one partial tile column, or several), K of 64-4096."""
+    rng = np.random.default_rng(seed)
+    return [(f"rand{i}", int(rng.integers(1, 5001)), 4 * int(rng.integers(1, 1025)),
+             64 * int(rng.integers(1, 65))) for i in range(n)]
+
+
+LINEAR_CASES += _random_linear_shapes(8)
+
+
 @pytest.mark.parametrize("case", LINEAR_CASES, ids=[c[0] for c in LINEAR_CASES])
 def test_linear_fp32_against_oracle(case):
     """dit_linear_forward with bf16-exact operands against the oracle's
@@ -290,16 +302,20 @@ def test_linear_fp32_against_oracle(case):
     remains is the rounding of K fp32 additions. Bounds: each element within
     K 2^-24 (|a| |w|^T) of the float64 result (the standard bound for a
     K-term fp32 sum), and rel-L2 <= 1e-5 over the output. A wrong row,
-    column or k index would be off by O(1) relative. Tile heights 256, 384
-    and the planner's choice give the same bits."""
+    column or k index would be off by O(1) relative. Tile heights 256, 384,
+    a forced split at row 384 and the planner's choice give the same bits."""
     name, M, N, K = case
     rng = np.random.default_rng(M * 7 + N * 3 + K)
     a = synth.bf16_round(rng.standard_normal((M, K)).astype(np.float32))
     w = synth.bf16_round((rng.standard_normal((N, K)) / np.sqrt(K)).astype(np.float32))
     a_d, w_d = dit.to_bf16_device(a), dit.to_bf16_device(w)
     outs = {}
-    for rows in (None, 256, 384):
-        with gemm_tile_rows(rows) if rows else contextlib.nullcontext():
+    for rows in (None, 256, 384, "split"):
+        if rows == "split":
+            ctx = gemm_split_rows(384)
+        else:
+            ctx = gemm_tile_rows(rows) if rows else contextlib.nullcontext()
+        with ctx:
             outs[rows] = to_np(dit.linear(a_d, w_d))
     a64, w64 = a.astype(np.float64), w.astype(np.float64)
     want = O.linear(a64, w64)
@@ -311,8 +327,8 @@ def test_linear_fp32_against_oracle(case):
         f"max |err| {err.max():.3e}, rel_l2 {rl:.3e}")
     assert np.all(err <= bound + 1e-30), f"{name}: error above the fp32 summation bound"
     assert rl <= 1e-5, f"{name}: rel_l2 {rl:.3e}"
-    for rows in (256, 384):
-        assert np.array_equal(outs[rows], got), f"{name}: {rows}-row tiles differ"
+    for rows in (256, 384, "split"):
+        assert np.array_equal(outs[rows], got), f"{name}: tiling {rows} differs"
 
 
 TILE_CASES = [
