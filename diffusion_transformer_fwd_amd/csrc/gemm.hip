@@ -289,6 +289,70 @@ __device__ __forceinline__ void gemm_tile(const GemmBatch& args, const GemmProbl
   }
   __syncthreads();
   auto main_loop = [&](auto fna) {
+    if constexpr (FM == 2 && BNT == BN) {
+      // 256-row tiles at full width (the only shape whose registers allow
+      // it without spills): fragments two k-steps ahead in four buffers, one
+      // per k-step of a slice, each k-step's six reads issued one after each
+      // of its first MFMAs, so a read has a k-step and a half of MFMAs
+      // before its use even when all eight waves read at once. The slice
+      // barrier sits before k-step 2: k-step 2 and 3's fragments were read
+      // (and waited for) before it, so after it slice kt's stage takes the
+      // loads of slice kt + 2. Same MFMAs in the same k order as below.
+      constexpr int FNA = decltype(fna)::value;
+      bf16x8 af4[4][FM], wf4[4][FNA];
+      auto read_all = [&](int stage, int s, int buf) {
+        const u32x4* sa = lds + stage * (BM * ROW_U);
+        const u32x4* sw = lds + stage * (BN * ROW_U);
+        const int ch = (2 * s + fg) ^ sfr;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+          af4[buf][i] = __builtin_bit_cast(bf16x8, sa[a_rd + i * 32 * ROW_U + ch]);
+#pragma unroll
+        for (int j = 0; j < FNA; ++j)
+          wf4[buf][j] = __builtin_bit_cast(bf16x8, sw[w_rd + j * 32 * ROW_U + ch]);
+      };
+      // the MFMAs on buffer buf; with RD, k-step s of `stage` read into
+      // buffer rb, one fragment after each MFMA
+      auto kstep = [&](int buf, auto rdc, int stage, int s, int rb) {
+        constexpr bool RD = decltype(rdc)::value;
+        const u32x4* sa = lds + stage * (BM * ROW_U);
+        const u32x4* sw = lds + stage * (BN * ROW_U);
+        const int ch = (2 * s + fg) ^ sfr;
+#pragma unroll
+        for (int t = 0; t < FM * FNA; ++t) {
+          const int i = t / FNA, j = t % FNA;
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf4[buf][j], af4[buf][i],
+                                                              acc[i][j], 0, 0, 0);
+          if constexpr (RD) {
+            if (t < FM)
+              af4[rb][t] = __builtin_bit_cast(bf16x8, sa[a_rd + t * 32 * ROW_U + ch]);
+            else if (t < FM + FNA)
+              wf4[rb][t - FM] = __builtin_bit_cast(bf16x8, sw[w_rd + (t - FM) * 32 * ROW_U + ch]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      };
+      using T = std::true_type;
+      // MORE: a slice kt + 1 exists
+      auto slice = [&](int kt, auto morec) {
+        constexpr bool MORE = decltype(morec)::value;
+        const int cur = kt & 1;
+        kstep(0, T{}, cur, 2, 2);
+        kstep(1, T{}, cur, 3, 3);
+        // every read of this stage is done and slice kt + 1 has landed
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (MORE && kt + 2 < nk) dma(kt + 2, cur);
+        kstep(2, morec, cur ^ 1, 0, 0);
+        kstep(3, morec, cur ^ 1, 1, 1);
+      };
+      read_all(0, 0, 0);
+      read_all(0, 1, 1);
+      int kt = 0;
+      for (; kt + 1 < nk; ++kt) slice(kt, T{});
+      slice(kt, std::false_type{});
+      return;
+    }
     fload(fna, 0, 0, 0);
     if (FM == 3) {
       for (int kt = 0; kt < nk; ++kt) {
