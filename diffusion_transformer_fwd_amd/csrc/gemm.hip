@@ -13,8 +13,9 @@
 //    straight into LDS with buffer loads that write LDS (no register
 //    staging, no LDS store instructions), their 16-byte chunks XOR-swizzled
 //    by row so that MFMA fragment reads are free of bank conflicts. Two LDS
-//    stages, one barrier per slice; fragments for the next 16-wide k-step
-//    are read while the current one's MFMAs run.
+//    stages, one barrier per slice; fragments are read ahead of the MFMAs
+//    that use them (two k-steps ahead, one read after each MFMA, in 256-row
+//    full-width tiles; one k-step ahead elsewhere).
 //  * What paces a slice is the stream of slice bytes from L2 into the CU
 //    (about 23 bytes per clock under full MFMA load), not the matrix cores:
 //    a 256 x 256 tile needs 32 B/clk to keep them busy. A 384-row tile does
@@ -205,8 +206,9 @@ __device__ __forceinline__ void gemm_tile(const GemmBatch& args, const GemmProbl
   };
 
   // ---- MFMA fragments. 256-row tiles double-buffer both operands across
-  // k-steps; 384-row tiles (192 accumulators per lane) double-buffer A only
-  // and refetch each W fragment right after its last MFMA of the k-step.
+  // k-steps (at full width the main loop keeps four buffers instead, below);
+  // 384-row tiles (192 accumulators per lane) double-buffer A only and
+  // refetch each W fragment right after its last MFMA of the k-step.
   constexpr int WB = FM == 2 ? 2 : 1;  // W fragment buffers
   const int fr = lane & 31, fg = lane >> 5;
   const int wm = wave & 3, wn = wave >> 2;
