@@ -197,14 +197,17 @@ __global__ __launch_bounds__(256) void time_features_kernel(const TimeArgs a) {
 
 // ------------------------------------------------------------------ gemv
 // y[b, out_off + n] = act_out(sum_k W[n, k] act_in(x[b, k])) for B <= 4
-// batch rows per launch. Workgroup = 4 waves, one weight row per wave per
+// batch rows per launch. Workgroup = NW waves, one weight row per wave per
 // iteration; the B input rows are staged in LDS (fp32, after act_in; B * K
-// floats of dynamic LDS, so a small batch leaves room for more workgroups
-// per CU and more weight loads in flight) and the weight row is streamed
-// once with 16-byte loads: the kernel reads each weight byte exactly once.
+// floats of dynamic LDS) and the weight row is streamed once with 16-byte
+// loads: the kernel reads each weight byte exactly once. One input row
+// leaves room for many 4-wave workgroups per CU; with four rows (48 KiB at
+// K = 3072) only three would fit, so those launches share one LDS copy
+// among 16 waves. An element's arithmetic does not depend on NW.
 constexpr int kGemvMaxB = 4;
 constexpr int kGemvMaxK = 4096;
-__global__ __launch_bounds__(256) void gemv_kernel(const GemvArgs a) {
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void gemv_kernel(const GemvArgs a) {
   // x as [B][2][K / 8][4]: element k = 8 c + e of row b at ((2 b + e / 4) K/8 + c) 4 + e % 4,
   // so the lanes of a wave, which take consecutive chunks c, read consecutive
   // 16-byte words (a plain [B][K] layout has them 32 bytes apart, which
@@ -212,14 +215,14 @@ __global__ __launch_bounds__(256) void gemv_kernel(const GemvArgs a) {
   extern __shared__ __attribute__((aligned(16))) float xs_dyn[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int K8 = a.K >> 3;
-  for (int i = tid; i < a.B * a.K; i += 256) {
+  for (int i = tid; i < a.B * a.K; i += 64 * NW) {
     const int b = i / a.K, k = i - b * a.K;
     const float v = a.x[(int64_t)b * a.K + k];
     const int c = k >> 3, e = k & 7;
     xs_dyn[((2 * b + (e >> 2)) * K8 + c) * 4 + (e & 3)] = a.act_in == ACT_SILU ? silu_f(v) : v;
   }
   __syncthreads();
-  for (int row = blockIdx.x * 4 + wave; row < a.total_rows; row += gridDim.x * 4) {
+  for (int row = blockIdx.x * NW + wave; row < a.total_rows; row += gridDim.x * NW) {
     int si = 0;
 #pragma unroll
     for (int i = 1; i < 4; ++i)
@@ -380,9 +383,15 @@ hipError_t gemv_launch(const GemvArgs& a, hipStream_t stream) {
   // more of them cost more than their extra loads in flight bring (the
   // three modulation GEMVs: 84 us at 1024, 87-90 at 2048, 104 at 512, 122
   // at one row per wave)
-  const int blocks = min(1024, (a.total_rows + 3) / 4);
   const size_t lds = (size_t)a.B * a.K * sizeof(float);
-  hipLaunchKernelGGL(gemv_kernel, dim3((unsigned)blocks), dim3(256), lds, stream, a);
+  if (a.B == 1) {
+    const int blocks = min(1024, (a.total_rows + 3) / 4);
+    hipLaunchKernelGGL(gemv_kernel<4>, dim3((unsigned)blocks), dim3(256), lds, stream, a);
+  } else {
+    // 16-wave workgroups, two per CU
+    const int blocks = min(512, (a.total_rows + 15) / 16);
+    hipLaunchKernelGGL(gemv_kernel<16>, dim3((unsigned)blocks), dim3(1024), lds, stream, a);
+  }
   return hipGetLastError();
 }
 
