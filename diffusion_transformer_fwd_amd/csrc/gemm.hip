@@ -417,58 +417,95 @@ __device__ __forceinline__ void gemm_tile(const GemmBatch& args, const GemmProbl
   if (EK == EK_F32) {
     // fp32 stage [128][256] per pass: pass p holds accumulator block i = p
     // of every wave (stage row r is tile row (r / 32) WTM + 32 p + r % 32),
-    // so each pass frees its registers; 16-byte chunk c of row r at c ^ (r & 31)
-#pragma unroll
-    for (int pass = 0; pass < FM; ++pass) {
+    // so each pass frees its registers; 16-byte chunk c of row r at c ^ (r & 31).
+    // A wave writes 16 rows of a pass: row r = 8 k + wave for k < 16, one
+    // 16-byte unit per lane (chunk = lane). The rows' output offsets are
+    // wave-uniform.
+    int m0p = m0;
+    asm volatile("" : "+s"(m0p));
+    const int c = lane, col = tn * BNT + c * 4;
+    const bool col_ok = c * 4 < BNT && col < N;
+    const float* const gate = P.gate;
+    const int64_t gate_bs = P.gate_bstride;
+    const bool resid = epi == EPI_RESID;
+    float* const Cf = static_cast<float*>(Cp);
+    // inside one batch segment a lane's gate is one vector for the whole tile
+    // (read once at 256 rows; at 384 rows, with its batch of 8 rows, like a
+    // tile across batch segments)
+    const bool gate_once = FM == 2 && one_seg;
+    f32x4 g1 = {};
+    if (resid && gate_once && col_ok) g1 = *reinterpret_cast<const f32x4*>(gate + (int64_t)b_first * gate_bs + col);
+    // The residual reads of RB rows per wave are in flight together. At 256
+    // rows (registers allow 16) a pass's reads are issued before its
+    // accumulators are staged, so their latency hides behind the staging and
+    // its barrier (and, in the first pass, behind the last MFMAs' results
+    // arriving): one memory latency per pass. At 384 rows they go in batches
+    // of 8 after the barrier.
+    constexpr int RB = FM == 2 ? 16 : 8;
+    auto stage = [&](int pass) {
 #pragma unroll
       for (int j = 0; j < FN; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int r = wm * 32 + fr;
-          const int c = (wn * WTN + j * 32 + 8 * q + 4 * fg) >> 2;
+          const int cc = (wn * WTN + j * 32 + 8 * q + 4 * fg) >> 2;
           f32x4 v;
 #pragma unroll
           for (int e = 0; e < 4; ++e) v[e] = acc[pass][j][4 * q + e];
-          *reinterpret_cast<f32x4*>(T + r * 1024 + ((c ^ (r & 31)) << 4)) = v;
+          *reinterpret_cast<f32x4*>(T + r * 1024 + ((cc ^ (r & 31)) << 4)) = v;
         }
-      __syncthreads();
-      // 16-byte unit u = it * NT + tid: row u / 64 = 8 it + wave, chunk
-      // u % 64 = lane. The residual and gate reads of 8 rows are issued
-      // together before any store (a store could alias a later read, so the
-      // compiler would not move reads above it), one memory latency per 8 rows.
-      constexpr int RF = 8;  // rows in flight
-      // the rows' addresses are wave-uniform (scalar registers): computed here,
-      // per pass, instead of all passes' up front
-      int m0p = m0;
-      asm volatile("" : "+s"(m0p));
-      const int c = lane, col = tn * BNT + c * 4;
-      const bool col_ok = c * 4 < BNT && col < N;
-      const float* const gate = P.gate;
-      const int64_t gate_bs = P.gate_bstride;
+    };
 #pragma unroll
-      for (int half = 0; half < 16 / RF; ++half) {
-        float* dst[RF];
-        f32x4 x[RF], g[RF];
+    for (int pass = 0; pass < FM; ++pass) {
+      f32x4 x[RB];
+      // row k of batch bt is stage row 8 (RB bt + k) + wave
+      auto reads = [&](int bt) {
 #pragma unroll
-        for (int k = 0; k < RF; ++k) {
-          const int r = 8 * (RF * half + k) + wave;
+        for (int k = 0; k < RB; ++k) {
+          const int r = 8 * (RB * bt + k) + wave;
           const int gr = m0p + (r >> 5) * WTM + 32 * pass + (r & 31);
-          dst[k] = nullptr;
-          if (col_ok && gr < M) {
+          if (resid && col_ok && gr < M) {
             int b;
-            dst[k] = static_cast<float*>(Cp) + out_row_of(gr, b) * ldc + col;
-            if (epi == EPI_RESID) {
-              g[k] = *reinterpret_cast<const f32x4*>(gate + (int64_t)b * gate_bs + col);
-              x[k] = *reinterpret_cast<const f32x4*>(dst[k]);
-            }
+            x[k] = *reinterpret_cast<const f32x4*>(Cf + out_row_of(gr, b) * ldc + col);
           }
         }
+      };
+      if (FM == 2) reads(0);
+      __builtin_amdgcn_sched_barrier(0);
+      stage(pass);
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();
+      // the row offsets again, from a copy of m0 the compiler cannot see
+      // through (kept from the reads they would hold 32 scalar registers)
+      int m0q = m0;
+      asm volatile("" : "+s"(m0q));
 #pragma unroll
-        for (int k = 0; k < RF; ++k) {
-          const int r = 8 * (RF * half + k) + wave;
-          if (dst[k] == nullptr) continue;
-          const f32x4 v = *reinterpret_cast<const f32x4*>(T + r * 1024 + ((c ^ (r & 31)) << 4));
-          *reinterpret_cast<f32x4*>(dst[k]) = epi == EPI_RESID ? x[k] + g[k] * v : v;
+      for (int bt = 0; bt < 16 / RB; ++bt) {
+        if (FM != 2) reads(bt);
+#pragma unroll
+        for (int h = 0; h < RB / 8; ++h) {
+          // a tile across batch segments reads each row's gate, 8 rows at a time
+          f32x4 g[8];
+          if (resid && !gate_once) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+              const int r = 8 * (RB * bt + 8 * h + k) + wave;
+              const int gr = m0q + (r >> 5) * WTM + 32 * pass + (r & 31);
+              g[k] = g1;
+              if (col_ok && gr < M)
+                g[k] = *reinterpret_cast<const f32x4*>(gate + (int64_t)batch_of(gr) * gate_bs + col);
+            }
+          }
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            const int r = 8 * (RB * bt + 8 * h + k) + wave;
+            const int gr = m0q + (r >> 5) * WTM + 32 * pass + (r & 31);
+            if (!col_ok || gr >= M) continue;
+            int b;
+            const f32x4 v = *reinterpret_cast<const f32x4*>(T + r * 1024 + ((c ^ (r & 31)) << 4));
+            float* const d = Cf + out_row_of(gr, b) * ldc + col;
+            *reinterpret_cast<f32x4*>(d) = resid ? x[8 * h + k] + (gate_once ? g1 : g[k]) * v : v;
+          }
         }
       }
       __syncthreads();
