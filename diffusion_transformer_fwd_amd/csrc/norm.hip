@@ -72,63 +72,119 @@ __global__ __launch_bounds__(256) void modnorm_kernel(const NormArgs a) {
   }
 }
 
-// One workgroup (4 waves) per output row, VPT float4 per thread (D <= 1024
-// VPT): the row's x, shift and scale loads are all issued before the first
-// reduction, and the sums go through LDS. Same arithmetic as modnorm_kernel,
-// with the reductions in another order.
-template <int VPT>
-__global__ __launch_bounds__(256) void modnorm_row_kernel(const NormArgs a) {
-  __shared__ float part[4];
+// One workgroup (4 waves) per R consecutive output rows, VPT float4 per
+// thread per row (D <= 1024 VPT). When the R rows belong to one segment and
+// one batch row (every workgroup but those at a segment's or batch row's
+// edge) the shift and scale vectors are read once for all R rows, and all
+// loads are issued before the first reduction; otherwise the rows are done
+// one at a time. The sums go through LDS, R at a time; each row's arithmetic
+// and summation order are the same either way. Same arithmetic as
+// modnorm_kernel, with the reductions in another order.
+template <int VPT, int R>
+__device__ __forceinline__ void modnorm_rows(const NormArgs& a, const int64_t (&xrow)[R],
+                                             const int64_t (&orow)[R], const float* shift,
+                                             const float* scale, float (*part)[4]) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t row = blockIdx.x;
-  const int si = (a.nseg > 1 && row >= a.seg[1].out_base) ? 1 : 0;
-  const NormSegment& sg = si ? a.seg[1] : a.seg[0];
-  const int64_t r = row - sg.out_base;
-  if (r < 0 || r >= (int64_t)a.B * sg.seg_len) return;  // uniform per workgroup
-  const int b = (int)(r / sg.seg_len);
-  const int64_t xrow = (int64_t)b * a.S + sg.seg_off + (r - (int64_t)b * sg.seg_len);
   const int D = a.D, D4 = D >> 2;
-  const f32x4* xr = reinterpret_cast<const f32x4*>(a.x + xrow * D);
-  const f32x4* sh = reinterpret_cast<const f32x4*>(sg.shift + (int64_t)b * a.mod_bstride);
-  const f32x4* sc = reinterpret_cast<const f32x4*>(sg.scale + (int64_t)b * a.mod_bstride);
-  f32x4 v[VPT], vs[VPT], vh[VPT];
+  const f32x4* sh = reinterpret_cast<const f32x4*>(shift);
+  const f32x4* sc = reinterpret_cast<const f32x4*>(scale);
+  f32x4 v[R][VPT], vs[VPT], vh[VPT];
 #pragma unroll
   for (int i = 0; i < VPT; ++i) {
     const int c = i * 256 + tid;
     const bool ok = c < D4;
-    v[i] = ok ? xr[c] : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < R; ++k)
+      v[k][i] = ok ? reinterpret_cast<const f32x4*>(a.x + xrow[k] * D)[c] : f32x4{0.f, 0.f, 0.f, 0.f};
     vh[i] = ok ? sh[c] : f32x4{0.f, 0.f, 0.f, 0.f};
     vs[i] = ok ? sc[c] : f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  auto block_sum = [&](float t) {
-    t = wave_sum(t);
-    if (lane == 0) part[wave] = t;
+  // R block sums at once: per wave, then the four waves' partials in a fixed order
+  auto block_sums = [&](float (&t)[R]) {
+#pragma unroll
+    for (int k = 0; k < R; ++k) t[k] = wave_sum(t[k]);
+    if (lane == 0) {
+#pragma unroll
+      for (int k = 0; k < R; ++k) part[k][wave] = t[k];
+    }
     __syncthreads();
-    const float total = (part[0] + part[1]) + (part[2] + part[3]);
-    __syncthreads();  // part is reused by the next sum
-    return total;
+#pragma unroll
+    for (int k = 0; k < R; ++k) t[k] = (part[k][0] + part[k][1]) + (part[k][2] + part[k][3]);
+    __syncthreads();  // part is reused by the next sums
   };
-  float mean = 0.f;
+  float mean[R], ss[R];
+#pragma unroll
+  for (int k = 0; k < R; ++k) mean[k] = 0.f;
   if (a.kind == 1) {
-    float s1 = 0.f;
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) s1 += v[i][0] + v[i][1] + v[i][2] + v[i][3];
-    mean = block_sum(s1) / D;
+    for (int k = 0; k < R; ++k) {
+      float s1 = 0.f;
+#pragma unroll
+      for (int i = 0; i < VPT; ++i) s1 += v[k][i][0] + v[k][i][1] + v[k][i][2] + v[k][i][3];
+      mean[k] = s1;
+    }
+    block_sums(mean);
+#pragma unroll
+    for (int k = 0; k < R; ++k) mean[k] = mean[k] / D;
   }
-  float ss = 0.f;
 #pragma unroll
-  for (int i = 0; i < VPT; ++i) {
-    if (i * 256 + tid < D4) {
-      const f32x4 d = v[i] - mean;
-      ss += d[0] * d[0] + d[1] * d[1] + d[2] * d[2] + d[3] * d[3];
+  for (int k = 0; k < R; ++k) {
+    ss[k] = 0.f;
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      if (i * 256 + tid < D4) {
+        const f32x4 d = v[k][i] - mean[k];
+        ss[k] += d[0] * d[0] + d[1] * d[1] + d[2] * d[2] + d[3] * d[3];
+      }
     }
   }
-  const float rstd = rsqrtf(block_sum(ss) / D + a.eps);
-  u32x2* out = reinterpret_cast<u32x2*>(a.h + row * D);
+  block_sums(ss);
 #pragma unroll
-  for (int i = 0; i < VPT; ++i) {
-    const int c = i * 256 + tid;
-    if (c < D4) out[c] = pack_bf16x4((v[i] - mean) * rstd * (1.f + vs[i]) + vh[i]);
+  for (int k = 0; k < R; ++k) {
+    const float rstd = rsqrtf(ss[k] / D + a.eps);
+    u32x2* out = reinterpret_cast<u32x2*>(a.h + orow[k] * D);
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int c = i * 256 + tid;
+      if (c < D4) out[c] = pack_bf16x4((v[k][i] - mean[k]) * rstd * (1.f + vs[i]) + vh[i]);
+    }
+  }
+}
+
+template <int VPT, int R>
+__global__ __launch_bounds__(256) void modnorm_row_kernel(const NormArgs a, int64_t rows) {
+  __shared__ float part[R][4];
+  // segment, batch row and x row of each of the workgroup's output rows
+  int si[R], bb[R];
+  int64_t xrow[R], orow[R];
+  bool ok[R];
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    const int64_t row = (int64_t)blockIdx.x * R + k;
+    orow[k] = row;
+    si[k] = (a.nseg > 1 && row >= a.seg[1].out_base) ? 1 : 0;
+    const NormSegment& sg = si[k] ? a.seg[1] : a.seg[0];
+    const int64_t r = row - sg.out_base;
+    ok[k] = row < rows && r >= 0 && r < (int64_t)a.B * sg.seg_len;
+    bb[k] = ok[k] ? (int)(r / sg.seg_len) : 0;
+    xrow[k] = ok[k] ? (int64_t)bb[k] * a.S + sg.seg_off + (r - (int64_t)bb[k] * sg.seg_len) : 0;
+  }
+  bool same = ok[0];
+#pragma unroll
+  for (int k = 1; k < R; ++k) same = same && ok[k] && si[k] == si[0] && bb[k] == bb[0];
+  if (same) {  // uniform per workgroup
+    const NormSegment& sg = si[0] ? a.seg[1] : a.seg[0];
+    modnorm_rows<VPT, R>(a, xrow, orow, sg.shift + (int64_t)bb[0] * a.mod_bstride,
+                         sg.scale + (int64_t)bb[0] * a.mod_bstride, part);
+    return;
+  }
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    if (!ok[k]) continue;  // uniform per workgroup
+    const NormSegment& sg = si[k] ? a.seg[1] : a.seg[0];
+    const int64_t x1[1] = {xrow[k]}, o1[1] = {orow[k]};
+    modnorm_rows<VPT, 1>(a, x1, o1, sg.shift + (int64_t)bb[k] * a.mod_bstride,
+                         sg.scale + (int64_t)bb[k] * a.mod_bstride, part);
   }
 }
 
@@ -331,11 +387,12 @@ hipError_t modnorm_launch(const NormArgs& a, hipStream_t stream) {
     rows = max(rows, a.seg[i].out_base + (int64_t)a.B * a.seg[i].seg_len);
   if (rows == 0) return hipSuccess;
   const int vpt = (a.D / 4 + 255) / 256;
-  if (vpt >= 2 && vpt <= 4) {  // wide rows: one workgroup per row
-    const dim3 rgrid((unsigned)rows);
-    if (vpt == 2) hipLaunchKernelGGL(modnorm_row_kernel<2>, rgrid, dim3(256), 0, stream, a);
-    else if (vpt == 3) hipLaunchKernelGGL(modnorm_row_kernel<3>, rgrid, dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL(modnorm_row_kernel<4>, rgrid, dim3(256), 0, stream, a);
+  if (vpt >= 2 && vpt <= 4) {  // wide rows: one workgroup per 3 rows
+    constexpr int R = 3;
+    const dim3 rgrid((unsigned)((rows + R - 1) / R));
+    if (vpt == 2) hipLaunchKernelGGL((modnorm_row_kernel<2, R>), rgrid, dim3(256), 0, stream, a, rows);
+    else if (vpt == 3) hipLaunchKernelGGL((modnorm_row_kernel<3, R>), rgrid, dim3(256), 0, stream, a, rows);
+    else hipLaunchKernelGGL((modnorm_row_kernel<4, R>), rgrid, dim3(256), 0, stream, a, rows);
     return hipGetLastError();
   }
   const dim3 grid((unsigned)((rows + 3) / 4));
